@@ -1,0 +1,234 @@
+// C ABI of libgdpa: host-side argument validation, workspace layout and kernel launches.
+// Every check here runs before the first HIP call of a request, so an invalid request enqueues
+// nothing and can be tested without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gdpa.h"
+#include "gdpa_launch.hpp"
+
+namespace gdpa {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t items = 0, keys = 0, delta = 0, total = 0;
+  int64_t n_items = 0, n_seqs = 0, delta_rows = 0;
+  int64_t delta_base[GDPA_MAX_GROUPS] = {};
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_problem(const gdpa_problem& p) {
+  if (p.num_seqs < 0 || p.num_seqs >= (1 << 19)) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.num_heads < 1 || p.num_heads > 256) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.head_dim != 32 && p.head_dim != 64 && p.head_dim != 128) return GDPA_ERR_UNSUPPORTED;
+  if (p.dtype != GDPA_DTYPE_BF16 && p.dtype != GDPA_DTYPE_FP32) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.act < GDPA_ACT_GELU || p.act > GDPA_ACT_SOFTMAX) return GDPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p.scale)) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.window_left < -1 || p.window_right < -1) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.reserved != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.self_attention != 0 && p.self_attention != 1) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.total_q < 0 || p.total_kv < 0 || p.max_seqlen_q < 0 || p.max_seqlen_kv < 0)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.total_q >= (int64_t)1 << 31 || p.total_kv >= (int64_t)1 << 31) return GDPA_ERR_UNSUPPORTED;
+  const bool windowed = p.window_left >= 0 || p.window_right >= 0;
+  if (windowed && !p.self_attention) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.self_attention && (p.total_q != p.total_kv || p.max_seqlen_q != p.max_seqlen_kv))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.num_seqs > 0 && (!p.q_offsets || !p.kv_offsets)) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.num_seqs == 0 && (p.total_q != 0 || p.total_kv != 0)) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p.max_seqlen_q > p.total_q || (int64_t)p.max_seqlen_kv > p.total_kv)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p.dtype == GDPA_DTYPE_BF16 &&
+      !fwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv))
+    return GDPA_ERR_UNSUPPORTED;
+  return GDPA_OK;
+}
+
+int check_backward_capacity(const gdpa_problem& p) {
+  if (p.dtype != GDPA_DTYPE_BF16) return GDPA_OK;
+  return bwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK
+                                                                                   : GDPA_ERR_UNSUPPORTED;
+}
+
+int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
+  const bool rows = p.total_q > 0, keys = p.total_kv > 0;
+  if (rows && (!t.q || !aligned16(t.q))) return GDPA_ERR_INVALID_ARGUMENT;
+  if (keys && (!t.k || !t.v || !aligned16(t.k) || !aligned16(t.v))) return GDPA_ERR_INVALID_ARGUMENT;
+  if (t.dg && !t.g) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((t.g && !aligned16(t.g)) || (t.lse && ((uintptr_t)t.lse & 3u))) return GDPA_ERR_INVALID_ARGUMENT;
+  if (pass == 0) {
+    if (rows && (!t.o || !aligned16(t.o))) return GDPA_ERR_INVALID_ARGUMENT;
+    if (rows && p.act == GDPA_ACT_SOFTMAX && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
+    if (t.dg) return GDPA_ERR_INVALID_ARGUMENT;
+  } else {
+    if (rows && (!t.dout || !t.dq || !aligned16(t.dout) || !aligned16(t.dq))) return GDPA_ERR_INVALID_ARGUMENT;
+    if (keys && (!t.dk || !t.dv || !aligned16(t.dk) || !aligned16(t.dv))) return GDPA_ERR_INVALID_ARGUMENT;
+    if (rows && p.act == GDPA_ACT_SOFTMAX && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
+  }
+  return GDPA_OK;
+}
+
+int layout(const gdpa_problem* ps, int n_groups, int pass, WsLayout* L) {
+  if (!ps || n_groups < 1 || n_groups > GDPA_MAX_GROUPS) return GDPA_ERR_INVALID_ARGUMENT;
+  if (pass != 0 && pass != 1) return GDPA_ERR_INVALID_ARGUMENT;
+  for (int g = 0; g < n_groups; ++g) {
+    int rc = check_problem(ps[g]);
+    if (rc != GDPA_OK) return rc;
+    if (pass == 1 && (rc = check_backward_capacity(ps[g])) != GDPA_OK) return rc;
+    if (ps[g].dtype != ps[0].dtype) return GDPA_ERR_INVALID_ARGUMENT;
+    L->n_items += (int64_t)ps[g].num_seqs * ps[g].num_heads;
+    L->n_seqs += ps[g].num_seqs;
+    L->delta_base[g] = L->delta_rows;
+    // fp32 softmax backward: per-row D_i between its two kernels
+    if (pass == 1 && ps[g].act == GDPA_ACT_SOFTMAX && ps[g].dtype == GDPA_DTYPE_FP32)
+      L->delta_rows += ps[g].total_q * ps[g].num_heads;
+  }
+  if (L->n_items >= ((int64_t)1 << 31) || L->n_seqs >= ((int64_t)1 << 31)) return GDPA_ERR_UNSUPPORTED;
+  L->items = 0;
+  L->keys = align_up((size_t)L->n_items * 4);
+  L->delta = L->keys + align_up((size_t)L->n_seqs * 4);
+  L->total = L->delta + align_up((size_t)L->delta_rows * 4);
+  if (L->total == 0) L->total = kAlign;
+  return GDPA_OK;
+}
+
+int bit_length(uint64_t x) {
+  int n = 0;
+  while (x) { ++n; x >>= 1; }
+  return n;
+}
+
+void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, const WsLayout& L,
+               LaunchDesc* d) {
+  std::memset(d, 0, sizeof(*d));
+  d->n_groups = n_groups;
+  d->n_items = (int32_t)L.n_items;
+  d->n_seqs_total = (int32_t)L.n_seqs;
+  char* base = static_cast<char*>(ws);
+  d->items = reinterpret_cast<int32_t*>(base + L.items);
+  d->scratch = reinterpret_cast<int32_t*>(base + L.keys);
+  uint64_t max_work = 1;
+  int seq_base = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const gdpa_problem& p = ps[g];
+    const gdpa_tensors& t = ts[g];
+    GroupDesc& gd = d->grp[g];
+    gd.q = t.q; gd.k = t.k; gd.v = t.v; gd.g = t.g; gd.o = t.o; gd.lse = t.lse;
+    gd.dout = t.dout; gd.dq = t.dq; gd.dk = t.dk; gd.dv = t.dv; gd.dg = t.dg;
+    gd.delta = reinterpret_cast<float*>(base + L.delta) + L.delta_base[g];
+    gd.q_off = p.q_offsets;
+    gd.kv_off = p.kv_offsets;
+    gd.num_seqs = p.num_seqs;
+    gd.num_heads = p.num_heads;
+    gd.head_dim = p.head_dim;
+    gd.act = p.act;
+    gd.scale = p.scale;
+    gd.wl = p.window_left;
+    gd.wr = p.window_right;
+    gd.seq_base = seq_base;
+    seq_base += p.num_seqs;
+    uint64_t n = (uint64_t)p.max_seqlen_kv;
+    if (p.window_left >= 0 && p.window_right >= 0) {
+      const uint64_t w = (uint64_t)p.window_left + p.window_right + 1;
+      n = n < w ? n : w;
+    }
+    const uint64_t work = ((uint64_t)p.max_seqlen_q + 32) * (n + 32) * (uint64_t)p.head_dim;
+    if (work > max_work) max_work = work;
+  }
+  const int bl = bit_length(max_work);
+  d->work_shift = bl > 10 ? bl - 10 : 0;
+}
+
+int dim_set_of(const gdpa_problem* ps, int n_groups) {
+  int s = 0;
+  for (int g = 0; g < n_groups; ++g) s |= ps[g].head_dim == 32 ? kDim32 : ps[g].head_dim == 64 ? kDim64 : kDim128;
+  return s;
+}
+
+int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, size_t ws_bytes, void* stream,
+        int pass) {
+  WsLayout L;
+  int rc = layout(ps, n_groups, pass, &L);
+  if (rc != GDPA_OK) return rc;
+  if (!ts) return GDPA_ERR_INVALID_ARGUMENT;
+  for (int g = 0; g < n_groups; ++g)
+    if ((rc = check_tensors(ps[g], ts[g], pass)) != GDPA_OK) return rc;
+  if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < L.total) return GDPA_ERR_WORKSPACE;
+  if (L.n_items == 0) return GDPA_OK;  // nothing to compute
+
+  LaunchDesc d;
+  fill_desc(ps, ts, n_groups, ws, L, &d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (ps[0].dtype == GDPA_DTYPE_FP32) {
+    Fp32Aux aux;
+    std::memset(&aux, 0, sizeof(aux));
+    for (int g = 0; g < n_groups; ++g) {
+      aux.row_pre[g + 1] = aux.row_pre[g] + ps[g].total_q * ps[g].num_heads;
+      aux.key_pre[g + 1] = aux.key_pre[g] + ps[g].total_kv * ps[g].num_heads;
+      aux.row_base[g] = L.delta_base[g];
+    }
+    aux.ws_delta = reinterpret_cast<float*>(static_cast<char*>(ws) + L.delta);
+    e = pass == 0 ? launch_fwd_fp32(d, aux, s) : launch_bwd_fp32(d, aux, s);
+  } else {
+    e = launch_schedule(d, s);
+    if (e == hipSuccess) {
+      const int dims = dim_set_of(ps, n_groups);
+      int acts = 0;
+      for (int g = 0; g < n_groups; ++g) acts |= 1 << ps[g].act;
+      e = pass == 0 ? launch_fwd_bf16(d, dims, acts, s) : launch_bwd_bf16(d, dims, acts, s);
+    }
+  }
+  return e == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace gdpa
+
+extern "C" {
+
+size_t gdpa_workspace_size(const gdpa_problem* problems, int32_t n_groups, int32_t pass) {
+  gdpa::WsLayout L;
+  if (gdpa::layout(problems, n_groups, pass, &L) != GDPA_OK) return 0;
+  return L.total;
+}
+
+int gdpa_fwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws, size_t ws_bytes, void* stream) {
+  return gdpa::run(problem, tensors, 1, ws, ws_bytes, stream, 0);
+}
+
+int gdpa_bwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws, size_t ws_bytes, void* stream) {
+  return gdpa::run(problem, tensors, 1, ws, ws_bytes, stream, 1);
+}
+
+int gdpa_fwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return gdpa::run(problems, tensors, n_groups, ws, ws_bytes, stream, 0);
+}
+
+int gdpa_bwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return gdpa::run(problems, tensors, n_groups, ws, ws_bytes, stream, 1);
+}
+
+const char* gdpa_strerror(int status) {
+  switch (status) {
+    case GDPA_OK: return "ok";
+    case GDPA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GDPA_ERR_UNSUPPORTED: return "unsupported problem shape";
+    case GDPA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GDPA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gdpa_version(void) { return 100; }
+
+}  // extern "C"

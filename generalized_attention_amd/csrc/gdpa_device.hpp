@@ -1,0 +1,182 @@
+// Device-side building blocks of the gfx950 GDPA kernels: descriptor types, the bf16 MFMA
+// fragment conventions, element-wise activations, and small LDS/global helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdpa.h"
+
+namespace gdpa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int kNumBuckets = 1024;
+
+// ----------------------------------------------------------------------------------------------
+// Per-group descriptor handed to the kernels by value (kernel arguments).
+// ----------------------------------------------------------------------------------------------
+struct GroupDesc {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  void* o;
+  float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* delta;  // softmax backward: D_i = <dO_i, O_i> per (row, head), in the workspace
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t act;
+  float scale;
+  int32_t wl;
+  int32_t wr;
+  int32_t seq_base;   // index of this group's first sequence in the global sequence numbering
+};
+
+struct LaunchDesc {
+  GroupDesc grp[GDPA_MAX_GROUPS];
+  int32_t n_groups;
+  int32_t n_seqs_total;
+  int32_t n_items;
+  int32_t work_shift;  // bucket = min(kNumBuckets-1, work >> work_shift)
+  int32_t* items;      // [n_items] packed (group, head, seq) in longest-first order
+  int32_t* scratch;    // builder scratch: [n_seqs_total] bucket keys + [2*kNumBuckets] counters
+};
+
+// Copy of group g's descriptor (g is uniform across the workgroup). A chain of uniform selects
+// instead of a dynamic index into the kernel-argument table keeps the table out of scratch.
+__device__ inline GroupDesc select_group(const LaunchDesc& d, int g) {
+  GroupDesc gd = d.grp[0];
+#pragma unroll
+  for (int i = 1; i < GDPA_MAX_GROUPS; ++i)
+    if (i == g) gd = d.grp[i];
+  return gd;
+}
+
+// Packed work item: group (5 bits) | head (8 bits) | sequence (19 bits).
+__host__ __device__ inline int32_t pack_item(int g, int h, int b) {
+  return (int32_t)(((uint32_t)g << 27) | ((uint32_t)h << 19) | (uint32_t)b);
+}
+__device__ inline void unpack_item(int32_t it, int& g, int& h, int& b) {
+  uint32_t u = (uint32_t)it;
+  g = (int)(u >> 27);
+  h = (int)((u >> 19) & 0xFF);
+  b = (int)(u & 0x7FFFF);
+}
+
+// ----------------------------------------------------------------------------------------------
+// MFMA conventions (v_mfma_f32_32x32x16_bf16, one wave):
+//   A (32 x 16, M x K): lane l holds row l%32, k-slots (l/32)*8 + e, e = 0..7
+//   B (16 x 32, K x N): lane l holds column l%32, k-slots (l/32)*8 + e
+//   C (32 x 32):        lane l holds column l%32, register r holds row (r/4)*8 + (l/32)*4 + r%4
+// Any bijection between k-slots and the true contraction index works if A and B use the same
+// one; the kernels choose bijections that make every operand a contiguous 16-byte read.
+// ----------------------------------------------------------------------------------------------
+__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// C-register -> row mapping of a 32x32 MFMA result, for lane half g = lane/32.
+__device__ __host__ inline constexpr int c_row(int r, int g) { return (r / 4) * 8 + g * 4 + (r % 4); }
+
+// When a C tile (rows = a contraction index of the next product) is fed back as a B operand,
+// B k-tile t (16 slots) takes C registers 8t..8t+7. Slot s = g*8+e of k-tile t then carries
+// row c_row(8t+e, g) = 16t + slot_row(s). slot_row is an involution on 0..15 that swaps the two
+// middle quads: [0..3, 8..11, 4..7, 12..15].
+__device__ __host__ inline constexpr int slot_row(int s) {
+  return ((s & 7) >> 2) * 8 + (s >> 3) * 4 + (s & 3);
+}
+
+// Output-row permutation of a C tile whose A operand rows are chosen so that each lane ends up
+// holding 16 consecutive output columns: C row m of d-tile dt carries output index
+// dt*32 + out_perm(m), so register r of lane half g is output index dt*32 + g*16 + r.
+__device__ __host__ inline constexpr int out_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
+
+// ----------------------------------------------------------------------------------------------
+// bf16 helpers (round to nearest even; gfx950 has a packed convert instruction)
+// ----------------------------------------------------------------------------------------------
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  bf16 x = (bf16)a, y = (bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ inline float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ inline float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+__device__ inline bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// ----------------------------------------------------------------------------------------------
+// Activations in fp32 registers.
+//   The bf16 kernels round P to bf16 right after, so the activations use short forms whose
+//   error is far below a bf16 ulp:
+//   - SiLU: x * rcp(1 + 2^(-x log2 e)) with the hardware exp2 / reciprocal.
+//   - GELU: x * Phi(x) with Phi(x) ~ sigmoid(1.5976 x + 0.07056 x^3), the logistic
+//     approximation of the normal CDF of Bowling, Khasawneh, Kaewkuekool and Cho (2009,
+//     J. Industrial Eng. & Management), |error| < 1.5e-4 on Phi.
+//   The fp32 kernels use the exact erf form (erff of the device math library).
+// ----------------------------------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// sigmoid(z) given t = -z*log2(e)
+__device__ inline float sigmoid_from_t(float t) { return fast_rcp(1.0f + fast_exp2(t)); }
+
+template <int ACT>
+struct Act;
+
+template <>
+struct Act<GDPA_ACT_SILU> {
+  // value and derivative; x is the scaled score
+  __device__ static inline float f(float x) { return x * sigmoid_from_t(-kLog2e * x); }
+  __device__ static inline void fg(float x, float& p, float& dp) {
+    float s = sigmoid_from_t(-kLog2e * x);
+    p = x * s;
+    dp = s + p * (1.0f - s);  // s (1 + x (1 - s))
+  }
+};
+
+template <>
+struct Act<GDPA_ACT_GELU> {
+  // z = 1.5976 x + 0.07056 x^3; Phi ~ sigmoid(z); Phi'(x) = phi(x) approximated by the
+  // derivative of the same logistic form: sigmoid(z)(1-sigmoid(z)) (1.5976 + 3*0.07056 x^2).
+  __device__ static inline float f(float x) {
+    float x2 = x * x;
+    float t = x * __builtin_fmaf(x2, -0.07056f * kLog2e, -1.5976f * kLog2e);
+    return x * sigmoid_from_t(t);
+  }
+  __device__ static inline void fg(float x, float& p, float& dp) {
+    float x2 = x * x;
+    float t = x * __builtin_fmaf(x2, -0.07056f * kLog2e, -1.5976f * kLog2e);
+    float s = sigmoid_from_t(t);
+    p = x * s;
+    float dz = __builtin_fmaf(x2, 3.0f * 0.07056f, 1.5976f);
+    dp = s + x * s * (1.0f - s) * dz;
+  }
+};
+
+// log sigmoid(g) in fp32, overflow-free: min(g, 0) - log1p(exp(-|g|)).
+__device__ inline float log_sigmoid_f(float g) {
+  return fminf(g, 0.0f) - log1pf(__expf(-fabsf(g)));
+}
+
+__device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ inline int wave_id() { return (int)(threadIdx.x >> 6); }
+
+}  // namespace gdpa

@@ -1,0 +1,344 @@
+// GDPA forward for bf16 on gfx950: one workgroup (4 waves) per (sequence, head) work item.
+//
+//   S = scale Q K^T [+ log sigmoid G];  O = phi(S) V   (element-wise phi)  or
+//   O = softmax(S) V with running row max / sum and lse = m + ln(l)           (softmax)
+//
+// (Kunlun review, section 2.3 and Figure 2: QK^T / tau, activation, times V, fused so that the
+// T x n score matrix never reaches HBM; gate from the reproduction README's "Core equations";
+// window from the review's section 2.5.)
+//
+// Data flow of one item:
+//   * K rows and V^T (keys contiguous, in the MFMA slot order) of the item's key range are staged
+//     into LDS once with coalesced 16-byte loads; the per-key gate term is staged beside them.
+//   * Each wave owns 32 or 64 query rows and keeps their Q in registers (the B operand of
+//     S^T = K Q^T: a lane holds 8..64 contiguous d of one row).
+//   * Per block of 32 keys: S^T on MFMA (A = K rows from LDS), mask / phi / online softmax on the
+//     fp32 accumulators, convert to bf16; the accumulator layout of S^T is directly the B operand
+//     of O^T = V^T P^T (A = V^T rows from LDS), so P never leaves registers.
+//   * Epilogue: each lane holds 16 consecutive d of one row of O: two 16-byte stores.
+// Short key ranges (personalized-FFN form: n keys per sample) are staged once and the waves sweep
+// all query tiles of the sequence; a bounded sliding window is swept in chunks of 128 rows whose
+// key range [r0 - left, r0 + 128 + right) is restaged per chunk.
+#include "gdpa_device.hpp"
+#include "gdpa_launch.hpp"
+
+namespace gdpa {
+
+template <int D>
+struct FwdGeo {
+  static constexpr int NKV = 16384 / D;        // keys that fit in LDS
+  static constexpr int KROW = D * 2 + 16;      // bytes per staged K row (16 B pad: no bank conflicts)
+  static constexpr int VROW = NKV * 2 + 16;    // bytes per staged V^T row
+  static constexpr int KK = D / 16;            // MFMA k-steps over d
+  static constexpr int DT = D / 32;            // 32-wide d tiles of the output
+  static constexpr int OFF_V = NKV * KROW;
+  static constexpr int OFF_G = OFF_V + D * VROW;
+  static constexpr int BYTES = OFF_G + NKV * 4;
+};
+
+constexpr int kFwdLdsBytes = FwdGeo<32>::BYTES > FwdGeo<64>::BYTES
+                                 ? (FwdGeo<32>::BYTES > FwdGeo<128>::BYTES ? FwdGeo<32>::BYTES : FwdGeo<128>::BYTES)
+                                 : (FwdGeo<64>::BYTES > FwdGeo<128>::BYTES ? FwdGeo<64>::BYTES : FwdGeo<128>::BYTES);
+
+// Position of local key kl inside the staged V^T row: blocks of 32 keys, halves of 16, and the
+// slot order of the B operand inside each half.
+__device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
+
+// Stage keys [k0, k0 + span) of one (sequence, head) into LDS; rows up to span_pad are zeroed.
+template <int D>
+__device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
+                         int span, int span_pad, bool softmax) {
+  using G = FwdGeo<D>;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const size_t rs = (size_t)hstride * D;
+  for (int idx = threadIdx.x; idx < span_pad * CPR; idx += kThreads) {
+    const int r = idx / CPR, c = idx % CPR;
+    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (r < span) {
+      kv = *reinterpret_cast<const u32x4*>(kb + r * rs + c * 8);
+      vv = *reinterpret_cast<const u32x4*>(vb + r * rs + c * 8);
+    }
+    *reinterpret_cast<u32x4*>(lds + r * G::KROW + c * 16) = kv;
+    const int pos = vt_pos(r);
+    char* vt = lds + G::OFF_V + pos * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = vv[i];
+      *reinterpret_cast<uint16_t*>(vt + (c * 8 + 2 * i) * G::VROW) = (uint16_t)(w & 0xFFFF);
+      *reinterpret_cast<uint16_t*>(vt + (c * 8 + 2 * i + 1) * G::VROW) = (uint16_t)(w >> 16);
+    }
+  }
+  float* gl = reinterpret_cast<float*>(lds + G::OFF_G);
+  for (int r = threadIdx.x; r < span_pad; r += kThreads) {
+    float t = 0.0f;
+    if (gb != nullptr && r < span) {
+      t = log_sigmoid_f(gb[(size_t)r * hstride]);
+      if (softmax) t *= kLog2e;
+    }
+    gl[r] = t;
+  }
+}
+
+// One wave: QS x 32 query rows starting at row0 (sequence-relative) against local key blocks
+// [kb0, kb1) of the staged range, whose first key has sequence position klo.
+template <int D, int ACT, int QS>
+__device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq, bf16* oseq,
+                         float* lseq, int L, int N, int row0, int klo, int span, int kb0, int kb1) {
+  using G = FwdGeo<D>;
+  const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
+  const int H = gd.num_heads;
+  const size_t rs = (size_t)H * D;
+  constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
+  const float* gl = reinterpret_cast<const float*>(lds + G::OFF_G);
+
+  bf16x8 qf[QS][G::KK];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int row = row0 + qs * 32 + qc;
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (row < L) u = *reinterpret_cast<const u32x4*>(qseq + row * rs + g * (D / 2) + kk * 8);
+      qf[qs][kk] = as_bf16x8(u);
+    }
+  }
+  f32x16 o[QS][G::DT];
+  float m[QS], lsum[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    m[qs] = -__builtin_inff();
+    lsum[qs] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt) o[qs][dt] = f32x16{};
+  }
+  const float sc = softmax ? gd.scale * kLog2e : gd.scale;
+  const int wl = gd.wl, wr = gd.wr;
+
+  for (int kb = kb0; kb < kb1; ++kb) {
+    f32x16 s[QS];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) s[qs] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) {
+      const u32x4 ku = *reinterpret_cast<const u32x4*>(lds + (kb * 32 + qc) * G::KROW + g * D + kk * 16);
+      const bf16x8 kf = as_bf16x8(ku);
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) s[qs] = mfma32(kf, qf[qs][kk], s[qs]);
+    }
+    // element-wise stage: register r of lane (qc, g) is key kb*32 + c_row(r, g), row qs*32 + qc
+    bool full_block = (kb * 32 + 32 <= span);
+    if (wl >= 0 || wr >= 0) {
+      const int kfirst = klo + kb * 32, klast = kfirst + 31;
+      const int rfirst = row0, rlast = row0 + QS * 32 - 1;
+      if (wl >= 0 && kfirst < rlast - wl) full_block = false;
+      if (wr >= 0 && klast > rfirst + wr) full_block = false;
+    }
+    float p[QS][16];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      const int row = row0 + qs * 32 + qc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = kb * 32 + c_row(r, g);
+        float x = __builtin_fmaf(s[qs][r], sc, gl[kl]);
+        bool ok = true;
+        if (!full_block) {
+          const int kpos = klo + kl;
+          ok = kl < span && (wl < 0 || kpos >= row - wl) && (wr < 0 || kpos <= row + wr);
+        }
+        if constexpr (softmax) {
+          p[qs][r] = ok ? x : -__builtin_inff();
+        } else {
+          p[qs][r] = ok ? Act<ACT>::f(x) : 0.0f;
+        }
+      }
+    }
+    if (softmax) {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        float bm = p[qs][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, p[qs][r]);
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mnew = fmaxf(m[qs], bm);
+        const float msafe = mnew == -__builtin_inff() ? 0.0f : mnew;
+        const float alpha = fast_exp2(m[qs] - msafe);
+        float rs_ = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[qs][r] = fast_exp2(p[qs][r] - msafe);
+          rs_ += p[qs][r];
+        }
+        lsum[qs] = lsum[qs] * alpha + rs_;
+        m[qs] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) o[qs][dt] *= alpha;
+      }
+    }
+    // P^T as B operand: k-tile t takes registers 8t..8t+7
+    bf16x8 pf[QS][2];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(p[qs][8 * t + 2 * e], p[qs][8 * t + 2 * e + 1]);
+        pf[qs][t] = as_bf16x8(u);
+      }
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 vu = *reinterpret_cast<const u32x4*>(lds + G::OFF_V + (dt * 32 + out_perm(qc)) * G::VROW +
+                                                         (kb * 32 + t * 16 + g * 8) * 2);
+        const bf16x8 vf = as_bf16x8(vu);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) o[qs][dt] = mfma32(vf, pf[qs][t], o[qs][dt]);
+      }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int row = row0 + qs * 32 + qc;
+    float inv = 1.0f, lse = 0.0f;
+    if (softmax) {
+      const float ltot = lsum[qs] + __shfl_xor(lsum[qs], 32);
+      inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+      lse = ltot > 0.0f ? (m[qs] + __log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
+    }
+    if (row < L) {
+#pragma unroll
+      for (int dt = 0; dt < G::DT; ++dt) {
+        u32x4 u0, u1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u0[e] = pack_bf16x2(o[qs][dt][2 * e] * inv, o[qs][dt][2 * e + 1] * inv);
+          u1[e] = pack_bf16x2(o[qs][dt][8 + 2 * e] * inv, o[qs][dt][8 + 2 * e + 1] * inv);
+        }
+        bf16* dst = oseq + row * rs + dt * 32 + g * 16;
+        *reinterpret_cast<u32x4*>(dst) = u0;
+        *reinterpret_cast<u32x4*>(dst + 8) = u1;
+      }
+      if (softmax && g == 0) lseq[(size_t)row * H] = lse;
+    }
+  }
+  (void)N;
+}
+
+// One work item: all query rows of one (sequence, head).
+template <int D, int ACT, int QS>
+__device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
+  using G = FwdGeo<D>;
+  const int q0 = gd.q_off[b], L = gd.q_off[b + 1] - q0;
+  const int k0 = gd.kv_off[b], N = gd.kv_off[b + 1] - k0;
+  if (L <= 0) return;
+  const int H = gd.num_heads;
+  const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
+  bf16* oseq = reinterpret_cast<bf16*>(gd.o) + ((size_t)q0 * H + h) * D;
+  float* lseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
+  const bf16* kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
+  const bf16* vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;
+  const float* gseq = gd.g ? gd.g + (size_t)k0 * H + h : nullptr;
+  constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
+  const int w = wave_id();
+  constexpr int RW = QS * 32;  // rows per wave tile
+
+  if (N <= G::NKV) {
+    // whole key range resident: stage once, sweep all query tiles
+    const int span_pad = (N + 31) & ~31;
+    stage_kv<D>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
+    __syncthreads();
+    for (int row0 = w * RW; row0 < L; row0 += 4 * RW) {
+      int lo = 0, hi = N - 1;
+      if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
+      if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
+      const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
+      fwd_tile<D, ACT, QS>(lds, gd, qseq, oseq, lseq, L, N, row0, 0, N, kb0, kb1);
+    }
+  } else {
+    // bounded window (both sides >= 0, checked on the host): chunks of kFwdChunkRows rows
+    if (gd.wl < 0 || gd.wr < 0 || gd.wl + gd.wr + kFwdChunkRows > G::NKV) return;  // host-rejected shape
+    for (int r0 = 0; r0 < L; r0 += kFwdChunkRows) {
+      const int klo = r0 - gd.wl > 0 ? r0 - gd.wl : 0;
+      int khi = r0 + kFwdChunkRows + gd.wr;
+      if (khi > N) khi = N;
+      const int span = khi - klo;
+      __syncthreads();  // previous chunk done with LDS
+      stage_kv<D>(lds, kseq + (size_t)klo * H * D, vseq + (size_t)klo * H * D,
+                  gseq ? gseq + (size_t)klo * H : nullptr, H, span, (span + 31) & ~31, softmax);
+      __syncthreads();
+      for (int row0 = r0 + w * RW; row0 < r0 + kFwdChunkRows && row0 < L; row0 += 4 * RW) {
+        int lo = row0 - gd.wl > klo ? row0 - gd.wl : klo;
+        int hi = row0 + RW - 1 + gd.wr < khi - 1 ? row0 + RW - 1 + gd.wr : khi - 1;
+        const int kb0 = (lo - klo) / 32, kb1 = hi >= lo ? (hi - klo) / 32 + 1 : kb0;
+        fwd_tile<D, ACT, QS>(lds, gd, qseq, oseq, lseq, L, N, row0, klo, span, kb0, kb1);
+      }
+    }
+  }
+}
+
+template <int D, int ASET>
+__device__ void fwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
+  const bool chunked = (gd.kv_off[b + 1] - gd.kv_off[b]) > FwdGeo<D>::NKV;
+  constexpr int QS2 = D <= 64 ? 2 : 1;
+  if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
+    if (gd.act == GDPA_ACT_GELU) {
+      if (chunked) fwd_item<D, GDPA_ACT_GELU, 1>(lds, gd, b, h);
+      else fwd_item<D, GDPA_ACT_GELU, QS2>(lds, gd, b, h);
+      return;
+    }
+  if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
+    if (gd.act == GDPA_ACT_SILU) {
+      if (chunked) fwd_item<D, GDPA_ACT_SILU, 1>(lds, gd, b, h);
+      else fwd_item<D, GDPA_ACT_SILU, QS2>(lds, gd, b, h);
+      return;
+    }
+  if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
+    if (gd.act == GDPA_ACT_SOFTMAX) {
+      if (chunked) fwd_item<D, GDPA_ACT_SOFTMAX, 1>(lds, gd, b, h);
+      else fwd_item<D, GDPA_ACT_SOFTMAX, QS2>(lds, gd, b, h);
+    }
+}
+
+template <int DSET, int ASET>
+__global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(LaunchDesc d) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  if ((int)blockIdx.x >= d.n_items) return;
+  int g, h, b;
+  unpack_item(d.items[blockIdx.x], g, h, b);
+  const GroupDesc gd = select_group(d, g);
+  if constexpr ((DSET & kDim32) != 0)
+    if (gd.head_dim == 32) { fwd_dispatch_act<32, ASET>(lds, gd, b, h); return; }
+  if constexpr ((DSET & kDim64) != 0)
+    if (gd.head_dim == 64) { fwd_dispatch_act<64, ASET>(lds, gd, b, h); return; }
+  if constexpr ((DSET & kDim128) != 0)
+    if (gd.head_dim == 128) { fwd_dispatch_act<128, ASET>(lds, gd, b, h); return; }
+}
+
+hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream) {
+  if (d.n_items == 0) return hipSuccess;
+  const dim3 grid(d.n_items), block(kThreads);
+  constexpr int kAll = (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX);
+#define GDPA_LAUNCH(DS, AS) hipLaunchKernelGGL((fwd_bf16_kernel<DS, AS>), grid, block, kFwdLdsBytes, stream, d)
+#define GDPA_LAUNCH_ACTS(DS)                                          \
+  switch (act_set) {                                                  \
+    case 1 << GDPA_ACT_GELU: GDPA_LAUNCH(DS, 1 << GDPA_ACT_GELU); break;  \
+    case 1 << GDPA_ACT_SILU: GDPA_LAUNCH(DS, 1 << GDPA_ACT_SILU); break;  \
+    case 1 << GDPA_ACT_SOFTMAX: GDPA_LAUNCH(DS, 1 << GDPA_ACT_SOFTMAX); break; \
+    default: GDPA_LAUNCH(DS, kAll); break;                            \
+  }
+  switch (dim_set) {
+    case kDim32: GDPA_LAUNCH_ACTS(kDim32); break;
+    case kDim64: GDPA_LAUNCH_ACTS(kDim64); break;
+    case kDim128: GDPA_LAUNCH_ACTS(kDim128); break;
+    case kDim32 | kDim128: GDPA_LAUNCH(kDim32 | kDim128, kAll); break;
+    default: GDPA_LAUNCH(kDim32 | kDim64 | kDim128, kAll); break;
+  }
+#undef GDPA_LAUNCH_ACTS
+#undef GDPA_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace gdpa

@@ -1,0 +1,49 @@
+// Host-side launch entry points of the kernels (internal to libgdpa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdpa_device.hpp"
+
+namespace gdpa {
+
+// Which head dims a launch contains (bit 0: 32, bit 1: 64, bit 2: 128).
+enum DimSet { kDim32 = 1, kDim64 = 2, kDim128 = 4 };
+
+hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream);
+// act_set: bit (1 << act) for every activation present in the launch.
+hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
+// fp32 kernels are flat over (row, head) / (key, head); prefix tables over groups.
+struct Fp32Aux {
+  int64_t row_pre[GDPA_MAX_GROUPS + 1];   // prefix of total_q * H
+  int64_t key_pre[GDPA_MAX_GROUPS + 1];   // prefix of total_kv * H
+  int64_t row_base[GDPA_MAX_GROUPS];      // offset of each group's rows*heads in ws_delta
+  float* ws_delta;                        // softmax backward: D_i per (row, head)
+};
+hipError_t launch_fwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t stream);
+hipError_t launch_bwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t stream);
+
+// Keys of one (sequence, head) whose K and V^T fit in the forward kernel's LDS at once.
+inline constexpr int fwd_kv_capacity(int d) { return 16384 / d; }
+// Rows per window chunk of the forward kernel (4 waves x 32 rows).
+constexpr int kFwdChunkRows = 128;
+// Forward: either every sequence's keys fit at once, or a bounded window whose per-chunk key
+// range [r0 - left, r0 + 128 + right) fits.
+inline bool fwd_shape_ok(int d, int wl, int wr, int max_kv) {
+  const int cap = fwd_kv_capacity(d);
+  if (max_kv <= cap) return true;
+  return wl >= 0 && wr >= 0 && wl + wr + kFwdChunkRows <= cap;
+}
+// Backward: each of the 4 waves owns a block of bwd_key_block(d) keys; query tiles of 64 rows.
+inline constexpr int bwd_key_block(int d) { return d == 128 ? 32 : 64; }
+constexpr int kBwdQueryTile = 64;
+// Either all keys are resident (4 blocks), or a bounded window whose key span for one query
+// tile touches at most 4 blocks.
+inline bool bwd_shape_ok(int d, int wl, int wr, int max_kv) {
+  const int kb = bwd_key_block(d);
+  if (max_kv <= 4 * kb) return true;
+  return wl >= 0 && wr >= 0 && kBwdQueryTile + wl + wr <= 3 * kb + 1;
+}
+
+}  // namespace gdpa

@@ -1,0 +1,145 @@
+/*
+ * gdpa.h - C ABI of the MI355X (gfx950) implementation of generalized dot-product attention.
+ *
+ * The operator (Kunlun paper review, liuzhao09.github.io, section 2.3 "GDPA" and Figure 2;
+ * Kunlun reproduction README, daiwk.github.io, "Core equations"; substack "Kunlun Breakdown",
+ * "The Core Architecture and Mechanics"): per sequence b and head h,
+ *
+ *     S = scale * Q_bh K_bh^T  [+ log sigmoid(G_bh) added to every row]
+ *     O_bh = phi(S) V_bh
+ *
+ * with phi an element-wise activation (GELU, SiLU: the personalized-FFN form, where the keys and
+ * values are per-sample weights generated from the context) or a row softmax (the gated-softmax
+ * form). Self-attention is the case q_offsets == kv_offsets; a sliding window (review, section
+ * 2.5) restricts query position i to key positions i-window_left .. i+window_right.
+ *
+ * Memory and ownership
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates,
+ *     frees or synchronizes; a call validates its arguments on the host, enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *   - Layouts are dense row-major with no strides: q, o, dout, dq are [total_q, H, d]; k, v, dk, dv
+ *     are [total_kv, H, d]; g, dg are [total_kv, H] float32; lse is [total_q, H] float32.
+ *   - q_offsets / kv_offsets are device int32 arrays of num_seqs+1 non-decreasing entries starting
+ *     at 0; sequence b owns rows [offsets[b], offsets[b+1]). They are trusted (not re-validated on
+ *     the device); the host-side hints max_seqlen_q / max_seqlen_kv must bound the real lengths.
+ *   - The workspace `ws` (device memory of at least gdpa_workspace_size() bytes, 256-byte aligned)
+ *     is scratch for the call's work list; its contents on entry are ignored.
+ *   - The library keeps no state between calls; distinct calls may run concurrently on different
+ *     streams as long as they use distinct workspaces and outputs.
+ *
+ * Errors
+ *   Every status check runs synchronously on the host before any HIP call: a non-zero return
+ *   means nothing was enqueued. GDPA_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ *   Faults inside kernels surface on the caller's next synchronization, as usual in HIP.
+ */
+#ifndef GDPA_H_
+#define GDPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDPA_MAX_GROUPS 16
+
+typedef enum gdpa_status {
+  GDPA_OK = 0,
+  GDPA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent window, ... */
+  GDPA_ERR_UNSUPPORTED = -2,      /* valid request outside what the kernels implement */
+  GDPA_ERR_WORKSPACE = -3,        /* workspace missing, misaligned or too small */
+  GDPA_ERR_HIP = -4               /* a kernel launch failed */
+} gdpa_status;
+
+typedef enum gdpa_dtype {
+  GDPA_DTYPE_BF16 = 0, /* q/k/v/o/dout/dq/dk/dv in bfloat16; MFMA with fp32 accumulation */
+  GDPA_DTYPE_FP32 = 1  /* all tensors float32, fp32 arithmetic */
+} gdpa_dtype;
+
+typedef enum gdpa_act {
+  GDPA_ACT_GELU = 0,   /* x * Phi(x), Phi the standard normal CDF */
+  GDPA_ACT_SILU = 1,   /* x * sigmoid(x) */
+  GDPA_ACT_SOFTMAX = 2 /* row softmax over the allowed keys; writes lse */
+} gdpa_act;
+
+/* One GDPA problem (one event group). */
+typedef struct gdpa_problem {
+  int32_t num_seqs;      /* B >= 0 */
+  int32_t num_heads;     /* H, 1..256 */
+  int32_t head_dim;      /* d: 32, 64 or 128 */
+  int32_t dtype;         /* gdpa_dtype */
+  int32_t act;           /* gdpa_act */
+  float scale;           /* multiplies Q K^T (finite) */
+  int32_t window_left;   /* >= 0, or -1 = unbounded; bounded only for self-attention */
+  int32_t window_right;  /* >= 0, or -1 = unbounded; bounded only for self-attention */
+  int64_t total_q;       /* rows of q (= q_offsets[B]) */
+  int64_t total_kv;      /* rows of k and v (= kv_offsets[B]) */
+  int32_t max_seqlen_q;  /* upper bound on any q_offsets[b+1]-q_offsets[b] */
+  int32_t max_seqlen_kv; /* upper bound on any kv_offsets[b+1]-kv_offsets[b] */
+  int32_t self_attention;/* 1: kv_offsets equal q_offsets (same sequences); 0: cross-attention */
+  int32_t reserved;      /* must be 0 */
+  const int32_t* q_offsets;  /* device [B+1] */
+  const int32_t* kv_offsets; /* device [B+1] */
+} gdpa_problem;
+
+/* Device tensors of one problem. Unused entries may be NULL. */
+typedef struct gdpa_tensors {
+  const void* q;     /* [total_q, H, d] */
+  const void* k;     /* [total_kv, H, d] */
+  const void* v;     /* [total_kv, H, d] */
+  const float* g;    /* gate G [total_kv, H] float32, or NULL for no gate */
+  void* o;           /* forward output [total_q, H, d] */
+  float* lse;        /* forward output [total_q, H] natural-log row log-sum-exp; softmax only */
+  const void* dout;  /* backward input: dL/dO [total_q, H, d] */
+  void* dq;          /* backward outputs, same layout and dtype as q, k, v */
+  void* dk;
+  void* dv;
+  float* dg;         /* gate gradient [total_kv, H] float32; NULL if not wanted */
+} gdpa_tensors;
+
+/*
+ * Bytes of workspace needed by one call covering `n_groups` problems (pass: 0 forward,
+ * 1 backward). Returns 0 if the arguments are invalid.
+ */
+size_t gdpa_workspace_size(const gdpa_problem* problems, int32_t n_groups, int32_t pass);
+
+/*
+ * Forward: O = phi(scale Q K^T [+ log sigmoid G]) V for every sequence and head (and lse for the
+ * softmax form). Reads q, k, v (g); writes o (lse). Source: the operator statement above.
+ */
+int gdpa_fwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws, size_t ws_bytes,
+             void* stream);
+
+/*
+ * Backward of the same definition for the upstream gradient dout: writes dq, dk, dv (and dg when
+ * non-NULL). For the softmax form it also reads lse from the forward (o is not needed: the row
+ * term sum_j p_ij dp_ij is recomputed from the scores). Keys that no query sees get zero
+ * gradients. (FlashAttention-style backward that keeps the score matrix on chip:
+ * Kunlun review, section 2.3 / Figure 2.)
+ */
+int gdpa_bwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws, size_t ws_bytes,
+             void* stream);
+
+/*
+ * Grouped forward / backward: `n_groups` (1..GDPA_MAX_GROUPS) independent problems, each with its
+ * own shapes, activation and tensors, in ONE launch of the main kernel (event-level
+ * personalization: each event type gets its own width, head count and depth; Kunlun review,
+ * section 2.5). All problems must share the dtype.
+ */
+int gdpa_fwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups,
+                     void* ws, size_t ws_bytes, void* stream);
+int gdpa_bwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gdpa_strerror(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDPA_H_ */

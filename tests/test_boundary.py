@@ -1,0 +1,187 @@
+"""The C-ABI boundary on the CPU: the library loads, exports what include/gdpa.h declares, its
+structures match the ctypes mirrors, and invalid requests are rejected before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from generalized_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdpa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from generalized_attention_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdpa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header():
+    prog = r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "gdpa.h"
+int main(void) {
+  printf("%zu %zu\n", sizeof(gdpa_problem), sizeof(gdpa_tensors));
+  printf("%zu %zu %zu %zu\n", offsetof(gdpa_problem, total_q), offsetof(gdpa_problem, q_offsets),
+         offsetof(gdpa_problem, kv_offsets), offsetof(gdpa_tensors, dg));
+  return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "t.c")
+        exe = os.path.join(tmp, "t")
+        open(c, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    got = [int(x) for x in out]
+    want = [ctypes.sizeof(_lib.gdpa_problem), ctypes.sizeof(_lib.gdpa_tensors),
+            _lib.gdpa_problem.total_q.offset, _lib.gdpa_problem.q_offsets.offset,
+            _lib.gdpa_problem.kv_offsets.offset, _lib.gdpa_tensors.dg.offset]
+    assert got == want
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation on the host first
+
+
+def good_problem(**kw):
+    p = _lib.gdpa_problem()
+    p.num_seqs, p.num_heads, p.head_dim = 2, 4, 64
+    p.dtype, p.act, p.scale = _lib.GDPA_DTYPE_BF16, _lib.GDPA_ACT_SILU, 1e-3
+    p.window_left = p.window_right = -1
+    p.total_q, p.total_kv = 100, 512
+    p.max_seqlen_q, p.max_seqlen_kv = 60, 256
+    p.self_attention, p.reserved = 0, 0
+    p.q_offsets = p.kv_offsets = FAKE
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def good_tensors(**kw):
+    t = _lib.gdpa_tensors()
+    for f, _ in _lib.gdpa_tensors._fields_:
+        setattr(t, f, 0)
+    t.q = t.k = t.v = t.o = FAKE
+    t.dout = t.dq = t.dk = t.dv = FAKE
+    for k, v in kw.items():
+        setattr(t, k, v)
+    return t
+
+
+def test_workspace_size(lib):
+    n0 = _lib.gdpa_workspace_size([good_problem()], 0)
+    n1 = _lib.gdpa_workspace_size([good_problem()], 1)
+    assert n0 > 0 and n1 >= n0 and n0 % 256 == 0
+    # softmax backward reserves per-row space
+    sm = good_problem(act=_lib.GDPA_ACT_SOFTMAX)
+    assert _lib.gdpa_workspace_size([sm], 1) >= n1
+    assert _lib.gdpa_workspace_size([good_problem(head_dim=48)], 0) == 0
+    assert _lib.gdpa_workspace_size([good_problem()] * 17, 0) == 0  # more than GDPA_MAX_GROUPS
+    assert _lib.gdpa_workspace_size([good_problem()], 2) == 0
+
+
+INVALID_PROBLEMS = [
+    ("negative seqs", dict(num_seqs=-1), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("zero heads", dict(num_heads=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("head dim 48", dict(head_dim=48), _lib.GDPA_ERR_UNSUPPORTED),
+    ("bad dtype", dict(dtype=7), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("bad act", dict(act=3), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("nan scale", dict(scale=float("nan")), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("window below -1", dict(window_left=-2), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("window on cross-attention", dict(window_left=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("reserved set", dict(reserved=1), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("null offsets", dict(q_offsets=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("max len above total", dict(max_seqlen_q=101), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("self-attention with unequal totals", dict(self_attention=1), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("too many keys for bf16", dict(max_seqlen_kv=257, total_kv=600), _lib.GDPA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", INVALID_PROBLEMS, ids=[c[0] for c in INVALID_PROBLEMS])
+def test_invalid_problem_rejected(lib, name, kw, code):
+    for fn in (_lib.gdpa_fwd, _lib.gdpa_bwd):
+        assert fn(good_problem(**kw), good_tensors(), FAKE * 16, 1 << 20, 0) == code
+
+
+INVALID_TENSORS = [
+    ("null q", dict(q=0)),
+    ("misaligned k", dict(k=FAKE + 2)),
+    ("dg without g", dict(dg=FAKE)),
+]
+
+
+@pytest.mark.parametrize("name,kw", INVALID_TENSORS, ids=[c[0] for c in INVALID_TENSORS])
+def test_invalid_tensors_rejected(lib, name, kw):
+    for fn in (_lib.gdpa_fwd, _lib.gdpa_bwd):
+        assert fn(good_problem(), good_tensors(**kw), FAKE * 16, 1 << 20, 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
+
+
+def test_forward_specific_checks(lib):
+    # softmax forward needs lse; forward rejects a dg pointer
+    sm = good_problem(act=_lib.GDPA_ACT_SOFTMAX)
+    assert _lib.gdpa_fwd(sm, good_tensors(), FAKE * 16, 1 << 20, 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
+    assert _lib.gdpa_fwd(good_problem(), good_tensors(g=FAKE, dg=FAKE), FAKE * 16, 1 << 20, 0) == \
+        _lib.GDPA_ERR_INVALID_ARGUMENT
+    # softmax backward needs the forward's lse
+    assert _lib.gdpa_bwd(sm, good_tensors(lse=0), FAKE * 16, 1 << 20, 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_checks(lib):
+    for fn in (_lib.gdpa_fwd, _lib.gdpa_bwd):
+        assert fn(good_problem(), good_tensors(), 0, 1 << 20, 0) == _lib.GDPA_ERR_WORKSPACE
+        assert fn(good_problem(), good_tensors(), FAKE * 16 + 8, 1 << 20, 0) == _lib.GDPA_ERR_WORKSPACE
+        assert fn(good_problem(), good_tensors(), FAKE * 16, 16, 0) == _lib.GDPA_ERR_WORKSPACE
+
+
+def test_window_capacity_rules(lib):
+    # bounded causal window on long self-attention sequences is supported (d=64: left+right <= 128)
+    p = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000, max_seqlen_kv=2000,
+                     window_left=127, window_right=0, act=_lib.GDPA_ACT_SOFTMAX)
+    assert _lib.gdpa_workspace_size([p], 0) > 0
+    assert _lib.gdpa_workspace_size([p], 1) > 0
+    wide = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000, max_seqlen_kv=2000,
+                        window_left=200, window_right=0)
+    assert _lib.gdpa_workspace_size([wide], 0) == 0
+    unbounded = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000,
+                             max_seqlen_kv=2000, window_left=-1, window_right=0)
+    assert _lib.gdpa_workspace_size([unbounded], 0) == 0
+
+
+def test_grouped_requires_same_dtype(lib):
+    a = good_problem()
+    b = good_problem(dtype=_lib.GDPA_DTYPE_FP32)
+    assert _lib.gdpa_fwd_grouped([a, b], [good_tensors(), good_tensors()], FAKE * 16, 1 << 20, 0) == \
+        _lib.GDPA_ERR_INVALID_ARGUMENT
+
+
+def test_strerror_and_version(lib):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(_lib.strerror(code), str)
+    assert lib.gdpa_version() >= 100
+
+
+def test_product_path_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "missing.so"))

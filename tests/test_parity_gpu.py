@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Sizes are reduced versions of the five workloads that the oracle finishes in seconds while still
+spanning several tiles and ragged tails (lengths 0, 1, tile-1, tile, tile+1, ...), plus the full
+workload sizes compared on sampled sequences (sequences are independent, so the oracle runs on
+the sampled subset). Tolerances: see gpu_harness.py.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gdpa_workloads import make_workload
+from gpu_harness import check, device_group, rows_of, to64
+
+import generalized_attention_amd as ga
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENGTHS = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300]
+
+
+def run_fwd(groups_dev):
+    if len(groups_dev) == 1:
+        return [ga.gdpa_fwd(groups_dev[0])]
+    return ga.gdpa_fwd_grouped(groups_dev)
+
+
+def run_bwd(groups_dev, douts, fwd_outs, want_dg):
+    if len(groups_dev) == 1:
+        o, lse = fwd_outs[0]
+        return [ga.gdpa_bwd(groups_dev[0], douts[0], o=o, lse=lse, want_dg=want_dg)]
+    return ga.gdpa_bwd_grouped(groups_dev, douts, fwd_outs=fwd_outs, want_dg=want_dg)
+
+
+def compare_workload(w, passes, sample=None, want_dg=True, scale=None):
+    """Run the workload on the GPU; compare all (or the sampled) sequences with the oracle."""
+    groups = w.groups
+    if scale is not None:
+        import dataclasses
+        for g in groups:
+            g.spec = dataclasses.replace(g.spec, scale=scale)
+    dev = [device_group(g) for g in groups]
+    print(f"[gpu] {w.name} seed={w.seed} groups={len(groups)} T={[g.total_q for g in groups][:3]} "
+          f"passes={passes}", flush=True)
+    fwd_outs = run_fwd(dev)
+    torch.cuda.synchronize()
+    bwd_outs = None
+    if "bwd" in passes:
+        douts = [g.dout.to("cuda:0") for g in groups]
+        bwd_outs = run_bwd(dev, douts, fwd_outs, want_dg)
+        torch.cuda.synchronize()
+    report = {}
+    failures = []
+
+    def chk(*a):
+        try:
+            return check(*a)
+        except AssertionError as e:
+            failures.append(str(e))
+            return float("nan")
+
+    for gi, g in enumerate(groups):
+        seqs = list(range(g.spec.num_seqs)) if sample is None else sample(g)
+        sub = g.subset(seqs)
+        qr = rows_of(g.q_offsets, seqs)
+        kr = rows_of(g.kv_offsets, seqs)
+        dt = g.spec.dtype
+        ref = oracle.group_fwd(sub)
+        o, lse = fwd_outs[gi]
+        report[f"g{gi}.o"] = chk(dt, to64(o)[qr], ref["o"], f"{w.name} g{gi} O")
+        if g.spec.act == "softmax":
+            lg = to64(lse)[qr]
+            fin = np.isfinite(ref["lse"])
+            assert np.array_equal(fin, np.isfinite(lg))
+            assert np.max(np.abs(lg[fin] - ref["lse"][fin]), initial=0.0) < 2e-3 * max(1.0, np.abs(ref["lse"][fin]).max(initial=1.0))
+        if bwd_outs is not None:
+            rb = oracle.group_bwd(sub, want_dg=want_dg and g.g is not None)
+            gb = bwd_outs[gi]
+            report[f"g{gi}.dq"] = chk(dt, to64(gb["dq"])[qr], rb["dq"], f"{w.name} g{gi} dQ")
+            report[f"g{gi}.dk"] = chk(dt, to64(gb["dk"])[kr], rb["dk"], f"{w.name} g{gi} dK")
+            report[f"g{gi}.dv"] = chk(dt, to64(gb["dv"])[kr], rb["dv"], f"{w.name} g{gi} dV")
+            if "dg" in gb:
+                # gate gradient in fp32: same relative-to-RMS rule (it is a sum over a column of dS)
+                ref_dg = rb["dg"]
+                err = np.abs(to64(gb["dg"])[kr] - ref_dg)
+                rms = math.sqrt(float(np.mean(ref_dg ** 2))) if ref_dg.size else 0.0
+                if not err.max(initial=0.0) <= 2e-2 * rms + 1e-7:
+                    failures.append(f"{w.name} g{gi} dG: max err {err.max():.3e} rms {rms:.3e}")
+    print(f"[gpu] {w.name} literal max|err|/RMS: " + ", ".join(f"{k}={v:.4f}" for k, v in report.items()), flush=True)
+    assert not failures, "\n".join(failures)
+    return report
+
+
+# ------------------------------------------------------------------------------------------------
+# Reduced sizes, all sequences compared
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cfg0_fp32_forward(seed):
+    compare_workload(make_workload("cfg0", seed), ("fwd",))
+
+
+@pytest.mark.parametrize("scale", [1.0, 1.0 / math.sqrt(32)])
+def test_cfg0_fp32_forward_scales(scale):
+    compare_workload(make_workload("cfg0", 0), ("fwd",), scale=scale)
+
+
+def test_cfg0_fp32_backward():
+    compare_workload(make_workload("cfg0", 0), ("fwd", "bwd"))
+
+
+@pytest.mark.parametrize("seed,scale", [(0, None), (1, None), (2, 1.0 / 8)])
+def test_cfg2_reduced(seed, scale):
+    w = make_workload("cfg2", seed, num_seqs=10, len_range=(1, 700))
+    compare_workload(w, ("fwd", "bwd"), scale=scale)
+
+
+def test_cfg2_edge_lengths():
+    w = make_workload("cfg2", 3, lengths=EDGE_LENGTHS)
+    compare_workload(w, ("fwd", "bwd"), scale=1.0 / 8)
+
+
+def test_cfg1_gelu_variant():
+    # same shapes with the other element-wise activation
+    w = make_workload("cfg1", 4, num_seqs=6, len_range=(1, 400), act="gelu")
+    compare_workload(w, ("fwd", "bwd"), scale=1.0 / 8)
+
+
+FEATURES = [
+    ("softmax", False, (-1, -1)), ("softmax", True, (-1, -1)), ("softmax", False, (127, 0)),
+    ("softmax", True, (127, 0)), ("silu", False, (127, 0)), ("gelu", True, (20, 9)), ("softmax", True, (64, 64)),
+]
+
+
+@pytest.mark.parametrize("act,gate,window", FEATURES, ids=[f"{a}-g{int(g)}-w{w[0]}_{w[1]}" for a, g, w in FEATURES])
+def test_self_attention_features(act, gate, window):
+    """Self-attention forms on short sequences (all keys resident) and with windows."""
+    import dataclasses
+    lens = [1, 5, 64, 100, 200, 256] if window == (-1, -1) else [1, 5, 64, 100, 200, 256, 300, 700]
+    w = make_workload("cfg3", 7, lengths=lens, act=act, window=window)
+    g = w.groups[0]
+    if not gate:
+        g.g = None
+    g.spec = dataclasses.replace(g.spec, gate=gate)
+    compare_workload(w, ("fwd", "bwd"), want_dg=gate)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_cfg3_reduced(seed):
+    w = make_workload("cfg3", seed, num_seqs=5, len_range=(1, 900))
+    compare_workload(w, ("fwd", "bwd"))
+
+
+def test_cfg3_edge_lengths():
+    w = make_workload("cfg3", 2, lengths=EDGE_LENGTHS + [255, 256, 257, 600])
+    compare_workload(w, ("fwd", "bwd"))
+
+
+def test_cfg4_reduced():
+    w = make_workload("cfg4", 0, num_seqs=3, len_range=(1, 400))
+    compare_workload(w, ("fwd", "bwd"), scale=None)
+
+
+def test_cfg4_reduced_scale_sqrt_d():
+    w = make_workload("cfg4", 1, num_seqs=2, len_range=(1, 300))
+    for g in w.groups:
+        import dataclasses
+        g.spec = dataclasses.replace(g.spec, scale=1.0 / math.sqrt(g.spec.head_dim))
+    compare_workload(w, ("fwd", "bwd"))
+
+
+# ------------------------------------------------------------------------------------------------
+# Full workload sizes, sampled sequences (longest, shortest and random ones)
+# ------------------------------------------------------------------------------------------------
+
+def _sampler(k, seed=0):
+    def pick(g):
+        lens = g.lengths_q
+        rng = np.random.default_rng(seed)
+        chosen = {int(np.argmax(lens)), int(np.argmin(lens))}
+        chosen.update(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
+        return sorted(chosen)
+    return pick
+
+
+def test_cfg2_full_size_sampled():
+    compare_workload(make_workload("cfg2", 0), ("fwd", "bwd"), sample=_sampler(6))
+
+
+def test_cfg3_full_size_sampled():
+    compare_workload(make_workload("cfg3", 0), ("fwd", "bwd"), sample=_sampler(3))
+
+
+def test_cfg4_full_size_sampled():
+    compare_workload(make_workload("cfg4", 0), ("fwd", "bwd"), sample=_sampler(1))
+
+
+# ------------------------------------------------------------------------------------------------
+# Properties of the HIP path itself
+# ------------------------------------------------------------------------------------------------
+
+def test_outputs_fully_overwritten_and_deterministic():
+    w = make_workload("cfg3", 5, lengths=[0, 1, 70, 200, 3])
+    g = w.groups[0]
+    dev = device_group(g)
+    o = torch.full_like(dev.q, float("nan"))
+    lse = torch.full((dev.q.shape[0], dev.q.shape[1]), float("nan"), device="cuda:0")
+    ga.gdpa_fwd(dev, o=o, lse=lse)
+    dout = g.dout.to("cuda:0")
+    outs = [torch.full_like(t, float("nan")) for t in (dev.q, dev.k, dev.v)] + [torch.full_like(dev.g, float("nan"))]
+    r1 = ga.gdpa_bwd(dev, dout, o=o, lse=lse, want_dg=True, out=tuple(outs))
+    torch.cuda.synchronize()
+    for name, t in [("o", o), ("lse", lse)] + list(r1.items()):
+        assert not torch.isnan(t).any(), name
+    r2 = ga.gdpa_bwd(dev, dout, o=o, lse=lse, want_dg=True)
+    o2, _ = ga.gdpa_fwd(dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_sample_independence():
+    w = make_workload("cfg2", 6, num_seqs=4, len_range=(50, 300))
+    g = w.groups[0]
+    dev = device_group(g)
+    o1, _ = ga.gdpa_fwd(dev)
+    k2 = dev.k.clone()
+    k2[g.kv_offsets[1]:g.kv_offsets[2]] *= -1  # perturb sequence 1 only
+    dev2 = device_group(g)
+    dev2.k = k2
+    o2, _ = ga.gdpa_fwd(dev2)
+    torch.cuda.synchronize()
+    r0 = slice(int(g.q_offsets[0]), int(g.q_offsets[1]))
+    r1 = slice(int(g.q_offsets[1]), int(g.q_offsets[2]))
+    assert torch.equal(o1[r0], o2[r0])
+    assert not torch.equal(o1[r1], o2[r1])
