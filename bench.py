@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark the GDPA hot path on one MI355X and print one JSON line.
+
+A step is one pass of the whole path over one batch of the workload: the jagged work
+decomposition (gdpa_plan), the forward and the backward (dQ, dK, dV), with inputs resident in
+HBM. The default workload is the personalized-FFN form in bf16, forward+backward: B=256
+sequences with lengths uniform in [100, 1000], H=4, d=64, n=256 context-generated keys per
+sample, SiLU, scale 1/1000 (seed 0 of the input recipe; synthetic data).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_sched.hip", "gdpa_api.cpp",
+                  "gdpa_launch.hpp"]
+
+WORKLOAD_TEXT = {
+    "cfg1": "PFFN-form GDPA bf16 forward: B=256, L~U[100,1000], H=4, d=64, n=256 context-generated "
+            "keys/values, SiLU, scale 1/1000",
+    "cfg2": "PFFN-form GDPA bf16 forward+backward (dQ, dK, dV): B=256, L~U[100,1000], H=4, d=64, n=256 "
+            "context-generated keys/values, SiLU, scale 1/1000, upstream gradient N(0,1)",
+    "cfg3": "gated-softmax self-attention bf16 forward+backward: B=128, L~U[200,2000], H=8, d=64, "
+            "scale 1/8, log-sigmoid gate, causal window 128",
+    "cfg4": "10 event groups in one launch, bf16 forward+backward: B=64 each, L~U[100,1000], n=32, "
+            "groups 0-4 H=8 d=128, groups 5-9 H=2 d=32, GELU",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "generalized_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on the
+    current kernel sources; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(workload, passes, seqs: int):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+    import oracle
+    from gdpa_workloads import group_work
+
+    threads = min(os.cpu_count() or 1, 16)
+    rng = np.random.default_rng(123)
+    flops = 0.0
+    elapsed = 0.0
+    picked = 0
+    for g in workload.groups:
+        k = max(1, min(g.spec.num_seqs, int(round(seqs * g.spec.num_seqs / sum(x.spec.num_seqs for x in workload.groups)))))
+        sub = g.subset(sorted(rng.choice(g.spec.num_seqs, size=k, replace=False).tolist()))
+        picked += k
+        wk = group_work(sub)
+        t0 = time.perf_counter()
+        oracle.group_fwd(sub, nthreads=threads)
+        if "bwd" in passes:
+            oracle.group_bwd(sub, nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        flops += wk["fwd_flops"] + (wk["bwd_flops"] if "bwd" in passes else 0.0)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{picked} sequences drawn from the same workload (seeded), fwd{'+bwd' if 'bwd' in passes else ''}, "
+                      f"{elapsed:.1f} s, {flops / 1e9:.2f} GFLOP of model work"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seqs", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device-to-device copy (scales HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the GDPA path has no "
+              f"cross-GPU step and is run per GPU on its share of the batch.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        n = 512 << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+    import generalized_attention_amd as ga
+    from gdpa_workloads import make_workload, workload_work
+
+    w = make_workload(args.workload, args.seed)
+    passes = w.passes
+    work = workload_work(w)
+    dev = torch.device("cuda:0")
+    groups = []
+    for g in w.groups:
+        s = g.spec
+        groups.append(ga.make_group(g.q.to(dev), g.k.to(dev), g.v.to(dev), g.q_offsets, g.kv_offsets, act=s.act,
+                                    scale=s.scale, window=s.window, g=None if g.g is None else g.g.to(dev),
+                                    self_attention=s.keys_per_seq is None, lengths_q=g.lengths_q.tolist(),
+                                    lengths_kv=g.lengths_kv.tolist()))
+    douts = [g.dout.to(dev) for g in w.groups]
+    ws = ga.workspace(groups, 1 if "bwd" in passes else 0)
+    planned = [ga.GroupArgs(**{**gr.__dict__, "planned": True}) for gr in groups]
+    fwd_outs = [ga.ops._alloc_fwd(gr) for gr in groups]
+    bwd_outs = [ga.ops._alloc_bwd(gr, want_dg=gr.g is not None) for gr in groups]
+    single = len(groups) == 1
+
+    def plan():
+        ga.gdpa_plan(groups, ws)
+
+    def fwd():
+        if single:
+            ga.gdpa_fwd(planned[0], o=fwd_outs[0][0], lse=fwd_outs[0][1], ws=ws)
+        else:
+            ga.gdpa_fwd_grouped(planned, outs=fwd_outs, ws=ws)
+
+    def bwd():
+        if single:
+            ga.gdpa_bwd(planned[0], douts[0], o=fwd_outs[0][0], lse=fwd_outs[0][1], out=bwd_outs[0], ws=ws)
+        else:
+            ga.gdpa_bwd_grouped(planned, douts, fwd_outs=fwd_outs, outs=bwd_outs, ws=ws)
+
+    def step():
+        plan()
+        fwd()
+        if "bwd" in passes:
+            bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: events only at the ends of the timed region
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel timing: an event between consecutive launches (same stream as the kernels)
+    n_ev = 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record()
+        plan()
+        evs[i][1].record()
+        fwd()
+        evs[i][2].record()
+        if "bwd" in passes:
+            bwd()
+        evs[i][3].record()
+    torch.cuda.synchronize()
+    k_ms = {"plan": 0.0, "fwd": 0.0, "bwd": 0.0}
+    for e in evs:
+        k_ms["plan"] += e[0].elapsed_time(e[1]) / args.steps
+        k_ms["fwd"] += e[1].elapsed_time(e[2]) / args.steps
+        k_ms["bwd"] += e[2].elapsed_time(e[3]) / args.steps
+    for o in fwd_outs + [tuple(b[:3]) for b in bwd_outs]:
+        for t in o:
+            if t is not None and not torch.isfinite(t).all():
+                raise RuntimeError("non-finite output")
+
+    flops = work["fwd_flops"] + (work["bwd_flops"] if "bwd" in passes else 0.0)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    dominant = "bwd" if ("bwd" in passes and k_ms["bwd"] >= k_ms["fwd"]) else "fwd"
+    kbytes = work[f"{dominant}_bytes"]
+    kflops = work[f"{dominant}_flops"]
+    ridge = MFMA_PEAK_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    kms = k_ms[dominant]
+    if kflops / kbytes < ridge:
+        roof = {"bound": "hbm", "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": kflops / (kms * 1e-3) / 1e12, "peak": MFMA_PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(args.workload, dominant)
+    roof["kernel"] = f"gdpa_{dominant} main kernel ({dominant}_bf16_kernel)"
+    roof["kernel_ms"] = kms
+    roof["algorithmic_bytes"] = kbytes
+    roof["algorithmic_flops"] = kflops
+    roof["mfma_frac"] = kflops / (kms * 1e-3) / 1e12 / MFMA_PEAK_BF16_TFLOPS
+
+    out = {
+        "metric": "GDPA fwd+bwd bf16 TFLOP/s and % of MI355X MFMA peak, jagged L<=1000",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                   "global_batch": sum(g.spec.num_seqs for g in w.groups),
+                   "seq_len": "jagged", "total_rows": sum(g.total_q for g in w.groups),
+                   "score_entries": work["entries"], "model_gflop_per_step": flops / 1e9,
+                   "seed": args.seed},
+        "pct_of_mfma_peak": 100.0 * tflops / MFMA_PEAK_BF16_TFLOPS,
+        "hbm_gbps_step": (work["fwd_bytes"] + (work["bwd_bytes"] if "bwd" in passes else 0.0)) / (ms_per_step * 1e-3) / 1e9,
+        "kernel_ms": k_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, passes, args.cpu_seqs)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,5 +13,7 @@ from .ops import (  # noqa: F401
     gdpa_bwd_grouped,
     gdpa_fwd,
     gdpa_fwd_grouped,
+    gdpa_plan,
     make_group,
+    workspace,
 )

@@ -26,9 +26,10 @@ GDPA_ACT_SILU = 1
 GDPA_ACT_SOFTMAX = 2
 
 GDPA_MAX_GROUPS = 16
+GDPA_FLAG_PLANNED = 1
 
-EXPORTED = ("gdpa_workspace_size", "gdpa_fwd", "gdpa_bwd", "gdpa_fwd_grouped", "gdpa_bwd_grouped",
-            "gdpa_strerror", "gdpa_version")
+EXPORTED = ("gdpa_workspace_size", "gdpa_plan", "gdpa_fwd", "gdpa_bwd", "gdpa_fwd_grouped",
+            "gdpa_bwd_grouped", "gdpa_strerror", "gdpa_version")
 
 
 class gdpa_problem(ctypes.Structure):
@@ -46,7 +47,7 @@ class gdpa_problem(ctypes.Structure):
         ("max_seqlen_q", ctypes.c_int32),
         ("max_seqlen_kv", ctypes.c_int32),
         ("self_attention", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("q_offsets", ctypes.c_void_p),
         ("kv_offsets", ctypes.c_void_p),
     ]
@@ -97,6 +98,8 @@ def load(path: str = LIB_PATH):
         f.argtypes = [P(gdpa_problem), P(gdpa_tensors), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                       ctypes.c_void_p]
         f.restype = ctypes.c_int
+    lib.gdpa_plan.argtypes = [P(gdpa_problem), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.gdpa_plan.restype = ctypes.c_int
     lib.gdpa_strerror.argtypes = [ctypes.c_int]
     lib.gdpa_strerror.restype = ctypes.c_char_p
     lib.gdpa_version.argtypes = []
@@ -119,6 +122,12 @@ def _call_grouped(fn, problems, tensors, ws, ws_bytes, stream):
     pa = (gdpa_problem * n)(*problems)
     ta = (gdpa_tensors * n)(*tensors)
     return fn(pa, ta, n, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
+
+
+def gdpa_plan(problems, ws, ws_bytes, stream) -> int:
+    n = len(problems)
+    pa = (gdpa_problem * n)(*problems)
+    return load().gdpa_plan(pa, n, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
 
 
 def gdpa_fwd(problem, tensors, ws, ws_bytes, stream) -> int:

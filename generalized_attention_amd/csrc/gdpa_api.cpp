@@ -32,7 +32,7 @@ int check_problem(const gdpa_problem& p) {
   if (p.act < GDPA_ACT_GELU || p.act > GDPA_ACT_SOFTMAX) return GDPA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p.scale)) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.window_left < -1 || p.window_right < -1) return GDPA_ERR_INVALID_ARGUMENT;
-  if (p.reserved != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((p.flags & ~GDPA_FLAG_PLANNED) != 0) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.self_attention != 0 && p.self_attention != 1) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.total_q < 0 || p.total_kv < 0 || p.max_seqlen_q < 0 || p.max_seqlen_kv < 0)
     return GDPA_ERR_INVALID_ARGUMENT;
@@ -51,10 +51,9 @@ int check_problem(const gdpa_problem& p) {
   return GDPA_OK;
 }
 
-int check_backward_capacity(const gdpa_problem& p) {
+int check_backward_capacity(const gdpa_problem& p, int waves) {
   if (p.dtype != GDPA_DTYPE_BF16) return GDPA_OK;
-  return bwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK
-                                                                                   : GDPA_ERR_UNSUPPORTED;
+  return bwd_shape_ok(waves, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK : GDPA_ERR_UNSUPPORTED;
 }
 
 int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
@@ -78,11 +77,13 @@ int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
 int layout(const gdpa_problem* ps, int n_groups, int pass, WsLayout* L) {
   if (!ps || n_groups < 1 || n_groups > GDPA_MAX_GROUPS) return GDPA_ERR_INVALID_ARGUMENT;
   if (pass != 0 && pass != 1) return GDPA_ERR_INVALID_ARGUMENT;
+  bool has128 = false;
+  for (int g = 0; g < n_groups; ++g) has128 |= ps[g].head_dim == 128;
   for (int g = 0; g < n_groups; ++g) {
     int rc = check_problem(ps[g]);
     if (rc != GDPA_OK) return rc;
-    if (pass == 1 && (rc = check_backward_capacity(ps[g])) != GDPA_OK) return rc;
-    if (ps[g].dtype != ps[0].dtype) return GDPA_ERR_INVALID_ARGUMENT;
+    if (pass == 1 && (rc = check_backward_capacity(ps[g], bwd_waves_for(has128))) != GDPA_OK) return rc;
+    if (ps[g].dtype != ps[0].dtype || ps[g].flags != ps[0].flags) return GDPA_ERR_INVALID_ARGUMENT;
     L->n_items += (int64_t)ps[g].num_seqs * ps[g].num_heads;
     L->n_seqs += ps[g].num_seqs;
     L->delta_base[g] = L->delta_rows;
@@ -178,7 +179,7 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
     aux.ws_delta = reinterpret_cast<float*>(static_cast<char*>(ws) + L.delta);
     e = pass == 0 ? launch_fwd_fp32(d, aux, s) : launch_bwd_fp32(d, aux, s);
   } else {
-    e = launch_schedule(d, s);
+    e = (ps[0].flags & GDPA_FLAG_PLANNED) ? hipSuccess : launch_schedule(d, s);
     if (e == hipSuccess) {
       const int dims = dim_set_of(ps, n_groups);
       int acts = 0;
@@ -216,6 +217,19 @@ int gdpa_fwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, 
 int gdpa_bwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups, void* ws,
                      size_t ws_bytes, void* stream) {
   return gdpa::run(problems, tensors, n_groups, ws, ws_bytes, stream, 1);
+}
+
+int gdpa_plan(const gdpa_problem* problems, int32_t n_groups, void* ws, size_t ws_bytes, void* stream) {
+  gdpa::WsLayout L;
+  int rc = gdpa::layout(problems, n_groups, 0, &L);
+  if (rc != GDPA_OK) return rc;
+  if (!ws || ((uintptr_t)ws % gdpa::kAlign) != 0 || ws_bytes < L.total) return GDPA_ERR_WORKSPACE;
+  if (L.n_items == 0 || problems[0].dtype != GDPA_DTYPE_BF16) return GDPA_OK;  // fp32 kernels need no list
+  gdpa::LaunchDesc d;
+  gdpa_tensors none[GDPA_MAX_GROUPS];
+  std::memset(none, 0, sizeof(none));
+  gdpa::fill_desc(problems, none, n_groups, ws, L, &d);
+  return gdpa::launch_schedule(d, static_cast<hipStream_t>(stream)) == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
 }
 
 const char* gdpa_strerror(int status) {

@@ -92,6 +92,25 @@ __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16: A (16 x 32): lane l holds row l%16, k-slots (l/16)*8 + e;
+// B (32 x 16): lane l holds column l%16, k-slots (l/16)*8 + e; C (16 x 16): lane l holds column
+// l%16, register r holds row (l/16)*4 + r.
+__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane j supplies the
+// address of 4 consecutive 16-bit values, forming row j of a 16 x 4 matrix M; lane i receives
+// M[(i >> 2) + 4e][i & 3] for e = 0..3. Choosing row j = (4 consecutive columns starting at
+// c0 + 4 (j & 3)) of line l0 + (j >> 2) therefore gives lane i the 4 values of column c0 + i on
+// lines l0 .. l0+3: a column read out of a row-major tile.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 lds_read_tr16(const char* lds, int byte_offset) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + byte_offset));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // C-register -> row mapping of a 32x32 MFMA result, for lane half g = lane/32.
 __device__ __host__ inline constexpr int c_row(int r, int g) { return (r / 4) * 8 + g * 4 + (r % 4); }
 
@@ -111,9 +130,12 @@ __device__ __host__ inline constexpr int out_perm(int m) { return ((m >> 2) & 1)
 // ----------------------------------------------------------------------------------------------
 // bf16 helpers (round to nearest even; gfx950 has a packed convert instruction)
 // ----------------------------------------------------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// One v_cvt_pk_bf16_f32 (round to nearest even) for two values; a is the low half.
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  bf16 x = (bf16)a, y = (bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 __device__ inline float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ inline float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
@@ -138,36 +160,40 @@ __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 // sigmoid(z) given t = -z*log2(e)
 __device__ inline float sigmoid_from_t(float t) { return fast_rcp(1.0f + fast_exp2(t)); }
 
+// Both element-wise activations are x * g(x) with g(x) = sigmoid(a1 x + a3 x^3):
+//   SiLU: a1 = 1, a3 = 0 (exact);  GELU: a1 = 1.5976, a3 = 0.07056 (Phi approximation above).
+// The kernels evaluate g through t = -log2(e) (a1 x + a3 x^3) = x (c1 + c3 x^2), so that with the
+// score scale folded into c1, c3 a raw accumulator s gives phi(scale s) / scale = s g(scale s).
 template <int ACT>
-struct Act;
-
-template <>
-struct Act<GDPA_ACT_SILU> {
-  // value and derivative; x is the scaled score
-  __device__ static inline float f(float x) { return x * sigmoid_from_t(-kLog2e * x); }
-  __device__ static inline void fg(float x, float& p, float& dp) {
-    float s = sigmoid_from_t(-kLog2e * x);
-    p = x * s;
-    dp = s + p * (1.0f - s);  // s (1 + x (1 - s))
+struct PointAct {
+  static constexpr float a1 = ACT == GDPA_ACT_GELU ? 1.5976f : 1.0f;
+  static constexpr float a3 = ACT == GDPA_ACT_GELU ? 0.07056f : 0.0f;
+  // coefficients of t for an argument that is `scale` times the variable passed in
+  __device__ static inline void coeffs(float scale, float& c1, float& c3) {
+    c1 = -kLog2e * a1 * scale;
+    c3 = -kLog2e * a3 * scale * scale * scale;
   }
-};
-
-template <>
-struct Act<GDPA_ACT_GELU> {
-  // z = 1.5976 x + 0.07056 x^3; Phi ~ sigmoid(z); Phi'(x) = phi(x) approximated by the
-  // derivative of the same logistic form: sigmoid(z)(1-sigmoid(z)) (1.5976 + 3*0.07056 x^2).
-  __device__ static inline float f(float x) {
-    float x2 = x * x;
-    float t = x * __builtin_fmaf(x2, -0.07056f * kLog2e, -1.5976f * kLog2e);
-    return x * sigmoid_from_t(t);
+  __device__ static inline float t_of(float x, float c1, float c3) {
+    if constexpr (ACT == GDPA_ACT_SILU) return x * c1;
+    else return x * __builtin_fmaf(x * x, c3, c1);
   }
-  __device__ static inline void fg(float x, float& p, float& dp) {
-    float x2 = x * x;
-    float t = x * __builtin_fmaf(x2, -0.07056f * kLog2e, -1.5976f * kLog2e);
-    float s = sigmoid_from_t(t);
-    p = x * s;
-    float dz = __builtin_fmaf(x2, 3.0f * 0.07056f, 1.5976f);
-    dp = s + x * s * (1.0f - s) * dz;
+  // x * g(x') where x' = scale * x is encoded in c1, c3
+  __device__ static inline float value(float x, float c1, float c3) {
+    return x * fast_rcp(1.0f + fast_exp2(t_of(x, c1, c3)));
+  }
+  // value p = x g and derivative phi'(x') = g + x' g (1 - g)(a1 + 3 a3 x'^2), for x' = scale x
+  __device__ static inline void value_grad(float x, float scale, float c1, float c3, float& p, float& dphi) {
+    const float e = fast_exp2(t_of(x, c1, c3));
+    const float g = fast_rcp(1.0f + e);
+    p = x * g;
+    const float omg = e * g;  // 1 - g
+    if constexpr (ACT == GDPA_ACT_SILU) {
+      dphi = __builtin_fmaf(p * scale, omg, g);
+    } else {
+      const float xs = x * scale;
+      const float k = __builtin_fmaf(xs * xs, 3.0f * a3, a1);
+      dphi = __builtin_fmaf(p * scale * omg, k, g);
+    }
   }
 };
 
@@ -177,6 +203,8 @@ __device__ inline float log_sigmoid_f(float g) {
 }
 
 __device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
-__device__ inline int wave_id() { return (int)(threadIdx.x >> 6); }
+// The wave index is the same on every lane; readfirstlane puts it (and everything derived from
+// it) in scalar registers, so tests on it become scalar branches instead of exec-masked ones.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 }  // namespace gdpa

@@ -113,6 +113,13 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq,
   }
   const float sc = softmax ? gd.scale * kLog2e : gd.scale;
   const int wl = gd.wl, wr = gd.wr;
+  const bool windowed = wl >= 0 || wr >= 0;
+  const bool has_gate = gd.g != nullptr;
+  // element-wise forms: without a gate p' = s g(scale s) = phi(scale s) / scale and O is scaled
+  // once in the epilogue; with a gate the argument scale s + log sigmoid(G) is formed first.
+  float c1 = 0.0f, c3 = 0.0f;
+  if constexpr (!softmax) PointAct<ACT>::coeffs(has_gate ? 1.0f : gd.scale, c1, c3);
+  const float out_scale = (!softmax && !has_gate) ? gd.scale : 1.0f;
 
   for (int kb = kb0; kb < kb1; ++kb) {
     f32x16 s[QS];
@@ -125,35 +132,49 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq,
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) s[qs] = mfma32(kf, qf[qs][kk], s[qs]);
     }
-    // element-wise stage: register r of lane (qc, g) is key kb*32 + c_row(r, g), row qs*32 + qc
+    // element-wise stage: register r of lane (qc, g) is key kb*32 + c_row(r, g), row qs*32 + qc.
+    // Padded keys (beyond the staged range) have zero K and V rows in LDS, so the element-wise
+    // forms need a mask only inside a window; the softmax form also masks the padded keys.
     bool full_block = (kb * 32 + 32 <= span);
-    if (wl >= 0 || wr >= 0) {
+    if (windowed) {
       const int kfirst = klo + kb * 32, klast = kfirst + 31;
       const int rfirst = row0, rlast = row0 + QS * 32 - 1;
       if (wl >= 0 && kfirst < rlast - wl) full_block = false;
       if (wr >= 0 && klast > rfirst + wr) full_block = false;
     }
     float p[QS][16];
+    if (has_gate) {
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      const int row = row0 + qs * 32 + qc;
+      for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = kb * 32 + c_row(r, g);
-        float x = __builtin_fmaf(s[qs][r], sc, gl[kl]);
-        bool ok = true;
-        if (!full_block) {
-          const int kpos = klo + kl;
-          ok = kl < span && (wl < 0 || kpos >= row - wl) && (wr < 0 || kpos <= row + wr);
+        for (int r = 0; r < 16; ++r) {
+          const float x = __builtin_fmaf(s[qs][r], sc, gl[kb * 32 + c_row(r, g)]);
+          if constexpr (softmax) p[qs][r] = x;
+          else p[qs][r] = PointAct<ACT>::value(x, c1, c3);
         }
-        if constexpr (softmax) {
-          p[qs][r] = ok ? x : -__builtin_inff();
-        } else {
-          p[qs][r] = ok ? Act<ACT>::f(x) : 0.0f;
+    } else {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (softmax) p[qs][r] = s[qs][r] * sc;
+          else p[qs][r] = PointAct<ACT>::value(s[qs][r], c1, c3);
+        }
+    }
+    if (!full_block && (softmax || windowed)) {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        const int row = row0 + qs * 32 + qc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kl = kb * 32 + c_row(r, g);
+          const int kpos = klo + kl;
+          const bool ok = (kl < span) & ((wl < 0) | (kpos >= row - wl)) & ((wr < 0) | (kpos <= row + wr));
+          p[qs][r] = ok ? p[qs][r] : (softmax ? -__builtin_inff() : 0.0f);
         }
       }
     }
-    if (softmax) {
+    if constexpr (softmax) {
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
         float bm = p[qs][0];
@@ -202,7 +223,7 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq,
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
     const int row = row0 + qs * 32 + qc;
-    float inv = 1.0f, lse = 0.0f;
+    float inv = out_scale, lse = 0.0f;
     if (softmax) {
       const float ltot = lsum[qs] + __shfl_xor(lsum[qs], 32);
       inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
@@ -308,7 +329,9 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(LaunchDesc d) {
   if ((int)blockIdx.x >= d.n_items) return;
   int g, h, b;
   unpack_item(d.items[blockIdx.x], g, h, b);
+  if (g >= d.n_groups) return;
   const GroupDesc gd = select_group(d, g);
+  if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
   if constexpr ((DSET & kDim32) != 0)
     if (gd.head_dim == 32) { fwd_dispatch_act<32, ASET>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim64) != 0)

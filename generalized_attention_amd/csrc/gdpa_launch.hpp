@@ -35,15 +35,16 @@ inline bool fwd_shape_ok(int d, int wl, int wr, int max_kv) {
   if (max_kv <= cap) return true;
   return wl >= 0 && wr >= 0 && wl + wr + kFwdChunkRows <= cap;
 }
-// Backward: each of the 4 waves owns a block of bwd_key_block(d) keys; query tiles of 64 rows.
-inline constexpr int bwd_key_block(int d) { return d == 128 ? 32 : 64; }
+// Backward: each wave owns a block of 32 keys; 8 waves per workgroup, or 4 when the launch holds
+// any d = 128 problem; query tiles of 64 rows.
+constexpr int kBwdKeyBlock = 32;
 constexpr int kBwdQueryTile = 64;
-// Either all keys are resident (4 blocks), or a bounded window whose key span for one query
-// tile touches at most 4 blocks.
-inline bool bwd_shape_ok(int d, int wl, int wr, int max_kv) {
-  const int kb = bwd_key_block(d);
-  if (max_kv <= 4 * kb) return true;
-  return wl >= 0 && wr >= 0 && kBwdQueryTile + wl + wr <= 3 * kb + 1;
+inline int bwd_waves_for(bool launch_has_d128) { return launch_has_d128 ? 4 : 8; }
+// Either all keys are resident (one block per wave), or a bounded window whose key span for one
+// query tile touches at most `waves` blocks.
+inline bool bwd_shape_ok(int waves, int wl, int wr, int max_kv) {
+  if (max_kv <= waves * kBwdKeyBlock) return true;
+  return wl >= 0 && wr >= 0 && kBwdQueryTile - 1 + wl + wr <= (waves - 1) * kBwdKeyBlock;
 }
 
 }  // namespace gdpa

@@ -33,6 +33,7 @@ class GroupArgs:
     window: Tuple[int, int] = (-1, -1)
     g: Optional[torch.Tensor] = None  # float32 [total_kv, H]
     self_attention: bool = False
+    planned: bool = False  # the workspace holds a gdpa_plan() work list for this shape
 
     def problem(self) -> _lib.gdpa_problem:
         p = _lib.gdpa_problem()
@@ -48,7 +49,7 @@ class GroupArgs:
         p.max_seqlen_q = int(self.max_seqlen_q)
         p.max_seqlen_kv = int(self.max_seqlen_kv)
         p.self_attention = 1 if self.self_attention else 0
-        p.reserved = 0
+        p.flags = _lib.GDPA_FLAG_PLANNED if self.planned else 0
         p.q_offsets = self.q_offsets.data_ptr()
         p.kv_offsets = self.kv_offsets.data_ptr()
         return p
@@ -91,6 +92,13 @@ def workspace(groups: Sequence[GroupArgs], pass_: int) -> torch.Tensor:
     if n == 0:
         raise _lib.GdpaError(_lib.GDPA_ERR_INVALID_ARGUMENT, "gdpa_workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=groups[0].q.device)
+
+
+def gdpa_plan(groups: Sequence[GroupArgs], ws: torch.Tensor) -> None:
+    """Build the longest-first work list of `groups` into `ws` (reused by planned calls)."""
+    rc = _lib.gdpa_plan([g.problem() for g in groups], ws.data_ptr(), ws.numel(), _stream(groups[0].q.device))
+    if rc != _lib.GDPA_OK:
+        raise _lib.GdpaError(rc, "gdpa_plan")
 
 
 def _fwd_tensors(grp: GroupArgs, o, lse) -> _lib.gdpa_tensors:

@@ -44,6 +44,12 @@ extern "C" {
 
 #define GDPA_MAX_GROUPS 16
 
+/* gdpa_problem.flags: the workspace already holds the work list that gdpa_plan() built for
+ * problems with the same n_groups, num_seqs and num_heads; the call skips rebuilding it. The list
+ * is a permutation of (group, head, sequence) items, so a list built from older offsets of the
+ * same shape is still complete (only its longest-first order may be stale). */
+#define GDPA_FLAG_PLANNED 1
+
 typedef enum gdpa_status {
   GDPA_OK = 0,
   GDPA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent window, ... */
@@ -78,7 +84,7 @@ typedef struct gdpa_problem {
   int32_t max_seqlen_q;  /* upper bound on any q_offsets[b+1]-q_offsets[b] */
   int32_t max_seqlen_kv; /* upper bound on any kv_offsets[b+1]-kv_offsets[b] */
   int32_t self_attention;/* 1: kv_offsets equal q_offsets (same sequences); 0: cross-attention */
-  int32_t reserved;      /* must be 0 */
+  int32_t flags;         /* 0 or GDPA_FLAG_PLANNED (same value in every problem of a call) */
   const int32_t* q_offsets;  /* device [B+1] */
   const int32_t* kv_offsets; /* device [B+1] */
 } gdpa_problem;
@@ -131,6 +137,15 @@ int gdpa_fwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, 
                      void* ws, size_t ws_bytes, void* stream);
 int gdpa_bwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Jagged work decomposition on its own: enqueue the kernel that orders the (group, head, sequence)
+ * work items of `problems` longest-first from the device offsets, into `ws` (sized by
+ * gdpa_workspace_size for the pass that follows). Subsequent gdpa_fwd / gdpa_bwd (and grouped)
+ * calls with GDPA_FLAG_PLANNED set reuse it, e.g. one plan per training step for both passes.
+ * (Tile scheduling over jagged, large-batch inputs: Kunlun review, section 2.3.)
+ */
+int gdpa_plan(const gdpa_problem* problems, int32_t n_groups, void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* gdpa_strerror(int status);

@@ -71,7 +71,7 @@ def good_problem(**kw):
     p.window_left = p.window_right = -1
     p.total_q, p.total_kv = 100, 512
     p.max_seqlen_q, p.max_seqlen_kv = 60, 256
-    p.self_attention, p.reserved = 0, 0
+    p.self_attention, p.flags = 0, 0
     p.q_offsets = p.kv_offsets = FAKE
     for k, v in kw.items():
         setattr(p, k, v)
@@ -110,7 +110,7 @@ INVALID_PROBLEMS = [
     ("nan scale", dict(scale=float("nan")), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window below -1", dict(window_left=-2), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window on cross-attention", dict(window_left=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
-    ("reserved set", dict(reserved=1), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("unknown flag", dict(flags=2), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("null offsets", dict(q_offsets=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("max len above total", dict(max_seqlen_q=101), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("self-attention with unequal totals", dict(self_attention=1), _lib.GDPA_ERR_INVALID_ARGUMENT),
