@@ -7,7 +7,7 @@ HBM. The default workload is the personalized-FFN form in bf16, forward+backward
 sequences with lengths uniform in [100, 1000], H=4, d=64, n=256 context-generated keys per
 sample, SiLU, scale 1/1000 (seed 0 of the input recipe; synthetic data).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pffn_train] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -29,13 +29,13 @@ KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_sched
                   "gdpa_launch.hpp"]
 
 WORKLOAD_TEXT = {
-    "cfg1": "PFFN-form GDPA bf16 forward: B=256, L~U[100,1000], H=4, d=64, n=256 context-generated "
+    "pffn_fwd": "PFFN-form GDPA bf16 forward: B=256, L~U[100,1000], H=4, d=64, n=256 context-generated "
             "keys/values, SiLU, scale 1/1000",
-    "cfg2": "PFFN-form GDPA bf16 forward+backward (dQ, dK, dV): B=256, L~U[100,1000], H=4, d=64, n=256 "
+    "pffn_train": "PFFN-form GDPA bf16 forward+backward (dQ, dK, dV): B=256, L~U[100,1000], H=4, d=64, n=256 "
             "context-generated keys/values, SiLU, scale 1/1000, upstream gradient N(0,1)",
-    "cfg3": "gated-softmax self-attention bf16 forward+backward: B=128, L~U[200,2000], H=8, d=64, "
+    "causal_gated": "gated-softmax self-attention bf16 forward+backward: B=128, L~U[200,2000], H=8, d=64, "
             "scale 1/8, log-sigmoid gate, causal window 128",
-    "cfg4": "10 event groups in one launch, bf16 forward+backward: B=64 each, L~U[100,1000], n=32, "
+    "grouped10": "10 event groups in one launch, bf16 forward+backward: B=64 each, L~U[100,1000], n=32, "
             "groups 0-4 H=8 d=128, groups 5-9 H=2 d=32, GELU",
 }
 
@@ -94,7 +94,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="pffn_train", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")

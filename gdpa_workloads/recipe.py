@@ -124,17 +124,18 @@ def _lengths(rng, b: int, lo_hi: Tuple[int, int]) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
-# Config registry (shapes from the workload statements; dtype/scale readings documented in
-# the design doc).
+# Workload registry. Shapes follow the pages' workload descriptions; where the pages leave a value
+# open (dtype, score scale) the recipe takes one reading: bf16 for the training shapes, scale
+# 1/L_max for the pointwise forms, 1/sqrt(d) for the softmax form.
 # ----------------------------------------------------------------------------------------------
 CONFIGS: Dict[str, str] = {
-    "cfg0": "tiny PFFN-form GDPA fp32: B=4, L in [1,64], H=2, d=32, n=64, GELU, fwd",
-    "cfg1": "PFFN-form GDPA bf16 fwd: B=256, L in [100,1000], H=4, d=64, n=256 generated from a "
+    "tiny_fp32": "tiny PFFN-form GDPA fp32: B=4, L in [1,64], H=2, d=32, n=64, GELU, fwd",
+    "pffn_fwd": "PFFN-form GDPA bf16 fwd: B=256, L in [100,1000], H=4, d=64, n=256 generated from a "
             "512-dim context by a random linear map, SiLU",
-    "cfg2": "cfg1 shapes, bf16 fwd+bwd (dQ, dK, dV), upstream gradient N(0,1)",
-    "cfg3": "gated softmax self-attention bf16 fwd+bwd: B=128, L in [200,2000], H=8, d=64, "
+    "pffn_train": "pffn_fwd shapes, bf16 fwd+bwd (dQ, dK, dV), upstream gradient N(0,1)",
+    "causal_gated": "gated softmax self-attention bf16 fwd+bwd: B=128, L in [200,2000], H=8, d=64, "
             "scale 1/sqrt(d), log sigmoid gate G~N(0,1), causal sliding window 128",
-    "cfg4": "10 event groups in one launch, bf16 fwd+bwd: each B=64, L in [100,1000], n=32; "
+    "grouped10": "10 event groups in one launch, bf16 fwd+bwd: each B=64, L in [100,1000], n=32; "
             "groups 0-4 H=8 d=128, groups 5-9 H=2 d=32; GELU",
 }
 
@@ -206,30 +207,30 @@ def make_workload(name: str, seed: int = 0, *, num_seqs: Optional[int] = None,
             return np.asarray(lengths, dtype=np.int64)
         return _lengths(rng, b, lr)
 
-    if name == "cfg0":
+    if name == "tiny_fp32":
         b = num_seqs or 4
-        spec = GroupSpec("cfg0", b, 2, 32, len_range or (1, 64), 64, act or "gelu",
+        spec = GroupSpec("tiny_fp32", b, 2, 32, len_range or (1, 64), 64, act or "gelu",
                          1.0 / 64 if scale is None else scale, dtype="fp32")
         L = lens(b, spec.len_range)
         grp = _pffn_plain(rng, dataclasses.replace(spec, num_seqs=len(L)), L, 1.0 / math.sqrt(32))
         return Workload(name, CONFIGS[name], [grp], ("fwd",), seed)
-    if name in ("cfg1", "cfg2"):
+    if name in ("pffn_fwd", "pffn_train"):
         b = num_seqs or 256
         spec = GroupSpec(name, b, 4, 64, len_range or (100, 1000), 256, act or "silu",
                          1.0 / 1000 if scale is None else scale)
         L = lens(b, spec.len_range)
         grp = _pffn_context(rng, dataclasses.replace(spec, num_seqs=len(L)), L, ctx_dim)
-        passes = ("fwd",) if name == "cfg1" else ("fwd", "bwd")
+        passes = ("fwd",) if name == "pffn_fwd" else ("fwd", "bwd")
         return Workload(name, CONFIGS[name], [grp], passes, seed)
-    if name == "cfg3":
+    if name == "causal_gated":
         b = num_seqs or 128
-        spec = GroupSpec("cfg3", b, 8, 64, len_range or (200, 2000), None, act or "softmax",
+        spec = GroupSpec("causal_gated", b, 8, 64, len_range or (200, 2000), None, act or "softmax",
                          1.0 / 8 if scale is None else scale,
                          window=(127, 0) if window is None else window, gate=True)
         L = lens(b, spec.len_range)
         grp = _self_attention(rng, dataclasses.replace(spec, num_seqs=len(L)), L)
         return Workload(name, CONFIGS[name], [grp], ("fwd", "bwd"), seed)
-    if name == "cfg4":
+    if name == "grouped10":
         b = num_seqs or 64
         lr = len_range or (100, 1000)
         if lengths is not None:
@@ -239,7 +240,7 @@ def make_workload(name: str, seed: int = 0, *, num_seqs: Optional[int] = None,
         groups = []
         for e in range(10):
             h, d = (8, 128) if e < 5 else (2, 32)
-            spec = GroupSpec(f"cfg4.g{e}", all_l.shape[1], h, d, lr, 32, act or "gelu",
+            spec = GroupSpec(f"grouped10.g{e}", all_l.shape[1], h, d, lr, 32, act or "gelu",
                              1.0 / 1000 if scale is None else scale)
             groups.append(_pffn_plain(rng, spec, all_l[e], 1.0))
         return Workload(name, CONFIGS[name], groups, ("fwd", "bwd"), seed)

@@ -208,7 +208,9 @@ __device__ inline bf16x8 tr_operand(const char* lds, int off, int qs, int t, int
   return as_bf16x8(u);
 }
 
-template <int D, int NW, int ACT>
+// GATED: the problem has a gate G (then dG may also be requested); a template parameter so that
+// the ungated element-wise code is straight-line.
+template <int D, int NW, int ACT, bool GATED>
 __device__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   using G = BwdGeo<D, NW>;
   const int q0 = gd.q_off[b], L = gd.q_off[b + 1] - q0;
@@ -252,8 +254,8 @@ __device__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   BwdWave<D, NW> st;
   int cur = -1;  // key block held by this wave
   const float sc = softmax ? gd.scale * kLog2e : gd.scale;
-  const bool has_gate = gd.g != nullptr;
-  const bool want_dg = dgseq != nullptr;
+  constexpr bool has_gate = GATED;
+  const bool want_dg = GATED && dgseq != nullptr;
   // element-wise forms without a gate carry p' = phi(scale s) / scale; dV is scaled at the end
   float c1 = 0.0f, c3 = 0.0f;
   if constexpr (!softmax) PointAct<ACT>::coeffs(has_gate ? 1.0f : gd.scale, c1, c3);
@@ -382,12 +384,14 @@ __device__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           if constexpr (softmax) {
-            const float x = has_gate ? __builtin_fmaf(s[r], sc, st.gate) : s[r] * sc;
+            float x;
+            if constexpr (has_gate) x = __builtin_fmaf(s[r], sc, st.gate);
+            else x = s[r] * sc;
             p[r] = fast_exp2(x - lrow[r]);
             ds[r] = p[r] * (dp[r] - drow[r]);
           } else {
             float dphi;
-            if (has_gate) {
+            if constexpr (has_gate) {
               PointAct<ACT>::value_grad(__builtin_fmaf(s[r], sc, st.gate), 1.0f, c1, c3, p[r], dphi);
             } else {
               PointAct<ACT>::value_grad(s[r], sc, c1, c3, p[r], dphi);
@@ -404,7 +408,7 @@ __device__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
             ds[r] = ok ? ds[r] : 0.0f;
           }
         }
-        if (want_dg) {
+        if constexpr (GATED) if (want_dg) {
           float dsum = 0.0f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) dsum += ds[r];
@@ -497,14 +501,20 @@ __device__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   if (cur >= 0) flush_block<D, NW>(st, gd, dkseq, dvseq, dgseq, cur * G::KB, n, dv_scale);
 }
 
+template <int D, int NW, int ACT>
+__device__ void bwd_dispatch_gate(char* lds, const GroupDesc& gd, int b, int h) {
+  if (gd.g != nullptr) bwd_item<D, NW, ACT, true>(lds, gd, b, h);
+  else bwd_item<D, NW, ACT, false>(lds, gd, b, h);
+}
+
 template <int D, int NW, int ASET>
 __device__ void bwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
   if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
-    if (gd.act == GDPA_ACT_GELU) { bwd_item<D, NW, GDPA_ACT_GELU>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_GELU) { bwd_dispatch_gate<D, NW, GDPA_ACT_GELU>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
-    if (gd.act == GDPA_ACT_SILU) { bwd_item<D, NW, GDPA_ACT_SILU>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_SILU) { bwd_dispatch_gate<D, NW, GDPA_ACT_SILU>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
-    if (gd.act == GDPA_ACT_SOFTMAX) bwd_item<D, NW, GDPA_ACT_SOFTMAX>(lds, gd, b, h);
+    if (gd.act == GDPA_ACT_SOFTMAX) bwd_dispatch_gate<D, NW, GDPA_ACT_SOFTMAX>(lds, gd, b, h);
 }
 
 template <int DSET, int ASET>

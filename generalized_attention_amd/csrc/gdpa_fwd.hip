@@ -81,8 +81,45 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
 
 // One wave: QS x 32 query rows starting at row0 (sequence-relative) against local key blocks
 // [kb0, kb1) of the staged range, whose first key has sequence position klo.
+// Q fragments of one wave tile: lane (row, g) holds d = g*D/2 + kk*8 + 0..7 of its row.
+template <int D, int QS>
+struct QFrags {
+  bf16x8 f[QS][D / 16];
+};
+
+template <int D, int QS>
+__device__ inline void load_q(QFrags<D, QS>& q, const bf16* qseq, size_t rs, int row0, int L) {
+  const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int row = row0 + qs * 32 + qc;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (row < L) u = *reinterpret_cast<const u32x4*>(qseq + row * rs + g * (D / 2) + kk * 8);
+      q.f[qs][kk] = as_bf16x8(u);
+    }
+  }
+}
+
+// S^T block kb (32 keys x QS*32 rows) = K_kb Q^T on MFMA, K rows from LDS.
+template <int D, int QS>
+__device__ inline void scores_block(const char* lds, const QFrags<D, QS>& q, int kb, f32x16 (&s)[QS]) {
+  using G = FwdGeo<D>;
+  const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) s[qs] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < G::KK; ++kk) {
+    const u32x4 ku = *reinterpret_cast<const u32x4*>(lds + (kb * 32 + qc) * G::KROW + g * D + kk * 16);
+    const bf16x8 kf = as_bf16x8(ku);
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) s[qs] = mfma32(kf, q.f[qs][kk], s[qs]);
+  }
+}
+
 template <int D, int ACT, int QS>
-__device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq, bf16* oseq,
+__device__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
                          float* lseq, int L, int N, int row0, int klo, int span, int kb0, int kb1) {
   using G = FwdGeo<D>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
@@ -90,18 +127,6 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq,
   const size_t rs = (size_t)H * D;
   constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
   const float* gl = reinterpret_cast<const float*>(lds + G::OFF_G);
-
-  bf16x8 qf[QS][G::KK];
-#pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-    const int row = row0 + qs * 32 + qc;
-#pragma unroll
-    for (int kk = 0; kk < G::KK; ++kk) {
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (row < L) u = *reinterpret_cast<const u32x4*>(qseq + row * rs + g * (D / 2) + kk * 8);
-      qf[qs][kk] = as_bf16x8(u);
-    }
-  }
   f32x16 o[QS][G::DT];
   float m[QS], lsum[QS];
 #pragma unroll
@@ -121,17 +146,15 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const bf16* qseq,
   if constexpr (!softmax) PointAct<ACT>::coeffs(has_gate ? 1.0f : gd.scale, c1, c3);
   const float out_scale = (!softmax && !has_gate) ? gd.scale : 1.0f;
 
+  // Software pipeline: the score MFMAs of block kb+1 are issued before the element-wise work of
+  // block kb, so the matrix cores run while the vector units evaluate the activation.
+  f32x16 s_next[QS];
+  if (kb0 < kb1) scores_block<D, QS>(lds, qf, kb0, s_next);
   for (int kb = kb0; kb < kb1; ++kb) {
     f32x16 s[QS];
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) s[qs] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < G::KK; ++kk) {
-      const u32x4 ku = *reinterpret_cast<const u32x4*>(lds + (kb * 32 + qc) * G::KROW + g * D + kk * 16);
-      const bf16x8 kf = as_bf16x8(ku);
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) s[qs] = mfma32(kf, qf[qs][kk], s[qs]);
-    }
+    for (int qs = 0; qs < QS; ++qs) s[qs] = s_next[qs];
+    if (kb + 1 < kb1) scores_block<D, QS>(lds, qf, kb + 1, s_next);
     // element-wise stage: register r of lane (qc, g) is key kb*32 + c_row(r, g), row qs*32 + qc.
     // Padded keys (beyond the staged range) have zero K and V rows in LDS, so the element-wise
     // forms need a mask only inside a window; the softmax form also masks the padded keys.
@@ -256,6 +279,7 @@ __device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   const int k0 = gd.kv_off[b], N = gd.kv_off[b + 1] - k0;
   if (L <= 0) return;
   const int H = gd.num_heads;
+  const size_t rs = (size_t)H * D;
   const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
   bf16* oseq = reinterpret_cast<bf16*>(gd.o) + ((size_t)q0 * H + h) * D;
   float* lseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
@@ -271,12 +295,17 @@ __device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
     const int span_pad = (N + 31) & ~31;
     stage_kv<D>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
     __syncthreads();
+    QFrags<D, QS> qcur, qnext;
+    if (w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
     for (int row0 = w * RW; row0 < L; row0 += 4 * RW) {
+      // next tile's Q is loaded while this tile computes
+      if (row0 + 4 * RW < L) load_q<D, QS>(qnext, qseq, rs, row0 + 4 * RW, L);
       int lo = 0, hi = N - 1;
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
-      fwd_tile<D, ACT, QS>(lds, gd, qseq, oseq, lseq, L, N, row0, 0, N, kb0, kb1);
+      fwd_tile<D, ACT, QS>(lds, gd, qcur, oseq, lseq, L, N, row0, 0, N, kb0, kb1);
+      qcur = qnext;
     }
   } else {
     // bounded window (both sides >= 0, checked on the host): chunks of kFwdChunkRows rows
@@ -294,7 +323,9 @@ __device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
         int lo = row0 - gd.wl > klo ? row0 - gd.wl : klo;
         int hi = row0 + RW - 1 + gd.wr < khi - 1 ? row0 + RW - 1 + gd.wr : khi - 1;
         const int kb0 = (lo - klo) / 32, kb1 = hi >= lo ? (hi - klo) / 32 + 1 : kb0;
-        fwd_tile<D, ACT, QS>(lds, gd, qseq, oseq, lseq, L, N, row0, klo, span, kb0, kb1);
+        QFrags<D, QS> qf;
+        load_q<D, QS>(qf, qseq, rs, row0, L);
+        fwd_tile<D, ACT, QS>(lds, gd, qf, oseq, lseq, L, N, row0, klo, span, kb0, kb1);
       }
     }
   }

@@ -11,7 +11,8 @@
 
 namespace gdpa {
 
-__global__ void __launch_bounds__(1024) build_schedule_kernel(LaunchDesc d) {
+// Launched with exactly kNumBuckets threads (one per bucket in the scan).
+__global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc d) {
   __shared__ int32_t hist[kNumBuckets];
   __shared__ int32_t cursor[kNumBuckets];
   const int tid = threadIdx.x;
@@ -33,13 +34,24 @@ __global__ void __launch_bounds__(1024) build_schedule_kernel(LaunchDesc d) {
     atomicAdd(&hist[key], gd.num_heads);
   }
   __syncthreads();
-  if (tid == 0) {
-    // exclusive prefix in descending bucket order (longest work first)
-    int32_t run = 0;
-    for (int k = kNumBuckets - 1; k >= 0; --k) {
-      cursor[k] = run;
-      run += hist[k];
+  // exclusive prefix sum in descending bucket order (longest work first): thread t owns bucket
+  // kNumBuckets-1-t; Hillis-Steele scan over the 1024 buckets in LDS.
+  {
+    const int k = kNumBuckets - 1 - tid;
+    int32_t v = hist[k];
+    cursor[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kNumBuckets; off <<= 1) {
+      const int32_t add = tid >= off ? cursor[tid - off] : 0;
+      __syncthreads();
+      cursor[tid] += add;
+      __syncthreads();
     }
+    const int32_t excl = cursor[tid] - v;
+    __syncthreads();
+    hist[k] = excl;  // hist now holds the start position of each bucket
+    __syncthreads();
+    cursor[k] = excl;
   }
   __syncthreads();
   for (int s = tid; s < d.n_seqs_total; s += blockDim.x) {
@@ -54,7 +66,7 @@ __global__ void __launch_bounds__(1024) build_schedule_kernel(LaunchDesc d) {
 }
 
 hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream) {
-  hipLaunchKernelGGL(build_schedule_kernel, dim3(1), dim3(1024), 0, stream, d);
+  hipLaunchKernelGGL(build_schedule_kernel, dim3(1), dim3(kNumBuckets), 0, stream, d);
   return hipGetLastError();
 }
 

@@ -102,33 +102,33 @@ def compare_workload(w, passes, sample=None, want_dg=True, scale=None):
 # ------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_cfg0_fp32_forward(seed):
-    compare_workload(make_workload("cfg0", seed), ("fwd",))
+def test_tiny_fp32_forward(seed):
+    compare_workload(make_workload("tiny_fp32", seed), ("fwd",))
 
 
 @pytest.mark.parametrize("scale", [1.0, 1.0 / math.sqrt(32)])
-def test_cfg0_fp32_forward_scales(scale):
-    compare_workload(make_workload("cfg0", 0), ("fwd",), scale=scale)
+def test_tiny_fp32_forward_scales(scale):
+    compare_workload(make_workload("tiny_fp32", 0), ("fwd",), scale=scale)
 
 
-def test_cfg0_fp32_backward():
-    compare_workload(make_workload("cfg0", 0), ("fwd", "bwd"))
+def test_tiny_fp32_backward():
+    compare_workload(make_workload("tiny_fp32", 0), ("fwd", "bwd"))
 
 
 @pytest.mark.parametrize("seed,scale", [(0, None), (1, None), (2, 1.0 / 8)])
-def test_cfg2_reduced(seed, scale):
-    w = make_workload("cfg2", seed, num_seqs=10, len_range=(1, 700))
+def test_pffn_train_reduced(seed, scale):
+    w = make_workload("pffn_train", seed, num_seqs=10, len_range=(1, 700))
     compare_workload(w, ("fwd", "bwd"), scale=scale)
 
 
-def test_cfg2_edge_lengths():
-    w = make_workload("cfg2", 3, lengths=EDGE_LENGTHS)
+def test_pffn_train_edge_lengths():
+    w = make_workload("pffn_train", 3, lengths=EDGE_LENGTHS)
     compare_workload(w, ("fwd", "bwd"), scale=1.0 / 8)
 
 
-def test_cfg1_gelu_variant():
+def test_pffn_fwd_gelu_variant():
     # same shapes with the other element-wise activation
-    w = make_workload("cfg1", 4, num_seqs=6, len_range=(1, 400), act="gelu")
+    w = make_workload("pffn_fwd", 4, num_seqs=6, len_range=(1, 400), act="gelu")
     compare_workload(w, ("fwd", "bwd"), scale=1.0 / 8)
 
 
@@ -143,7 +143,7 @@ def test_self_attention_features(act, gate, window):
     """Self-attention forms on short sequences (all keys resident) and with windows."""
     import dataclasses
     lens = [1, 5, 64, 100, 200, 256] if window == (-1, -1) else [1, 5, 64, 100, 200, 256, 300, 700]
-    w = make_workload("cfg3", 7, lengths=lens, act=act, window=window)
+    w = make_workload("causal_gated", 7, lengths=lens, act=act, window=window)
     g = w.groups[0]
     if not gate:
         g.g = None
@@ -152,23 +152,23 @@ def test_self_attention_features(act, gate, window):
 
 
 @pytest.mark.parametrize("seed", [0, 1])
-def test_cfg3_reduced(seed):
-    w = make_workload("cfg3", seed, num_seqs=5, len_range=(1, 900))
+def test_causal_gated_reduced(seed):
+    w = make_workload("causal_gated", seed, num_seqs=5, len_range=(1, 900))
     compare_workload(w, ("fwd", "bwd"))
 
 
-def test_cfg3_edge_lengths():
-    w = make_workload("cfg3", 2, lengths=EDGE_LENGTHS + [255, 256, 257, 600])
+def test_causal_gated_edge_lengths():
+    w = make_workload("causal_gated", 2, lengths=EDGE_LENGTHS + [255, 256, 257, 600])
     compare_workload(w, ("fwd", "bwd"))
 
 
-def test_cfg4_reduced():
-    w = make_workload("cfg4", 0, num_seqs=3, len_range=(1, 400))
+def test_grouped10_reduced():
+    w = make_workload("grouped10", 0, num_seqs=3, len_range=(1, 400))
     compare_workload(w, ("fwd", "bwd"), scale=None)
 
 
-def test_cfg4_reduced_scale_sqrt_d():
-    w = make_workload("cfg4", 1, num_seqs=2, len_range=(1, 300))
+def test_grouped10_reduced_scale_sqrt_d():
+    w = make_workload("grouped10", 1, num_seqs=2, len_range=(1, 300))
     for g in w.groups:
         import dataclasses
         g.spec = dataclasses.replace(g.spec, scale=1.0 / math.sqrt(g.spec.head_dim))
@@ -189,16 +189,16 @@ def _sampler(k, seed=0):
     return pick
 
 
-def test_cfg2_full_size_sampled():
-    compare_workload(make_workload("cfg2", 0), ("fwd", "bwd"), sample=_sampler(6))
+def test_pffn_train_full_size_sampled():
+    compare_workload(make_workload("pffn_train", 0), ("fwd", "bwd"), sample=_sampler(6))
 
 
-def test_cfg3_full_size_sampled():
-    compare_workload(make_workload("cfg3", 0), ("fwd", "bwd"), sample=_sampler(3))
+def test_causal_gated_full_size_sampled():
+    compare_workload(make_workload("causal_gated", 0), ("fwd", "bwd"), sample=_sampler(3))
 
 
-def test_cfg4_full_size_sampled():
-    compare_workload(make_workload("cfg4", 0), ("fwd", "bwd"), sample=_sampler(1))
+def test_grouped10_full_size_sampled():
+    compare_workload(make_workload("grouped10", 0), ("fwd", "bwd"), sample=_sampler(1))
 
 
 # ------------------------------------------------------------------------------------------------
@@ -206,7 +206,7 @@ def test_cfg4_full_size_sampled():
 # ------------------------------------------------------------------------------------------------
 
 def test_outputs_fully_overwritten_and_deterministic():
-    w = make_workload("cfg3", 5, lengths=[0, 1, 70, 200, 3])
+    w = make_workload("causal_gated", 5, lengths=[0, 1, 70, 200, 3])
     g = w.groups[0]
     dev = device_group(g)
     o = torch.full_like(dev.q, float("nan"))
@@ -227,7 +227,7 @@ def test_outputs_fully_overwritten_and_deterministic():
 
 
 def test_sample_independence():
-    w = make_workload("cfg2", 6, num_seqs=4, len_range=(50, 300))
+    w = make_workload("pffn_train", 6, num_seqs=4, len_range=(50, 300))
     g = w.groups[0]
     dev = device_group(g)
     o1, _ = ga.gdpa_fwd(dev)
