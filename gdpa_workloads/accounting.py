@@ -40,10 +40,9 @@ def group_work(group) -> Dict[str, float]:
     lse_b = 4 * tq * h if softmax else 0
     # forward: read Q, K, V (+G); write O (+LSE)
     fwd_bytes = esize * (2 * tq * h * d + 2 * tk * h * d) + gate_b + lse_b
-    # backward: read Q, K, V, dO (+G; softmax also O and LSE); write dQ, dK, dV
-    bwd_bytes = esize * (3 * tq * h * d + 4 * tk * h * d) + gate_b
-    if softmax:
-        bwd_bytes += esize * tq * h * d + lse_b
+    # backward: read Q, K, V, dO (+G; softmax also LSE); write dQ, dK, dV (+dG). The softmax row
+    # term D_i = sum_j p_ij dp_ij is formed from P and dP in the kernel, so O is not read.
+    bwd_bytes = esize * (3 * tq * h * d + 4 * tk * h * d) + 2 * gate_b + lse_b
     return {
         "entries": float(e),
         "fwd_flops": 4.0 * d * e,
