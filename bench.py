@@ -25,8 +25,8 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_sched.hip", "gdpa_api.cpp",
-                  "gdpa_launch.hpp"]
+KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hpp", "gdpa_bwd.hip", "gdpa_bwd_sm128.hip",
+                  "gdpa_sched.hip", "gdpa_api.cpp", "gdpa_launch.hpp"]
 
 WORKLOAD_TEXT = {
     "pffn_fwd": "PFFN-form GDPA bf16 forward: B=256, L~U[100,1000], H=4, d=64, n=256 context-generated "

@@ -17,7 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgdpa.so")
 
-SOURCES = ["gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_fp32.hip"]
+SOURCES = ["gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_bwd_sm128.hip", "gdpa_fp32.hip"]
+# Per-source options. The backward kernels keep MFMA results in the VGPR form (no register-class
+# copies between the score accumulators and the element-wise code); one kernel variant that this
+# compiler cannot build that way lives in its own source.
+EXTRA = {"gdpa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -30,7 +34,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "is not a recognized feature for this target" not in l)

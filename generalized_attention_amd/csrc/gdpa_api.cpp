@@ -51,9 +51,9 @@ int check_problem(const gdpa_problem& p) {
   return GDPA_OK;
 }
 
-int check_backward_capacity(const gdpa_problem& p, int waves) {
+int check_backward_capacity(const gdpa_problem& p) {
   if (p.dtype != GDPA_DTYPE_BF16) return GDPA_OK;
-  return bwd_shape_ok(waves, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK : GDPA_ERR_UNSUPPORTED;
+  return bwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK : GDPA_ERR_UNSUPPORTED;
 }
 
 int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
@@ -77,12 +77,10 @@ int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
 int layout(const gdpa_problem* ps, int n_groups, int pass, WsLayout* L) {
   if (!ps || n_groups < 1 || n_groups > GDPA_MAX_GROUPS) return GDPA_ERR_INVALID_ARGUMENT;
   if (pass != 0 && pass != 1) return GDPA_ERR_INVALID_ARGUMENT;
-  bool has128 = false;
-  for (int g = 0; g < n_groups; ++g) has128 |= ps[g].head_dim == 128;
   for (int g = 0; g < n_groups; ++g) {
     int rc = check_problem(ps[g]);
     if (rc != GDPA_OK) return rc;
-    if (pass == 1 && (rc = check_backward_capacity(ps[g], bwd_waves_for(has128))) != GDPA_OK) return rc;
+    if (pass == 1 && (rc = check_backward_capacity(ps[g])) != GDPA_OK) return rc;
     if (ps[g].dtype != ps[0].dtype || ps[g].flags != ps[0].flags) return GDPA_ERR_INVALID_ARGUMENT;
     L->n_items += (int64_t)ps[g].num_seqs * ps[g].num_heads;
     L->n_seqs += ps[g].num_seqs;

@@ -1,0 +1,713 @@
+// GDPA backward for bf16 on gfx950: one workgroup (4 waves, one per SIMD) per (sequence, head).
+//
+//   dp_ij = <dO_i, V_j>;   ds_ij = dp_ij phi'(s_ij)   or   p_ij (dp_ij - D_i), D_i = sum_j p_ij dp_ij
+//   dQ = scale dS K;   dK = scale dS^T Q;   dV = P^T dO;   dG_j = sigmoid(-G_j) sum_i ds_ij
+//
+// (Block-wise backward that recomputes the scores tile by tile and never writes the score matrix
+// to HBM: Kunlun review, section 2.3 and Figure 2. Gate: reproduction README "Core equations";
+// window: review section 2.5.)
+//
+// Work split inside an item. The keys are cut into blocks of 32; block b lives in ring slot
+// b mod NB, slot s belongs to wave s mod 4. A wave therefore owns KB = 2 blocks (1 at d = 128):
+// their K and V rows stay in registers (B operands of S = Q K^T and dP = dO V^T) and their
+// dK^T, dV^T accumulate in registers for the whole sweep over the 64-row query tiles. Per tile:
+//   1. Blocks entering the window are taken (K^T of a new block goes to an LDS staging area).
+//      Q and dO of a tile are loaded from HBM two tiles ahead and stored row-major into LDS
+//      while the previous tile's dQ runs.
+//   2. Softmax only: D_i = sum_j p_ij dp_ij exactly, from a pass with the query on the lane
+//      (S^T = K Q^T, dP^T = V dO^T); the waves' partial sums meet in LDS.
+//   3. Each wave, per 32-row half and owned block: S, dP on 32x32x16 MFMA; P and dS in fp32
+//      registers; their accumulator layout is the B operand of dV^T = dO^T P and dK^T = Q^T dS,
+//      whose dO^T / Q^T operands come from the row-major tiles by the transposing LDS read
+//      (loaded once per half and reused for both owned blocks). dS also goes to LDS as
+//      [key][query].
+//   4. dQ^T = K^T dS^T on 32x32x16 MFMA: each wave owns a 32(d) x 32(query) output tile (two at
+//      d = 128); K^T comes from the staging area, dS^T by the transposing LDS read.
+// Every wave runs on its own SIMD, so the wave's own instruction stream overlaps MFMA with the
+// element-wise VALU work. Every output element is written exactly once (no atomics).
+#pragma once
+
+#include "gdpa_device.hpp"
+#include "gdpa_launch.hpp"
+
+namespace gdpa {
+
+template <int D>
+struct BwdGeo {
+  static constexpr int NW = kBwdWaves;
+  static constexpr int THREADS = NW * kWave;
+  static constexpr int KPW = bwd_keys_per_wave(D);
+  static constexpr int KB = KPW / kBwdKeyBlock;    // blocks per wave
+  static constexpr int NB = NW * KB;               // ring slots
+  static constexpr int CAP = NB * kBwdKeyBlock;    // resident keys
+  static constexpr int QT = kBwdQueryTile;
+  static constexpr int KK = D / 16;                // MFMA k-steps over d
+  static constexpr int DT = D / 32;                // 32-wide d tiles
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int NPF = (QT * CPR + THREADS - 1) / THREADS;  // prefetch chunks per thread
+  // dQ^T output tiles (32 d x 32 queries): DT x 2; wave w takes d-tile w % DT and QH query halves
+  static constexpr int QH = (2 * DT >= NW) ? 2 * DT / NW : 1;
+  static constexpr int NROW = D * 2 + 16;          // row-major Q / dO tile row (bytes)
+  static constexpr int KTROW = CAP * 2 + 16;       // K^T staging row: CAP keys
+  static constexpr int SXROW = QT * 2 + 16;        // dS^T row (one key): QT queries
+  static constexpr int OFF_QN = 0;
+  static constexpr int OFF_DON = OFF_QN + QT * NROW;
+  static constexpr int OFF_KT = OFF_DON + QT * NROW;
+  static constexpr int OFF_SX = OFF_KT + D * KTROW;         // dS^T (bf16; softmax: high part)
+  static constexpr int OFF_SXL = OFF_SX + CAP * SXROW;      // softmax: dS - high part, in bf16
+  static constexpr int OFF_ROW = OFF_SXL + CAP * SXROW;     // lse2[QT] (log2 units)
+  static constexpr int OFF_DPART = OFF_ROW + QT * 4;        // softmax: partial D_i per wave [NW][QT]
+  static constexpr int OFF_GATE = OFF_DPART + NW * QT * 4;  // gate term per ring position [CAP]
+  static constexpr int BYTES = OFF_GATE + CAP * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+constexpr int max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+template <int DSET>
+constexpr int bwd_lds_bytes() {
+  return max3((DSET & kDim32) ? BwdGeo<32>::BYTES : 0, (DSET & kDim64) ? BwdGeo<64>::BYTES : 0,
+              (DSET & kDim128) ? BwdGeo<128>::BYTES : 0);
+}
+
+template <int N>
+__device__ inline int pmod(int x) { return ((x % N) + N) % N; }
+
+// Per-wave state of its owned blocks.
+template <int D>
+struct BwdWave {
+  using G = BwdGeo<D>;
+  bf16x8 kreg[G::KB][G::KK];
+  bf16x8 vreg[G::KB][G::KK];
+  f32x16 dk[G::KB][G::DT];
+  f32x16 dv[G::KB][G::DT];
+  float dgs[G::KB];
+  float gate[G::KB];   // this lane's key: gate term (natural units; log2 units for softmax)
+  float graw[G::KB];   // raw G of this lane's key (for dG)
+  int cur[G::KB];      // block held in each owned slot (-1: none); uniform
+};
+
+// Take block `blk` into owned slot kb (ring slot s): K/V rows into registers, K^T into the LDS
+// staging area, gate terms; zero the block's accumulators.
+template <int D, int ACT>
+__device__ __forceinline__ void take_block(BwdWave<D>& st, int kb, char* lds, const GroupDesc& gd, const bf16* kseq,
+                           const bf16* vseq, const float* gseq, int blk, int n, int s) {
+  using G = BwdGeo<D>;
+  const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
+  const size_t rs = (size_t)gd.num_heads * D;
+  const int key = blk * kBwdKeyBlock + kc;
+  const bool ok = key < n;
+  const int pos = s * kBwdKeyBlock + kc;
+#pragma unroll
+  for (int kk = 0; kk < G::KK; ++kk) {
+    u32x4 ku = {0u, 0u, 0u, 0u}, vu = {0u, 0u, 0u, 0u};
+    if (ok) {
+      ku = *reinterpret_cast<const u32x4*>(kseq + key * rs + g * (D / 2) + kk * 8);
+      vu = *reinterpret_cast<const u32x4*>(vseq + key * rs + g * (D / 2) + kk * 8);
+    }
+    st.kreg[kb][kk] = as_bf16x8(ku);
+    st.vreg[kb][kk] = as_bf16x8(vu);
+    // K^T staging: this lane's 8 d values of `key` (d = g*D/2 + kk*8 + e), keys in ring order
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d0 = g * (D / 2) + kk * 8 + 2 * e;
+      *reinterpret_cast<uint16_t*>(lds + G::OFF_KT + d0 * G::KTROW + pos * 2) = (uint16_t)(ku[e] & 0xFFFF);
+      *reinterpret_cast<uint16_t*>(lds + G::OFF_KT + (d0 + 1) * G::KTROW + pos * 2) = (uint16_t)(ku[e] >> 16);
+    }
+  }
+  float t = 0.0f, gr = 0.0f;
+  if (gseq != nullptr && ok) {
+    gr = gseq[(size_t)key * gd.num_heads];
+    t = log_sigmoid_f(gr);
+    if (ACT == GDPA_ACT_SOFTMAX) t *= kLog2e;
+  }
+  st.gate[kb] = t;
+  st.graw[kb] = gr;
+  st.dgs[kb] = 0.0f;
+  if (g == 0) reinterpret_cast<float*>(lds + G::OFF_GATE)[pos] = t;
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) {
+    st.dk[kb][dt] = f32x16{};
+    st.dv[kb][dt] = f32x16{};
+  }
+}
+
+// Write dK, dV (and dG) of owned slot kb. Accumulator register r of lane (key, g) in d-tile dt
+// is d = dt*32 + c_row(r, g): four runs of 4 consecutive d per lane.
+template <int D>
+__device__ __forceinline__ void flush_block(BwdWave<D>& st, int kb, const GroupDesc& gd, bf16* dkseq, bf16* dvseq, float* dgseq,
+                            int n, float dv_scale) {
+  using G = BwdGeo<D>;
+  const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
+  const size_t rs = (size_t)gd.num_heads * D;
+  const int key = st.cur[kb] * kBwdKeyBlock + kc;
+  const float dgsum = st.dgs[kb] + __shfl_xor(st.dgs[kb], 32);
+  if (key < n) {
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = dt * 32 + a * 8 + g * 4;
+        u32x2 uk, uv;
+        uk[0] = pack_bf16x2(st.dk[kb][dt][4 * a] * gd.scale, st.dk[kb][dt][4 * a + 1] * gd.scale);
+        uk[1] = pack_bf16x2(st.dk[kb][dt][4 * a + 2] * gd.scale, st.dk[kb][dt][4 * a + 3] * gd.scale);
+        uv[0] = pack_bf16x2(st.dv[kb][dt][4 * a] * dv_scale, st.dv[kb][dt][4 * a + 1] * dv_scale);
+        uv[1] = pack_bf16x2(st.dv[kb][dt][4 * a + 2] * dv_scale, st.dv[kb][dt][4 * a + 3] * dv_scale);
+        *reinterpret_cast<u32x2*>(dkseq + key * rs + d) = uk;
+        *reinterpret_cast<u32x2*>(dvseq + key * rs + d) = uv;
+      }
+    if (dgseq != nullptr && g == 0) {
+      const float sg = 1.0f / (1.0f + __expf(st.graw[kb]));  // sigmoid(-G)
+      dgseq[(size_t)key * gd.num_heads] = sg * dgsum;
+    }
+  }
+}
+
+// Registers holding the next query tile of Q and dO (and its lse) between the global load and
+// the LDS store.
+template <int D>
+struct QTileRegs {
+  u32x4 q[BwdGeo<D>::NPF];
+  u32x4 d[BwdGeo<D>::NPF];
+  float lse;
+};
+
+template <int D, bool SOFTMAX>
+__device__ void prefetch_qtile(QTileRegs<D>& pf, const bf16* qseq, const bf16* doseq, const float* lseseq,
+                               size_t rs, int H, int r0, int L) {
+  using G = BwdGeo<D>;
+#pragma unroll
+  for (int i = 0; i < G::NPF; ++i) {
+    const int idx = threadIdx.x + i * G::THREADS;
+    const int r = idx / G::CPR, c = idx % G::CPR;
+    const int row = r0 + r;
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (idx < G::QT * G::CPR && row < L) {
+      a = *reinterpret_cast<const u32x4*>(qseq + row * rs + c * 8);
+      b = *reinterpret_cast<const u32x4*>(doseq + row * rs + c * 8);
+    }
+    pf.q[i] = a;
+    pf.d[i] = b;
+  }
+  if constexpr (SOFTMAX) {
+    const int row = r0 + (int)threadIdx.x;
+    pf.lse = (threadIdx.x < G::QT && row < L) ? lseseq[(size_t)row * H] * kLog2e : __builtin_inff();
+  }
+}
+
+template <int D, bool SOFTMAX>
+__device__ void store_qtile(char* lds, const QTileRegs<D>& pf) {
+  using G = BwdGeo<D>;
+#pragma unroll
+  for (int i = 0; i < G::NPF; ++i) {
+    const int idx = threadIdx.x + i * G::THREADS;
+    if (idx < G::QT * G::CPR) {
+      const int r = idx / G::CPR, c = idx % G::CPR;
+      *reinterpret_cast<u32x4*>(lds + G::OFF_QN + r * G::NROW + c * 16) = pf.q[i];
+      *reinterpret_cast<u32x4*>(lds + G::OFF_DON + r * G::NROW + c * 16) = pf.d[i];
+    }
+  }
+  if constexpr (SOFTMAX)
+    if (threadIdx.x < G::QT) reinterpret_cast<float*>(lds + G::OFF_ROW)[threadIdx.x] = pf.lse;
+}
+
+// A operand (M = d, K = query) of a 32x32x16 product, read from a row-major [query][d] LDS tile
+// with two transposing reads: lane (m, g) gets column d = dt*32 + m of the 8 query rows that
+// B k-tile t of a C tile (rows = queries qs*32 + c_row(.)) carries in its slots (g, e), i.e.
+// rows qs*32 + 16t + 8h + 4g + (0..3) for h = 0, 1.
+template <int ROWBYTES>
+__device__ inline bf16x8 tr_operand(const char* lds, int off, int qs, int t, int dt) {
+  const int lane = lane_id(), i = lane & 15, hh = (lane >> 4) & 1, g = lane >> 5;
+  const int col = dt * 32 + hh * 16 + 4 * (i & 3);
+  const int row0 = qs * 32 + 16 * t + g * 4 + (i >> 2);
+  const u32x2 lo = lds_read_tr16(lds, off + row0 * ROWBYTES + col * 2);
+  const u32x2 hi = lds_read_tr16(lds, off + (row0 + 8) * ROWBYTES + col * 2);
+  const u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(u);
+}
+
+// B operand (K = 16 keys, N = 32 queries) of dQ^T = K^T dS^T, read from the [key][query] dS^T
+// tile with two transposing reads: lane (n, g) gets query qh*32 + n, keys kbase + 8g + (0..7).
+template <int SXROW>
+__device__ inline bf16x8 sx_operand(const char* lds, int off, int kbase, int qh) {
+  const int lane = lane_id(), i = lane & 15, hh = (lane >> 4) & 1, g = lane >> 5;
+  const int row = kbase + g * 8 + (i >> 2);
+  const int col = qh * 32 + hh * 16 + 4 * (i & 3);
+  const u32x2 lo = lds_read_tr16(lds, off + row * SXROW + col * 2);
+  const u32x2 hi = lds_read_tr16(lds, off + (row + 4) * SXROW + col * 2);
+  const u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(u);
+}
+
+// Which rows / keys of the (query half, key block) pair are allowed.
+struct BlockMask {
+  bool empty;  // no allowed entry (skip)
+  bool full;   // every entry allowed (no mask needed)
+};
+__device__ inline BlockMask block_mask(int kf, int rf, int n, int L, int wl, int wr) {
+  const int kl = kf + 31, rl = rf + 31;
+  BlockMask m;
+  m.empty = kf >= n || rf >= L;
+  if (wl >= 0 && kl < rf - wl) m.empty = true;
+  if (wr >= 0 && kf > rl + wr) m.empty = true;
+  m.full = kl < n && rl < L;
+  if (wl >= 0 && kf < rl - wl) m.full = false;
+  if (wr >= 0 && kl > rf + wr) m.full = false;
+  return m;
+}
+
+// Pointers and scalars of one (sequence, head) item.
+struct BwdItem {
+  const bf16* qseq;
+  const bf16* doseq;
+  const float* lseseq;
+  bf16* dqseq;
+  const bf16* kseq;
+  const bf16* vseq;
+  const float* gseq;
+  bf16* dkseq;
+  bf16* dvseq;
+  float* dgseq;
+  size_t rs;
+  int H, L, n, wl, wr;
+};
+
+// The sweep over the query tiles of one item. KACT: owned blocks processed per wave (KB, or 1
+// when every key of the item fits in one block per wave). The per-block work runs without
+// branches around the MFMA accumulations (a skipped block contributes zero operands), which keeps
+// the dK / dV accumulators in place in the register file; only the element-wise work is skipped.
+// GATED: the problem has a gate G (then dG may also be requested).
+template <int D, int ACT, bool GATED, int KACT, bool WINDOWED>
+__device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const BwdItem& it) {
+  using G = BwdGeo<D>;
+  constexpr int NS = G::NW * KACT;  // ring slots in use
+  const int L = it.L, n = it.n, wl = it.wl, wr = it.wr, H = it.H;
+  const size_t rs = it.rs;
+  const int w = wave_id(), lane = lane_id(), lc = lane & 31, g = lane >> 5;
+  constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
+  // entries need explicit masks in the softmax form or inside a window; without a window every
+  // block is resident for the whole sweep (taken once, before it)
+  constexpr bool MASKED = softmax || WINDOWED;
+  const int nkb = (n + kBwdKeyBlock - 1) / kBwdKeyBlock;
+  const int ntiles = (L + G::QT - 1) / G::QT;
+
+  BwdWave<D> st;
+#pragma unroll
+  for (int kb = 0; kb < G::KB; ++kb) {
+    st.cur[kb] = -1;
+    st.gate[kb] = 0.0f;
+    st.graw[kb] = 0.0f;
+    st.dgs[kb] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) {
+      st.kreg[kb][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      st.vreg[kb][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt) {
+      st.dk[kb][dt] = f32x16{};
+      st.dv[kb][dt] = f32x16{};
+    }
+  }
+  const int dtile = w % G::DT;
+  const int qh_first = (G::QH == 2) ? 0 : w / G::DT;  // query half of this wave's dQ tile
+  const bool dq_role = qh_first < 2;
+
+  const float sc = softmax ? gd.scale * kLog2e : gd.scale;
+  constexpr bool has_gate = GATED;
+  const bool want_dg = GATED && it.dgseq != nullptr;
+  // element-wise forms without a gate carry p' = phi(scale s) / scale; dV is scaled at the end
+  float c1 = 0.0f, c3 = 0.0f;
+  if constexpr (!softmax) PointAct<ACT>::coeffs(has_gate ? 1.0f : gd.scale, c1, c3);
+  const float dv_scale = (!softmax && !has_gate) ? gd.scale : 1.0f;
+  const float* lse2 = reinterpret_cast<const float*>(lds + G::OFF_ROW);
+  float* dpart = reinterpret_cast<float*>(lds + G::OFF_DPART);
+  const float* gl = reinterpret_cast<const float*>(lds + G::OFF_GATE);
+
+  // K^T staging of slots never taken must hold finite values (they meet zero dS in dQ)
+  for (int idx = threadIdx.x; idx < D * (G::KTROW / 16); idx += G::THREADS)
+    reinterpret_cast<u32x4*>(lds + G::OFF_KT)[idx] = u32x4{0u, 0u, 0u, 0u};
+  QTileRegs<D> pf;
+  prefetch_qtile<D, softmax>(pf, it.qseq, it.doseq, it.lseseq, rs, H, 0, L);
+  __syncthreads();  // K^T staging zeroed
+  store_qtile<D, softmax>(lds, pf);  // tile 0
+  if (ntiles > 1) prefetch_qtile<D, softmax>(pf, it.qseq, it.doseq, it.lseseq, rs, H, G::QT, L);
+  if constexpr (!WINDOWED) {
+    // every block of the sequence is resident for the whole sweep: take them once
+#pragma unroll
+    for (int kb = 0; kb < KACT; ++kb) {
+      const int s = kb * G::NW + w;
+      if (s < nkb) {
+        take_block<D, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, s, n, s);
+        st.cur[kb] = s;
+      }
+    }
+  }
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int r0 = j * G::QT;
+    // blocks touched by this query tile
+    int kmin = 0, kmax = nkb - 1;
+    if (wl >= 0) kmin = (r0 - wl > 0 ? r0 - wl : 0) / kBwdKeyBlock;
+    if (wr >= 0) {
+      const int hi = r0 + G::QT - 1 + wr < n - 1 ? r0 + G::QT - 1 + wr : n - 1;
+      kmax = hi / kBwdKeyBlock;
+    }
+    const bool any_keys = kmin <= kmax;
+
+    // ---- 1. take the blocks entering the window (all LDS readers of the previous tile are done)
+    int blk[KACT];
+    bool act[KACT];
+#pragma unroll
+    for (int kb = 0; kb < KACT; ++kb) {
+      const int s = kb * G::NW + w;
+      blk[kb] = kmax - pmod<NS>(kmax - s);
+      act[kb] = any_keys && blk[kb] >= kmin && blk[kb] >= 0;
+      if constexpr (WINDOWED) {
+        if (act[kb] && blk[kb] != st.cur[kb]) {
+          if (st.cur[kb] >= 0) flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
+          take_block<D, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, blk[kb], n, s);
+          st.cur[kb] = blk[kb];
+        }
+      }
+    }
+    if (WINDOWED || j == 0) __syncthreads();  // tile, lse, K^T staging and gate terms visible
+
+    // ---- 2. softmax: D_i = sum_j p_ij dp_ij, exactly as defined (not <dO_i, O_i> of the rounded
+    // forward output). S^T = K Q^T and dP^T = V dO^T put the query on the lane; the waves' partial
+    // sums are combined in a fixed order (deterministic).
+    if constexpr (softmax) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        float part = 0.0f;
+        const int rf = r0 + qs * 32;
+        const int row = rf + lc;
+        bf16x8 qb[G::KK], db[G::KK];
+#pragma unroll
+        for (int kk = 0; kk < G::KK; ++kk) {
+          qb[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_QN + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+          db[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_DON + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+        }
+        const float l2 = lse2[qs * 32 + lc];
+#pragma unroll
+        for (int kb = 0; kb < KACT; ++kb) {
+          const int kf = blk[kb] * kBwdKeyBlock;
+          const BlockMask bm = block_mask(kf, rf, n, L, wl, wr);
+          if (!act[kb] || bm.empty) continue;
+          const int s = kb * G::NW + w;
+          f32x16 st_ = f32x16{}, dpt = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < G::KK; ++kk) {
+            st_ = mfma32(st.kreg[kb][kk], qb[kk], st_);
+            dpt = mfma32(st.vreg[kb][kk], db[kk], dpt);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kloc = c_row(r, g);
+            const int key = kf + kloc;
+            float x = st_[r] * sc;
+            if constexpr (has_gate) x += gl[s * kBwdKeyBlock + kloc];
+            const bool ok = (key < n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+            part += ok ? fast_exp2(x - l2) * dpt[r] : 0.0f;
+          }
+        }
+        part += __shfl_xor(part, 32);
+        if (g == 0) dpart[w * G::QT + qs * 32 + lc] = part;
+      }
+      __syncthreads();
+    }
+
+    // ---- 3. S, dP, P, dS; dV, dK; dS^T to LDS. Iteration it = (query half qs, owned block kb);
+    // the S / dP products of iteration it+1 are issued before the element-wise work of it, so the
+    // MFMA pipe runs while the VALU works.
+    {
+      constexpr int NIT = 2 * KACT;
+      f32x16 sacc[2], dpacc[2];
+      bf16x8 qa[G::KK], da[G::KK];
+      bf16x8 dota[G::DT][2], qta[G::DT][2];
+      float lrow[16], drow[16];
+      auto load_a = [&](int qs) {
+#pragma unroll
+        for (int kk = 0; kk < G::KK; ++kk) {
+          qa[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_QN + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+          da[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_DON + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+        }
+      };
+      auto issue_sdp = [&](int kb, int slot) {
+        sacc[slot] = f32x16{};
+        dpacc[slot] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < G::KK; ++kk) {
+          sacc[slot] = mfma32(qa[kk], st.kreg[kb][kk], sacc[slot]);
+          dpacc[slot] = mfma32(da[kk], st.vreg[kb][kk], dpacc[slot]);
+        }
+      };
+      load_a(0);
+      issue_sdp(0, 0);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int qs = it / KACT, kb = it % KACT, cs = it & 1;
+        if (it + 1 < NIT) {
+          if ((it + 1) / KACT != qs) load_a((it + 1) / KACT);
+          issue_sdp((it + 1) % KACT, cs ^ 1);
+        }
+        const int rf = r0 + qs * 32;
+        if (kb == 0) {
+          // per half: dO^T / Q^T operands of dV^T, dK^T (shared by the owned blocks) and, for
+          // softmax, the rows' lse and D (register group a = rows qs*32 + a*8 + g*4 + 0..3)
+#pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              dota[dt][t] = tr_operand<G::NROW>(lds, G::OFF_DON, qs, t, dt);
+              qta[dt][t] = tr_operand<G::NROW>(lds, G::OFF_QN, qs, t, dt);
+            }
+          if constexpr (softmax) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int rr = qs * 32 + a * 8 + g * 4;
+              const f32x4 lv = *reinterpret_cast<const f32x4*>(lse2 + rr);
+              f32x4 dsum = *reinterpret_cast<const f32x4*>(dpart + rr);
+#pragma unroll
+              for (int ww = 1; ww < G::NW; ++ww) dsum += *reinterpret_cast<const f32x4*>(dpart + ww * G::QT + rr);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lrow[4 * a + e] = lv[e];
+                drow[4 * a + e] = dsum[e];
+              }
+            }
+          }
+        }
+        const int s = kb * G::NW + w;
+        const int kf = blk[kb] * kBwdKeyBlock;
+        const int key = kf + lc;  // this lane's key
+        const int spos = (s * kBwdKeyBlock + lc) * G::SXROW;
+        // P and dS as bf16 B operands (k-tile t = registers 8t..8t+7); zero for a block outside
+        // the tile. The softmax form also carries the rounding remainder as a second bf16 term
+        // (x ~ hi + lo): its products mix a few large probabilities, whose bf16 rounding alone
+        // would exceed the tolerance.
+        u32x4 pu[2], du[2], plu[2], dlu[2];
+        auto elementwise = [&]() {
+          // register r is query row rf + c_row(r, g), key `key`
+          float p[16], ds[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (softmax) {
+              float x;
+              if constexpr (has_gate) x = __builtin_fmaf(sacc[cs][r], sc, st.gate[kb]);
+              else x = sacc[cs][r] * sc;
+              p[r] = fast_exp2(x - lrow[r]);
+              ds[r] = p[r] * (dpacc[cs][r] - drow[r]);
+            } else {
+              float dphi;
+              if constexpr (has_gate) {
+                PointAct<ACT>::value_grad(__builtin_fmaf(sacc[cs][r], sc, st.gate[kb]), 1.0f, c1, c3, p[r], dphi);
+              } else {
+                PointAct<ACT>::value_grad(sacc[cs][r], sc, c1, c3, p[r], dphi);
+              }
+              ds[r] = dpacc[cs][r] * dphi;
+            }
+          }
+          if constexpr (MASKED) {
+            if (!block_mask(kf, rf, n, L, wl, wr).full) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = rf + c_row(r, g);
+                const bool ok = (key < n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+                p[r] = ok ? p[r] : 0.0f;
+                ds[r] = ok ? ds[r] : 0.0f;
+              }
+            }
+          }
+          if constexpr (GATED) if (want_dg) {
+            float dsum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dsum += ds[r];
+            st.dgs[kb] += dsum;
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pu[t][e] = pack_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
+              du[t][e] = pack_bf16x2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1]);
+              if constexpr (softmax) {
+                plu[t][e] = pack_bf16x2(p[8 * t + 2 * e] - bf16_lo(pu[t][e]), p[8 * t + 2 * e + 1] - bf16_hi(pu[t][e]));
+                dlu[t][e] = pack_bf16x2(ds[8 * t + 2 * e] - bf16_lo(du[t][e]), ds[8 * t + 2 * e + 1] - bf16_hi(du[t][e]));
+              }
+            }
+        };
+        if constexpr (MASKED) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) pu[t] = du[t] = plu[t] = dlu[t] = u32x4{0u, 0u, 0u, 0u};
+          if (act[kb] && !block_mask(kf, rf, n, L, wl, wr).empty) elementwise();
+        } else {
+          // no mask: keys and rows past the ends meet zero operands, and phi(0) = 0
+          elementwise();
+        }
+        // dS^T to the exchange tile: registers 4a..4a+3 are 4 consecutive query rows
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int qo = (qs * 32 + a * 8 + g * 4) * 2;
+          const int t = a >> 1, hlf = (a & 1) * 2;
+          *reinterpret_cast<u32x2*>(lds + G::OFF_SX + spos + qo) = u32x2{du[t][hlf], du[t][hlf + 1]};
+          if constexpr (softmax)
+            *reinterpret_cast<u32x2*>(lds + G::OFF_SXL + spos + qo) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(pu[t]), st.dv[kb][dt]);
+            st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(du[t]), st.dk[kb][dt]);
+            if constexpr (softmax) {
+              st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(plu[t]), st.dv[kb][dt]);
+              st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(dlu[t]), st.dk[kb][dt]);
+            }
+          }
+      }
+    }
+    __syncthreads();  // dS^T tile complete; this tile's Q / dO / lse no longer read
+    if (j + 1 < ntiles) {
+      // next tile into LDS (while dQ runs), then the loads of the one after it: issued before this
+      // tile's dQ stores, so waiting for them never waits for those stores
+      store_qtile<D, softmax>(lds, pf);
+      if (j + 2 < ntiles) prefetch_qtile<D, softmax>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L);
+    }
+
+    // ---- 4. dQ^T = K^T dS^T over the ring slots in use (a slot outside the tile holds zero dS);
+    // register r of lane (query, g) is d = dtile*32 + g*16 + r (out_perm order of the K^T rows)
+    if (dq_role) {
+      const int drow = dtile * 32 + out_perm(lc);  // K^T row carried by this lane's A-operand row
+#pragma unroll
+      for (int qi = 0; qi < G::QH; ++qi) {
+        const int qh = qh_first + qi;
+        // 16-key steps over the slots in use; the operands of step k+1 are read while step k
+        // multiplies, and two accumulators keep consecutive MFMAs independent
+        constexpr int NK = 2 * NS;
+        bf16x8 ka[2], sb[2], sl[2];
+        auto load_step = [&](int k, int buf) {
+          const int kbase = k * 16;
+          ka[buf] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_KT + drow * G::KTROW + (kbase + g * 8) * 2));
+          sb[buf] = sx_operand<G::SXROW>(lds, G::OFF_SX, kbase, qh);
+          if constexpr (softmax) sl[buf] = sx_operand<G::SXROW>(lds, G::OFF_SXL, kbase, qh);
+        };
+        f32x16 acc2[2] = {f32x16{}, f32x16{}};
+        load_step(0, 0);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          if (k + 1 < NK) load_step(k + 1, (k + 1) & 1);
+          acc2[k & 1] = mfma32(ka[k & 1], sb[k & 1], acc2[k & 1]);
+          if constexpr (softmax) acc2[k & 1] = mfma32(ka[k & 1], sl[k & 1], acc2[k & 1]);
+        }
+        const f32x16 acc = acc2[0] + acc2[1];
+        const int row = r0 + qh * 32 + lc;
+        if (row < L) {
+          u32x4 u0, u1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            u0[e] = pack_bf16x2(acc[2 * e] * gd.scale, acc[2 * e + 1] * gd.scale);
+            u1[e] = pack_bf16x2(acc[8 + 2 * e] * gd.scale, acc[8 + 2 * e + 1] * gd.scale);
+          }
+          bf16* dst = it.dqseq + row * rs + dtile * 32 + g * 16;
+          *reinterpret_cast<u32x4*>(dst) = u0;
+          *reinterpret_cast<u32x4*>(dst + 8) = u1;
+        }
+      }
+    }
+    if (j + 1 < ntiles) __syncthreads();  // next tile staged; dS^T and K^T staging free
+  }
+#pragma unroll
+  for (int kb = 0; kb < KACT; ++kb)
+    if (st.cur[kb] >= 0) flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
+}
+
+template <int D, int ACT, bool GATED>
+__device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
+  using G = BwdGeo<D>;
+  BwdItem it;
+  const int q0 = gd.q_off[b], k0 = gd.kv_off[b];
+  it.L = gd.q_off[b + 1] - q0;
+  it.n = gd.kv_off[b + 1] - k0;
+  it.H = gd.num_heads;
+  it.rs = (size_t)it.H * D;
+  it.wl = gd.wl;
+  it.wr = gd.wr;
+  const int H = it.H;
+  it.qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
+  it.doseq = reinterpret_cast<const bf16*>(gd.dout) + ((size_t)q0 * H + h) * D;
+  it.lseseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
+  it.dqseq = reinterpret_cast<bf16*>(gd.dq) + ((size_t)q0 * H + h) * D;
+  it.kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
+  it.vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;
+  it.gseq = gd.g ? gd.g + (size_t)k0 * H + h : nullptr;
+  it.dkseq = reinterpret_cast<bf16*>(gd.dk) + ((size_t)k0 * H + h) * D;
+  it.dvseq = reinterpret_cast<bf16*>(gd.dv) + ((size_t)k0 * H + h) * D;
+  it.dgseq = gd.dg ? gd.dg + (size_t)k0 * H + h : nullptr;
+  const int L = it.L, n = it.n;
+  const size_t rs = it.rs;
+
+  if (n <= 0) {  // no keys: dQ = 0
+    for (int idx = threadIdx.x; idx < L * G::CPR; idx += G::THREADS) {
+      const int r = idx / G::CPR, c = idx % G::CPR;
+      *reinterpret_cast<u32x4*>(it.dqseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  if (L <= 0) {  // no queries: dK = dV = dG = 0
+    for (int idx = threadIdx.x; idx < n * G::CPR; idx += G::THREADS) {
+      const int r = idx / G::CPR, c = idx % G::CPR;
+      *reinterpret_cast<u32x4*>(it.dkseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(it.dvseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (it.dgseq)
+      for (int r = threadIdx.x; r < n; r += G::THREADS) it.dgseq[(size_t)r * H] = 0.0f;
+    return;
+  }
+  // One owned block per wave suffices when all keys fit in NW blocks. Zero padding makes the
+  // entries past the ends vanish for the element-wise forms (phi(0) = 0; dO and V rows past the
+  // ends are zero), so only the softmax form and windows need explicit masks.
+  const bool few_keys = (n + kBwdKeyBlock - 1) / kBwdKeyBlock <= G::NW;
+  const bool windowed = it.wl >= 0 || it.wr >= 0;
+  if (windowed) {
+    if (G::KB > 1 && few_keys) bwd_sweep<D, ACT, GATED, 1, true>(lds, gd, it);
+    else bwd_sweep<D, ACT, GATED, G::KB, true>(lds, gd, it);
+  } else {
+    if (G::KB > 1 && few_keys) bwd_sweep<D, ACT, GATED, 1, false>(lds, gd, it);
+    else bwd_sweep<D, ACT, GATED, G::KB, false>(lds, gd, it);
+  }
+}
+
+template <int D, int ACT>
+__device__ __forceinline__ void bwd_dispatch_gate(char* lds, const GroupDesc& gd, int b, int h) {
+  if (gd.g != nullptr) bwd_item<D, ACT, true>(lds, gd, b, h);
+  else bwd_item<D, ACT, false>(lds, gd, b, h);
+}
+
+template <int D, int ASET>
+__device__ __forceinline__ void bwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
+  if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
+    if (gd.act == GDPA_ACT_GELU) { bwd_dispatch_gate<D, GDPA_ACT_GELU>(lds, gd, b, h); return; }
+  if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
+    if (gd.act == GDPA_ACT_SILU) { bwd_dispatch_gate<D, GDPA_ACT_SILU>(lds, gd, b, h); return; }
+  if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
+    if (gd.act == GDPA_ACT_SOFTMAX) bwd_dispatch_gate<D, GDPA_ACT_SOFTMAX>(lds, gd, b, h);
+}
+
+template <int DSET, int ASET>
+__global__ void __launch_bounds__(kBwdWaves * kWave, 1) bwd_bf16_kernel(LaunchDesc d) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  if ((int)blockIdx.x >= d.n_items) return;
+  int g, h, b;
+  unpack_item(d.items[blockIdx.x], g, h, b);
+  if (g >= d.n_groups) return;
+  const GroupDesc gd = select_group(d, g);
+  if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
+  if constexpr ((DSET & kDim32) != 0)
+    if (gd.head_dim == 32) { bwd_dispatch_act<32, ASET>(lds, gd, b, h); return; }
+  if constexpr ((DSET & kDim64) != 0)
+    if (gd.head_dim == 64) { bwd_dispatch_act<64, ASET>(lds, gd, b, h); return; }
+  if constexpr ((DSET & kDim128) != 0)
+    if (gd.head_dim == 128) { bwd_dispatch_act<128, ASET>(lds, gd, b, h); return; }
+}
+
+}  // namespace gdpa

@@ -24,6 +24,11 @@
 
 namespace gdpa {
 
+// Waves per workgroup. Two workgroups share a CU (LDS bound), so six waves give three waves per
+// SIMD when the register footprint allows it (launches without d = 128 problems); else four.
+template <int DSET>
+constexpr int fwd_waves() { return (DSET & kDim128) ? 4 : 4; }
+
 template <int D>
 struct FwdGeo {
   static constexpr int NKV = 16384 / D;        // keys that fit in LDS
@@ -45,13 +50,13 @@ constexpr int kFwdLdsBytes = FwdGeo<32>::BYTES > FwdGeo<64>::BYTES
 __device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
 
 // Stage keys [k0, k0 + span) of one (sequence, head) into LDS; rows up to span_pad are zeroed.
-template <int D>
+template <int D, int NT>
 __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
                          int span, int span_pad, bool softmax) {
   using G = FwdGeo<D>;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   const size_t rs = (size_t)hstride * D;
-  for (int idx = threadIdx.x; idx < span_pad * CPR; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < span_pad * CPR; idx += NT) {
     const int r = idx / CPR, c = idx % CPR;
     u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (r < span) {
@@ -69,7 +74,7 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
     }
   }
   float* gl = reinterpret_cast<float*>(lds + G::OFF_G);
-  for (int r = threadIdx.x; r < span_pad; r += kThreads) {
+  for (int r = threadIdx.x; r < span_pad; r += NT) {
     float t = 0.0f;
     if (gb != nullptr && r < span) {
       t = log_sigmoid_f(gb[(size_t)r * hstride]);
@@ -118,9 +123,11 @@ __device__ inline void scores_block(const char* lds, const QFrags<D, QS>& q, int
   }
 }
 
-template <int D, int ACT, int QS>
-__device__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
-                         float* lseq, int L, int N, int row0, int klo, int span, int kb0, int kb1) {
+// GATED: the problem has a gate. MASKED: entries may need an explicit mask (the softmax form, or
+// a window); without it, keys past the end meet zero K and V rows in LDS and phi(0) = 0.
+template <int D, int ACT, int QS, bool GATED, bool MASKED>
+__device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
+                                         float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   using G = FwdGeo<D>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
   const int H = gd.num_heads;
@@ -138,62 +145,42 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, Q
   }
   const float sc = softmax ? gd.scale * kLog2e : gd.scale;
   const int wl = gd.wl, wr = gd.wr;
-  const bool windowed = wl >= 0 || wr >= 0;
-  const bool has_gate = gd.g != nullptr;
   // element-wise forms: without a gate p' = s g(scale s) = phi(scale s) / scale and O is scaled
   // once in the epilogue; with a gate the argument scale s + log sigmoid(G) is formed first.
   float c1 = 0.0f, c3 = 0.0f;
-  if constexpr (!softmax) PointAct<ACT>::coeffs(has_gate ? 1.0f : gd.scale, c1, c3);
-  const float out_scale = (!softmax && !has_gate) ? gd.scale : 1.0f;
+  if constexpr (!softmax) PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
+  const float out_scale = (!softmax && !GATED) ? gd.scale : 1.0f;
 
-  // Software pipeline: the score MFMAs of block kb+1 are issued before the element-wise work of
-  // block kb, so the matrix cores run while the vector units evaluate the activation.
-  f32x16 s_next[QS];
-  if (kb0 < kb1) scores_block<D, QS>(lds, qf, kb0, s_next);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    f32x16 s[QS];
+  // Element-wise stage and P V for block kb whose scores are in s: register r of lane (qc, g) is
+  // key kb*32 + c_row(r, g), row qs*32 + qc.
+  auto process = [&](int kb, const f32x16 (&s)[QS]) {
+    float p[QS][16];
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) s[qs] = s_next[qs];
-    if (kb + 1 < kb1) scores_block<D, QS>(lds, qf, kb + 1, s_next);
-    // element-wise stage: register r of lane (qc, g) is key kb*32 + c_row(r, g), row qs*32 + qc.
-    // Padded keys (beyond the staged range) have zero K and V rows in LDS, so the element-wise
-    // forms need a mask only inside a window; the softmax form also masks the padded keys.
-    bool full_block = (kb * 32 + 32 <= span);
-    if (windowed) {
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x;
+        if constexpr (GATED) x = __builtin_fmaf(s[qs][r], sc, gl[kb * 32 + c_row(r, g)]);
+        if constexpr (softmax) p[qs][r] = GATED ? x : s[qs][r] * sc;
+        else p[qs][r] = GATED ? PointAct<ACT>::value(x, c1, c3) : PointAct<ACT>::value(s[qs][r], c1, c3);
+      }
+    if constexpr (MASKED) {
+      bool full_block = (kb * 32 + 32 <= span);
       const int kfirst = klo + kb * 32, klast = kfirst + 31;
       const int rfirst = row0, rlast = row0 + QS * 32 - 1;
       if (wl >= 0 && kfirst < rlast - wl) full_block = false;
       if (wr >= 0 && klast > rfirst + wr) full_block = false;
-    }
-    float p[QS][16];
-    if (has_gate) {
+      if (!full_block) {
 #pragma unroll
-      for (int qs = 0; qs < QS; ++qs)
+        for (int qs = 0; qs < QS; ++qs) {
+          const int row = row0 + qs * 32 + qc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = __builtin_fmaf(s[qs][r], sc, gl[kb * 32 + c_row(r, g)]);
-          if constexpr (softmax) p[qs][r] = x;
-          else p[qs][r] = PointAct<ACT>::value(x, c1, c3);
-        }
-    } else {
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (softmax) p[qs][r] = s[qs][r] * sc;
-          else p[qs][r] = PointAct<ACT>::value(s[qs][r], c1, c3);
-        }
-    }
-    if (!full_block && (softmax || windowed)) {
-#pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        const int row = row0 + qs * 32 + qc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = kb * 32 + c_row(r, g);
-          const int kpos = klo + kl;
-          const bool ok = (kl < span) & ((wl < 0) | (kpos >= row - wl)) & ((wr < 0) | (kpos <= row + wr));
-          p[qs][r] = ok ? p[qs][r] : (softmax ? -__builtin_inff() : 0.0f);
+          for (int r = 0; r < 16; ++r) {
+            const int kl = kb * 32 + c_row(r, g);
+            const int kpos = klo + kl;
+            const bool ok = (kl < span) & ((wl < 0) | (kpos >= row - wl)) & ((wr < 0) | (kpos <= row + wr));
+            p[qs][r] = ok ? p[qs][r] : (softmax ? -__builtin_inff() : 0.0f);
+          }
         }
       }
     }
@@ -240,6 +227,26 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, Q
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) o[qs][dt] = mfma32(vf, pf[qs][t], o[qs][dt]);
       }
+  };
+
+  // Software pipeline over pairs of blocks with two score buffers: the score MFMAs of the next
+  // block are issued before the element-wise work of the current one, so the matrix cores run
+  // while the vector units evaluate the activation; the loop body has no branches.
+  f32x16 sa[QS], sb[QS];
+  int kb = kb0;
+  if (kb < kb1) scores_block<D, QS>(lds, qf, kb, sa);
+  for (; kb + 2 < kb1; kb += 2) {
+    scores_block<D, QS>(lds, qf, kb + 1, sb);
+    process(kb, sa);
+    scores_block<D, QS>(lds, qf, kb + 2, sa);
+    process(kb + 1, sb);
+  }
+  if (kb + 1 < kb1) {
+    scores_block<D, QS>(lds, qf, kb + 1, sb);
+    process(kb, sa);
+    process(kb + 1, sb);
+  } else if (kb < kb1) {
+    process(kb, sa);
   }
 
   // epilogue
@@ -268,12 +275,11 @@ __device__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, Q
       if (softmax && g == 0) lseq[(size_t)row * H] = lse;
     }
   }
-  (void)N;
 }
 
 // One work item: all query rows of one (sequence, head).
-template <int D, int ACT, int QS>
-__device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
+template <int D, int NW, int ACT, int QS, bool GATED, bool MASKED>
+__device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   using G = FwdGeo<D>;
   const int q0 = gd.q_off[b], L = gd.q_off[b + 1] - q0;
   const int k0 = gd.kv_off[b], N = gd.kv_off[b + 1] - k0;
@@ -293,18 +299,18 @@ __device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   if (N <= G::NKV) {
     // whole key range resident: stage once, sweep all query tiles
     const int span_pad = (N + 31) & ~31;
-    stage_kv<D>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
+    stage_kv<D, NW * kWave>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
     __syncthreads();
     QFrags<D, QS> qcur, qnext;
     if (w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
-    for (int row0 = w * RW; row0 < L; row0 += 4 * RW) {
+    for (int row0 = w * RW; row0 < L; row0 += NW * RW) {
       // next tile's Q is loaded while this tile computes
-      if (row0 + 4 * RW < L) load_q<D, QS>(qnext, qseq, rs, row0 + 4 * RW, L);
+      if (row0 + NW * RW < L) load_q<D, QS>(qnext, qseq, rs, row0 + NW * RW, L);
       int lo = 0, hi = N - 1;
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
-      fwd_tile<D, ACT, QS>(lds, gd, qcur, oseq, lseq, L, N, row0, 0, N, kb0, kb1);
+      fwd_tile<D, ACT, QS, GATED, MASKED>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       qcur = qnext;
     }
   } else {
@@ -316,46 +322,60 @@ __device__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
       if (khi > N) khi = N;
       const int span = khi - klo;
       __syncthreads();  // previous chunk done with LDS
-      stage_kv<D>(lds, kseq + (size_t)klo * H * D, vseq + (size_t)klo * H * D,
+      stage_kv<D, NW * kWave>(lds, kseq + (size_t)klo * H * D, vseq + (size_t)klo * H * D,
                   gseq ? gseq + (size_t)klo * H : nullptr, H, span, (span + 31) & ~31, softmax);
       __syncthreads();
-      for (int row0 = r0 + w * RW; row0 < r0 + kFwdChunkRows && row0 < L; row0 += 4 * RW) {
+      for (int row0 = r0 + w * RW; row0 < r0 + kFwdChunkRows && row0 < L; row0 += NW * RW) {
         int lo = row0 - gd.wl > klo ? row0 - gd.wl : klo;
         int hi = row0 + RW - 1 + gd.wr < khi - 1 ? row0 + RW - 1 + gd.wr : khi - 1;
         const int kb0 = (lo - klo) / 32, kb1 = hi >= lo ? (hi - klo) / 32 + 1 : kb0;
         QFrags<D, QS> qf;
         load_q<D, QS>(qf, qseq, rs, row0, L);
-        fwd_tile<D, ACT, QS>(lds, gd, qf, oseq, lseq, L, N, row0, klo, span, kb0, kb1);
+        fwd_tile<D, ACT, QS, GATED, MASKED>(lds, gd, qf, oseq, lseq, L, row0, klo, span, kb0, kb1);
       }
     }
   }
 }
 
-template <int D, int ASET>
-__device__ void fwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
+// Gate and mask variants of one activation: the chunked window path and the softmax form are
+// masked; a problem without window or softmax runs the mask-free body.
+template <int D, int NW, int ACT, int QS>
+__device__ __forceinline__ void fwd_dispatch_variant(char* lds, const GroupDesc& gd, int b, int h) {
+  const bool masked = ACT == GDPA_ACT_SOFTMAX || gd.wl >= 0 || gd.wr >= 0;
+  if (gd.g != nullptr) {
+    if (masked) fwd_item<D, NW, ACT, QS, true, true>(lds, gd, b, h);
+    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, true, false>(lds, gd, b, h);
+  } else {
+    if (masked) fwd_item<D, NW, ACT, QS, false, true>(lds, gd, b, h);
+    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, false, false>(lds, gd, b, h);
+  }
+}
+
+template <int D, int NW, int ASET>
+__device__ __forceinline__ void fwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
   const bool chunked = (gd.kv_off[b + 1] - gd.kv_off[b]) > FwdGeo<D>::NKV;
-  constexpr int QS2 = D <= 64 ? 2 : 1;
+  constexpr int QS2 = 1;
   if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
     if (gd.act == GDPA_ACT_GELU) {
-      if (chunked) fwd_item<D, GDPA_ACT_GELU, 1>(lds, gd, b, h);
-      else fwd_item<D, GDPA_ACT_GELU, QS2>(lds, gd, b, h);
+      if (chunked) fwd_dispatch_variant<D, NW, GDPA_ACT_GELU, 1>(lds, gd, b, h);
+      else fwd_dispatch_variant<D, NW, GDPA_ACT_GELU, QS2>(lds, gd, b, h);
       return;
     }
   if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
     if (gd.act == GDPA_ACT_SILU) {
-      if (chunked) fwd_item<D, GDPA_ACT_SILU, 1>(lds, gd, b, h);
-      else fwd_item<D, GDPA_ACT_SILU, QS2>(lds, gd, b, h);
+      if (chunked) fwd_dispatch_variant<D, NW, GDPA_ACT_SILU, 1>(lds, gd, b, h);
+      else fwd_dispatch_variant<D, NW, GDPA_ACT_SILU, QS2>(lds, gd, b, h);
       return;
     }
   if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
     if (gd.act == GDPA_ACT_SOFTMAX) {
-      if (chunked) fwd_item<D, GDPA_ACT_SOFTMAX, 1>(lds, gd, b, h);
-      else fwd_item<D, GDPA_ACT_SOFTMAX, QS2>(lds, gd, b, h);
+      if (chunked) fwd_dispatch_variant<D, NW, GDPA_ACT_SOFTMAX, 1>(lds, gd, b, h);
+      else fwd_dispatch_variant<D, NW, GDPA_ACT_SOFTMAX, QS2>(lds, gd, b, h);
     }
 }
 
 template <int DSET, int ASET>
-__global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(LaunchDesc d) {
+__global__ void __launch_bounds__(fwd_waves<DSET>() * kWave, 2) fwd_bf16_kernel(LaunchDesc d) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if ((int)blockIdx.x >= d.n_items) return;
   int g, h, b;
@@ -364,18 +384,19 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(LaunchDesc d) {
   const GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
   if constexpr ((DSET & kDim32) != 0)
-    if (gd.head_dim == 32) { fwd_dispatch_act<32, ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 32) { fwd_dispatch_act<32, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim64) != 0)
-    if (gd.head_dim == 64) { fwd_dispatch_act<64, ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 64) { fwd_dispatch_act<64, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim128) != 0)
-    if (gd.head_dim == 128) { fwd_dispatch_act<128, ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 128) { fwd_dispatch_act<128, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
 }
 
 hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream) {
   if (d.n_items == 0) return hipSuccess;
-  const dim3 grid(d.n_items), block(kThreads);
+  const dim3 grid(d.n_items);
   constexpr int kAll = (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX);
-#define GDPA_LAUNCH(DS, AS) hipLaunchKernelGGL((fwd_bf16_kernel<DS, AS>), grid, block, kFwdLdsBytes, stream, d)
+#define GDPA_LAUNCH(DS, AS) \
+  hipLaunchKernelGGL((fwd_bf16_kernel<DS, AS>), grid, dim3(fwd_waves<DS>() * kWave), kFwdLdsBytes, stream, d)
 #define GDPA_LAUNCH_ACTS(DS)                                          \
   switch (act_set) {                                                  \
     case 1 << GDPA_ACT_GELU: GDPA_LAUNCH(DS, 1 << GDPA_ACT_GELU); break;  \

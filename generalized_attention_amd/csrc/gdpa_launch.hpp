@@ -35,16 +35,19 @@ inline bool fwd_shape_ok(int d, int wl, int wr, int max_kv) {
   if (max_kv <= cap) return true;
   return wl >= 0 && wr >= 0 && wl + wr + kFwdChunkRows <= cap;
 }
-// Backward: each wave owns a block of 32 keys; 8 waves per workgroup, or 4 when the launch holds
-// any d = 128 problem; query tiles of 64 rows.
+// Backward: 4 waves per workgroup; each wave owns 64 keys (two blocks of 32; 32 keys at d = 128)
+// for the whole sweep over query tiles of 64 rows.
+constexpr int kBwdWaves = 4;
 constexpr int kBwdKeyBlock = 32;
 constexpr int kBwdQueryTile = 64;
-inline int bwd_waves_for(bool launch_has_d128) { return launch_has_d128 ? 4 : 8; }
-// Either all keys are resident (one block per wave), or a bounded window whose key span for one
-// query tile touches at most `waves` blocks.
-inline bool bwd_shape_ok(int waves, int wl, int wr, int max_kv) {
-  if (max_kv <= waves * kBwdKeyBlock) return true;
-  return wl >= 0 && wr >= 0 && kBwdQueryTile - 1 + wl + wr <= (waves - 1) * kBwdKeyBlock;
+inline constexpr int bwd_keys_per_wave(int d) { return d == 128 ? 32 : 64; }
+inline constexpr int bwd_capacity(int d) { return kBwdWaves * bwd_keys_per_wave(d); }
+// Either all keys of a sequence are resident at once, or a bounded window whose key span for one
+// query tile fits in the ring of resident blocks with one block to spare (misalignment).
+inline bool bwd_shape_ok(int d, int wl, int wr, int max_kv) {
+  const int cap = bwd_capacity(d);
+  if (max_kv <= cap) return true;
+  return wl >= 0 && wr >= 0 && kBwdQueryTile - 1 + wl + wr <= cap - kBwdKeyBlock;
 }
 
 }  // namespace gdpa
