@@ -50,37 +50,88 @@ constexpr int kFwdLdsBytes = FwdGeo<32>::BYTES > FwdGeo<64>::BYTES
 __device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
 
 // Stage keys [k0, k0 + span) of one (sequence, head) into LDS; rows up to span_pad are zeroed.
+// Every global load of the range is issued before the first LDS write, so the staging costs one
+// memory latency. K rows are copied as 16-byte chunks; V is transposed in units of 4 consecutive
+// keys x 8 d: the 4 keys of one d are adjacent in the V^T slot order, so each d is one 8-byte
+// write.
 template <int D, int NT>
 __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
                          int span, int span_pad, bool softmax) {
   using G = FwdGeo<D>;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int CPR = D / 8;                                  // 16-byte chunks per row
+  constexpr int KI = (G::NKV * CPR + NT - 1) / NT;           // K chunks per thread (at most)
+  constexpr int VI = (G::NKV / 4 * CPR + NT - 1) / NT;       // V units per thread (at most)
+  constexpr int GI = (G::NKV + NT - 1) / NT;                 // gate values per thread
+  // d = 128: one round per 16-byte chunk group (the d = 128 kernels have no registers to spare)
+  constexpr int ROUNDS = D == 128 ? KI : 1;
+  static_assert(KI % ROUNDS == 0, "staging rounds");
   const size_t rs = (size_t)hstride * D;
-  for (int idx = threadIdx.x; idx < span_pad * CPR; idx += NT) {
-    const int r = idx / CPR, c = idx % CPR;
-    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (r < span) {
-      kv = *reinterpret_cast<const u32x4*>(kb + r * rs + c * 8);
-      vv = *reinterpret_cast<const u32x4*>(vb + r * rs + c * 8);
-    }
-    *reinterpret_cast<u32x4*>(lds + r * G::KROW + c * 16) = kv;
-    const int pos = vt_pos(r);
-    char* vt = lds + G::OFF_V + pos * 2;
+  float gv[GI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = vv[i];
-      *reinterpret_cast<uint16_t*>(vt + (c * 8 + 2 * i) * G::VROW) = (uint16_t)(w & 0xFFFF);
-      *reinterpret_cast<uint16_t*>(vt + (c * 8 + 2 * i + 1) * G::VROW) = (uint16_t)(w >> 16);
+  for (int i = 0; i < GI; ++i) {
+    const int r = threadIdx.x + i * NT;
+    gv[i] = 0.0f;
+    if (gb != nullptr && r < span) gv[i] = gb[(size_t)r * hstride];
+  }
+#pragma unroll
+  for (int round = 0; round < ROUNDS; ++round) {
+    constexpr int KR = KI / ROUNDS, VR = (VI + ROUNDS - 1) / ROUNDS;
+    u32x4 kbuf[KR], vbuf[VR][4];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int idx = threadIdx.x + (round * KR + i) * NT;
+      const int r = idx / CPR, c = idx % CPR;
+      kbuf[i] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < span_pad * CPR && r < span) kbuf[i] = *reinterpret_cast<const u32x4*>(kb + r * rs + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VR; ++i) {
+      const int u = threadIdx.x + (round * VR + i) * NT;
+      const int r4 = (u / CPR) * 4, c = u % CPR;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vbuf[i][e] = u32x4{0u, 0u, 0u, 0u};
+        if (u < span_pad / 4 * CPR && r4 + e < span)
+          vbuf[i][e] = *reinterpret_cast<const u32x4*>(vb + (r4 + e) * rs + c * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int idx = threadIdx.x + (round * KR + i) * NT;
+      const int r = idx / CPR, c = idx % CPR;
+      if (idx < span_pad * CPR) *reinterpret_cast<u32x4*>(lds + r * G::KROW + c * 16) = kbuf[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VR; ++i) {
+      const int u = threadIdx.x + (round * VR + i) * NT;
+      const int r4 = (u / CPR) * 4, c = u % CPR;
+      if (u < span_pad / 4 * CPR) {
+        char* vt = lds + G::OFF_V + vt_pos(r4) * 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // d = 8c + e of keys r4 .. r4+3: 16-bit half (e & 1) of word e / 2 of each key's chunk
+          const int wd = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x2 pk;
+          pk[0] = __builtin_amdgcn_perm(vbuf[i][1][wd], vbuf[i][0][wd], sel);
+          pk[1] = __builtin_amdgcn_perm(vbuf[i][3][wd], vbuf[i][2][wd], sel);
+          *reinterpret_cast<u32x2*>(vt + (c * 8 + e) * G::VROW) = pk;
+        }
+      }
     }
   }
   float* gl = reinterpret_cast<float*>(lds + G::OFF_G);
-  for (int r = threadIdx.x; r < span_pad; r += NT) {
-    float t = 0.0f;
-    if (gb != nullptr && r < span) {
-      t = log_sigmoid_f(gb[(size_t)r * hstride]);
-      if (softmax) t *= kLog2e;
+#pragma unroll
+  for (int i = 0; i < GI; ++i) {
+    const int r = threadIdx.x + i * NT;
+    if (r < span_pad) {
+      float t = 0.0f;
+      if (gb != nullptr && r < span) {
+        t = log_sigmoid_f(gv[i]);
+        if (softmax) t *= kLog2e;
+      }
+      gl[r] = t;
     }
-    gl[r] = t;
   }
 }
 
@@ -299,19 +350,23 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
   if (N <= G::NKV) {
     // whole key range resident: stage once, sweep all query tiles
     const int span_pad = (N + 31) & ~31;
+    // d <= 64: the first Q tile is in flight during the staging and each next tile's Q during
+    // the current tile (d = 128: the registers do not allow it; Q is loaded per tile)
+    constexpr bool kPrefetchQ = D < 128;
+    QFrags<D, QS> qcur, qnext;
+    if (kPrefetchQ && w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
     stage_kv<D, NW * kWave>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
     __syncthreads();
-    QFrags<D, QS> qcur, qnext;
-    if (w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
     for (int row0 = w * RW; row0 < L; row0 += NW * RW) {
       // next tile's Q is loaded while this tile computes
-      if (row0 + NW * RW < L) load_q<D, QS>(qnext, qseq, rs, row0 + NW * RW, L);
+      if (!kPrefetchQ) load_q<D, QS>(qcur, qseq, rs, row0, L);
+      if (kPrefetchQ && row0 + NW * RW < L) load_q<D, QS>(qnext, qseq, rs, row0 + NW * RW, L);
       int lo = 0, hi = N - 1;
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
       fwd_tile<D, ACT, QS, GATED, MASKED>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
-      qcur = qnext;
+      if (kPrefetchQ) qcur = qnext;
     }
   } else {
     // bounded window (both sides >= 0, checked on the host): chunks of kFwdChunkRows rows
