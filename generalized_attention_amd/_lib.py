@@ -50,6 +50,7 @@ class gdpa_problem(ctypes.Structure):
         ("flags", ctypes.c_int32),
         ("q_offsets", ctypes.c_void_p),
         ("kv_offsets", ctypes.c_void_p),
+        ("head_acts", ctypes.c_void_p),
     ]
 
 

@@ -56,6 +56,9 @@ int check_backward_capacity(const gdpa_problem& p) {
   return bwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK : GDPA_ERR_UNSUPPORTED;
 }
 
+// The problem may contain softmax heads (its own act, or any head when the activation is per head).
+bool may_softmax(const gdpa_problem& p) { return p.act == GDPA_ACT_SOFTMAX || p.head_acts != nullptr; }
+
 int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
   const bool rows = p.total_q > 0, keys = p.total_kv > 0;
   if (rows && (!t.q || !aligned16(t.q))) return GDPA_ERR_INVALID_ARGUMENT;
@@ -64,12 +67,12 @@ int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
   if ((t.g && !aligned16(t.g)) || (t.lse && ((uintptr_t)t.lse & 3u))) return GDPA_ERR_INVALID_ARGUMENT;
   if (pass == 0) {
     if (rows && (!t.o || !aligned16(t.o))) return GDPA_ERR_INVALID_ARGUMENT;
-    if (rows && p.act == GDPA_ACT_SOFTMAX && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
+    if (rows && may_softmax(p) && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
     if (t.dg) return GDPA_ERR_INVALID_ARGUMENT;
   } else {
     if (rows && (!t.dout || !t.dq || !aligned16(t.dout) || !aligned16(t.dq))) return GDPA_ERR_INVALID_ARGUMENT;
     if (keys && (!t.dk || !t.dv || !aligned16(t.dk) || !aligned16(t.dv))) return GDPA_ERR_INVALID_ARGUMENT;
-    if (rows && p.act == GDPA_ACT_SOFTMAX && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
+    if (rows && may_softmax(p) && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
   }
   return GDPA_OK;
 }
@@ -86,7 +89,7 @@ int layout(const gdpa_problem* ps, int n_groups, int pass, WsLayout* L) {
     L->n_seqs += ps[g].num_seqs;
     L->delta_base[g] = L->delta_rows;
     // fp32 softmax backward: per-row D_i between its two kernels
-    if (pass == 1 && ps[g].act == GDPA_ACT_SOFTMAX && ps[g].dtype == GDPA_DTYPE_FP32)
+    if (pass == 1 && may_softmax(ps[g]) && ps[g].dtype == GDPA_DTYPE_FP32)
       L->delta_rows += ps[g].total_q * ps[g].num_heads;
   }
   if (L->n_items >= ((int64_t)1 << 31) || L->n_seqs >= ((int64_t)1 << 31)) return GDPA_ERR_UNSUPPORTED;
@@ -128,6 +131,7 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
     gd.num_heads = p.num_heads;
     gd.head_dim = p.head_dim;
     gd.act = p.act;
+    gd.head_acts = p.head_acts;
     gd.scale = p.scale;
     gd.wl = p.window_left;
     gd.wr = p.window_right;
@@ -181,7 +185,9 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
     if (e == hipSuccess) {
       const int dims = dim_set_of(ps, n_groups);
       int acts = 0;
-      for (int g = 0; g < n_groups; ++g) acts |= 1 << ps[g].act;
+      for (int g = 0; g < n_groups; ++g)
+        acts |= ps[g].head_acts ? (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX)
+                                : 1 << ps[g].act;
       e = pass == 0 ? launch_fwd_bf16(d, dims, acts, s) : launch_bwd_bf16(d, dims, acts, s);
     }
   }

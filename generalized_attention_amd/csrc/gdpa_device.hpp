@@ -39,6 +39,7 @@ struct GroupDesc {
   float* delta;  // softmax backward: D_i = <dO_i, O_i> per (row, head), in the workspace
   const int32_t* q_off;
   const int32_t* kv_off;
+  const int32_t* head_acts;  // activation per head, or null (act for every head)
   int32_t num_seqs;
   int32_t num_heads;
   int32_t head_dim;

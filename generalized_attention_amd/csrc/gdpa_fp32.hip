@@ -61,7 +61,8 @@ __device__ void fwd_row(const GroupDesc& gd, int64_t grow, int h) {
   for (int c = 0; c < D; ++c) { qr[c] = q[c]; acc[c] = 0.0f; }
   int lo, hi;
   key_range(gd, i, n, lo, hi);
-  const bool softmax = gd.act == GDPA_ACT_SOFTMAX;
+  const int act = gd.head_acts ? gd.head_acts[h] : gd.act;
+  const bool softmax = act == GDPA_ACT_SOFTMAX;
   float m = -__builtin_inff(), l = 0.0f;
   for (int j = lo; j <= hi; ++j) {
     const float* kj = K + ((int64_t)(k0 + j) * H + h) * D;
@@ -79,7 +80,7 @@ __device__ void fwd_row(const GroupDesc& gd, int64_t grow, int h) {
       for (int c = 0; c < D; ++c) acc[c] *= a;
       m = mn;
     } else {
-      p = act_f(gd.act, s);
+      p = act_f(act, s);
     }
     for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vj[c], acc[c]);
   }
@@ -104,7 +105,8 @@ __device__ void bwd_row(const GroupDesc& gd, int64_t grow, int h, const float* w
   for (int c = 0; c < D; ++c) { qr[c] = q[c]; dor[c] = dO[c]; dq[c] = 0.0f; }
   int lo, hi;
   key_range(gd, i, n, lo, hi);
-  const bool softmax = gd.act == GDPA_ACT_SOFTMAX;
+  const int act = gd.head_acts ? gd.head_acts[h] : gd.act;
+  const bool softmax = act == GDPA_ACT_SOFTMAX;
   const float lse = softmax ? ws_lse[grow * H + h] : 0.0f;
   // softmax: D_i = sum_j p_ij dp_ij first
   float Dsum = 0.0f;
@@ -127,7 +129,7 @@ __device__ void bwd_row(const GroupDesc& gd, int64_t grow, int h, const float* w
     for (int c = 0; c < D; ++c) { s = fmaf(qr[c], kj[c], s); dp = fmaf(dor[c], vj[c], dp); }
     s *= gd.scale;
     if (gd.g) s += log_sigmoid_exact(gd.g[(int64_t)(k0 + j) * H + h]);
-    const float ds = softmax ? expf(s - lse) * (dp - Dsum) : dp * act_g(gd.act, s);
+    const float ds = softmax ? expf(s - lse) * (dp - Dsum) : dp * act_g(act, s);
     for (int c = 0; c < D; ++c) dq[c] = fmaf(ds, kj[c], dq[c]);
   }
   float* o = reinterpret_cast<float*>(gd.dq) + (grow * H + h) * D;
@@ -147,7 +149,8 @@ __device__ void bwd_key(const GroupDesc& gd, int64_t gkey, int h, const float* w
   float kr[D], vr[D], dk[D], dv[D];
   for (int c = 0; c < D; ++c) { kr[c] = kj[c]; vr[c] = vj[c]; dk[c] = 0.0f; dv[c] = 0.0f; }
   const float gate = gd.g ? log_sigmoid_exact(gd.g[gkey * H + h]) : 0.0f;
-  const bool softmax = gd.act == GDPA_ACT_SOFTMAX;
+  const int act = gd.head_acts ? gd.head_acts[h] : gd.act;
+  const bool softmax = act == GDPA_ACT_SOFTMAX;
   // queries that see key j: i - wl <= j <= i + wr  <=>  j - wr <= i <= j + wl
   int ilo = 0, ihi = L - 1;
   if (gd.wr >= 0 && j - gd.wr > ilo) ilo = j - gd.wr;
@@ -165,8 +168,8 @@ __device__ void bwd_key(const GroupDesc& gd, int64_t gkey, int h, const float* w
       p = expf(s - ws_lse[grow * H + h]);  // softmax only: ws_lse = forward lse
       ds = p * (dp - ws_delta[grow * H + h]);
     } else {
-      p = act_f(gd.act, s);
-      ds = dp * act_g(gd.act, s);
+      p = act_f(act, s);
+      ds = dp * act_g(act, s);
     }
     dssum += ds;
     for (int c = 0; c < D; ++c) {

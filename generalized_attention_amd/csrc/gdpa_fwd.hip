@@ -436,8 +436,9 @@ __global__ void __launch_bounds__(fwd_waves<DSET>() * kWave, 2) fwd_bf16_kernel(
   int g, h, b;
   unpack_item(d.items[blockIdx.x], g, h, b);
   if (g >= d.n_groups) return;
-  const GroupDesc gd = select_group(d, g);
+  GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
+  if (gd.head_acts != nullptr) gd.act = gd.head_acts[h];  // activation of this item's head
   if constexpr ((DSET & kDim32) != 0)
     if (gd.head_dim == 32) { fwd_dispatch_act<32, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim64) != 0)

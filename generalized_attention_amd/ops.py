@@ -34,6 +34,11 @@ class GroupArgs:
     g: Optional[torch.Tensor] = None  # float32 [total_kv, H]
     self_attention: bool = False
     planned: bool = False  # the workspace holds a gdpa_plan() work list for this shape
+    head_acts: Optional[torch.Tensor] = None  # int32 [H] on the device: activation per head
+
+    @property
+    def may_softmax(self) -> bool:
+        return self.act == "softmax" or self.head_acts is not None
 
     def problem(self) -> _lib.gdpa_problem:
         p = _lib.gdpa_problem()
@@ -52,14 +57,23 @@ class GroupArgs:
         p.flags = _lib.GDPA_FLAG_PLANNED if self.planned else 0
         p.q_offsets = self.q_offsets.data_ptr()
         p.kv_offsets = self.kv_offsets.data_ptr()
+        p.head_acts = 0 if self.head_acts is None else self.head_acts.data_ptr()
         return p
 
 
-def make_group(q, k, v, q_offsets, kv_offsets, *, act: str, scale: float, window=(-1, -1), g=None,
+def make_group(q, k, v, q_offsets, kv_offsets, *, act, scale: float, window=(-1, -1), g=None,
                self_attention: Optional[bool] = None, lengths_q=None, lengths_kv=None) -> GroupArgs:
     """Build GroupArgs from device tensors. Offsets may be given on the host (int64 numpy/torch)
-    or the device; the max lengths come from host lengths when given (no device sync)."""
+    or the device; the max lengths come from host lengths when given (no device sync).
+    act: an activation name, or a sequence with one name per head."""
     dev = q.device
+    head_acts = None
+    if not isinstance(act, str):
+        names = list(act)
+        if len(names) != q.shape[1]:
+            raise ValueError("one activation per head expected")
+        head_acts = torch.tensor([_ACTS[a] for a in names], dtype=torch.int32).to(dev)
+        act = names[0]
 
     def dev_off(o):
         t = torch.as_tensor(o)
@@ -76,7 +90,7 @@ def make_group(q, k, v, q_offsets, kv_offsets, *, act: str, scale: float, window
         self_attention = window != (-1, -1)
     return GroupArgs(q=q, k=k, v=v, q_offsets=qo, kv_offsets=ko, act=act, scale=scale,
                      max_seqlen_q=int(max(lengths_q, default=0)), max_seqlen_kv=int(max(lengths_kv, default=0)),
-                     window=tuple(window), g=g, self_attention=bool(self_attention))
+                     window=tuple(window), g=g, self_attention=bool(self_attention), head_acts=head_acts)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> int:
@@ -111,13 +125,13 @@ def _fwd_tensors(grp: GroupArgs, o, lse) -> _lib.gdpa_tensors:
 def _alloc_fwd(grp: GroupArgs):
     o = torch.empty_like(grp.q)
     lse = None
-    if grp.act == "softmax":
+    if grp.may_softmax:
         lse = torch.empty(grp.q.shape[0], grp.q.shape[1], dtype=torch.float32, device=grp.q.device)
     return o, lse
 
 
 def gdpa_fwd(grp: GroupArgs, o=None, lse=None, ws=None):
-    """Forward. Returns (o, lse); lse is None unless act == 'softmax'."""
+    """Forward. Returns (o, lse); lse is None unless some head uses softmax."""
     if o is None:
         o, lse = _alloc_fwd(grp)
     if ws is None:

@@ -87,6 +87,10 @@ typedef struct gdpa_problem {
   int32_t flags;         /* 0 or GDPA_FLAG_PLANNED (same value in every problem of a call) */
   const int32_t* q_offsets;  /* device [B+1] */
   const int32_t* kv_offsets; /* device [B+1] */
+  /* Optional DEVICE array [num_heads] of gdpa_act: head h uses head_acts[h] instead of act (the
+   * review, section 2.3, lets the activation differ between heads). Trusted like the offsets.
+   * When given, lse must be provided (it is written, and read back, for the softmax heads). */
+  const int32_t* head_acts;
 } gdpa_problem;
 
 /* Device tensors of one problem. Unused entries may be NULL. */

@@ -46,9 +46,9 @@ def load(path: str = LIB_PATH):
     lib.gdpa_oracle_phi_grad.restype = d
     lib.gdpa_oracle_log_sigmoid.argtypes = [d]
     lib.gdpa_oracle_log_sigmoid.restype = d
-    lib.gdpa_oracle_fwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, i]
+    lib.gdpa_oracle_fwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, i, p]
     lib.gdpa_oracle_fwd.restype = i
-    lib.gdpa_oracle_bwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, p, p, p, i]
+    lib.gdpa_oracle_bwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, p, p, p, i, p]
     lib.gdpa_oracle_bwd.restype = i
     if path == LIB_PATH:
         _lib = lib
@@ -63,28 +63,40 @@ def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 
 
-def fwd(q, k, v, q_offsets, kv_offsets, *, act: str, scale: float, g=None,
+def _acts(act, h):
+    """(default code, per-head codes or None) for act = a name or one name per head."""
+    if isinstance(act, str):
+        return ACT_CODES[act], None
+    codes = np.ascontiguousarray([ACT_CODES[a] for a in act], dtype=np.int32)
+    if codes.shape != (h,):
+        raise ValueError("one activation per head expected")
+    return int(codes[0]), codes
+
+
+def fwd(q, k, v, q_offsets, kv_offsets, *, act, scale: float, g=None,
         window=(-1, -1), nthreads: int = 0, lib=None) -> Dict[str, np.ndarray]:
-    """Forward of the plain definition. Arrays: q [Tq,H,d], k/v [Tk,H,d], g [Tk,H] or None."""
+    """Forward of the plain definition. Arrays: q [Tq,H,d], k/v [Tk,H,d], g [Tk,H] or None.
+    act: an activation name, or a list with one name per head."""
     lib = lib or load()
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
     qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
     ko = np.ascontiguousarray(kv_offsets, dtype=np.int64)
     tq, h, d = q.shape
+    code, heads = _acts(act, h)
     o = np.zeros_like(q)
     lse = np.zeros((tq, h), dtype=np.float64)
     rc = lib.gdpa_oracle_fwd(len(qo) - 1, h, d, _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
-                             _ptr(g), ACT_CODES[act], float(scale), int(window[0]),
-                             int(window[1]), _ptr(o), _ptr(lse), int(nthreads))
+                             _ptr(g), code, float(scale), int(window[0]),
+                             int(window[1]), _ptr(o), _ptr(lse), int(nthreads), _ptr(heads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     out = {"o": o}
-    if act == "softmax":
-        out["lse"] = lse
+    if (act == "softmax") if isinstance(act, str) else ("softmax" in act):
+        out["lse"] = lse  # rows of non-softmax heads hold 0
     return out
 
 
-def bwd(q, k, v, dout, q_offsets, kv_offsets, *, act: str, scale: float, g=None,
+def bwd(q, k, v, dout, q_offsets, kv_offsets, *, act, scale: float, g=None,
         window=(-1, -1), want_dg: bool = False, nthreads: int = 0, lib=None) -> Dict[str, np.ndarray]:
     """Gradients of sum(dout * o) with respect to q, k, v (and the gate G if want_dg)."""
     lib = lib or load()
@@ -92,14 +104,15 @@ def bwd(q, k, v, dout, q_offsets, kv_offsets, *, act: str, scale: float, g=None,
     qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
     ko = np.ascontiguousarray(kv_offsets, dtype=np.int64)
     tq, h, d = q.shape
+    code, heads = _acts(act, h)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dg = np.zeros((k.shape[0], h), dtype=np.float64) if (want_dg and g is not None) else None
     rc = lib.gdpa_oracle_bwd(len(qo) - 1, h, d, _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
-                             _ptr(g), ACT_CODES[act], float(scale), int(window[0]),
+                             _ptr(g), code, float(scale), int(window[0]),
                              int(window[1]), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
-                             int(nthreads))
+                             int(nthreads), _ptr(heads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     out = {"dq": dq, "dk": dk, "dv": dv}

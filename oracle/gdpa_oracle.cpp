@@ -81,7 +81,11 @@ struct Problem {
   int act;
   double scale;
   int wl, wr;  // window sides, -1 = unbounded
+  const int* head_acts;  // activation of each head, or NULL: every head uses act
 };
+
+// Activation of head h (heads may each use their own; review section 2.3 lets phi vary by head).
+int act_of(const Problem& p, int h) { return p.head_acts ? p.head_acts[h] : p.act; }
 
 // Allowed key range [lo, hi] of query position i in a sequence with lk keys (empty if hi < lo).
 void allowed_range(const Problem& p, int64_t i, int64_t lk, int64_t* lo, int64_t* hi) {
@@ -114,8 +118,9 @@ double score_row(const Problem& p, int b, int h, int64_t i, int64_t lo, int64_t 
     if (p.g) sij += log_sigmoid(p.g[(k0 + j) * H + h]);
     s[j - lo] = sij;
   }
-  if (p.act != ACT_SOFTMAX) {
-    for (int64_t t = 0; t < n; ++t) pr[t] = phi(p.act, s[t]);
+  const int act = act_of(p, h);
+  if (act != ACT_SOFTMAX) {
+    for (int64_t t = 0; t < n; ++t) pr[t] = phi(act, s[t]);
     return 0.0;
   }
   if (n <= 0) return -std::numeric_limits<double>::infinity();
@@ -168,12 +173,13 @@ void bwd_item(const Problem& p, int b, int h, const double* dout, double* dq, do
     dp.assign(n, 0.0);
     ds.assign(n, 0.0);
     for (int64_t j = lo; j <= hi; ++j) dp[j - lo] = dot(doi, p.v + ((k0 + j) * H + h) * d, d);
-    if (p.act == ACT_SOFTMAX) {
+    const int act = act_of(p, h);
+    if (act == ACT_SOFTMAX) {
       double D = 0.0;
       for (int64_t t = 0; t < n; ++t) D += pr[t] * dp[t];
       for (int64_t t = 0; t < n; ++t) ds[t] = pr[t] * (dp[t] - D);
     } else {
-      for (int64_t t = 0; t < n; ++t) ds[t] = dp[t] * phi_grad(p.act, s[t]);
+      for (int64_t t = 0; t < n; ++t) ds[t] = dp[t] * phi_grad(act, s[t]);
     }
     double* dqi = dq + ((q0 + i) * H + h) * d;
     for (int c = 0; c < d; ++c) dqi[c] = 0.0;
@@ -195,6 +201,9 @@ void bwd_item(const Problem& p, int b, int h, const double* dout, double* dq, do
 bool valid(const Problem& p) {
   if (p.B < 0 || p.H <= 0 || p.d <= 0) return false;
   if (p.act < ACT_GELU || p.act > ACT_SOFTMAX) return false;
+  if (p.head_acts)
+    for (int h = 0; h < p.H; ++h)
+      if (p.head_acts[h] < ACT_GELU || p.head_acts[h] > ACT_SOFTMAX) return false;
   if (p.wl < -1 || p.wr < -1) return false;
   if (!p.q_off || !p.kv_off) return false;
   if (p.q_off[0] != 0 || p.kv_off[0] != 0) return false;
@@ -228,13 +237,14 @@ double gdpa_oracle_phi(int act, double x) { return phi(act, x); }
 double gdpa_oracle_phi_grad(int act, double x) { return phi_grad(act, x); }
 double gdpa_oracle_log_sigmoid(double x) { return log_sigmoid(x); }
 
-// Forward. g may be NULL (no gate). lse may be NULL; it is written for the softmax form.
+// Forward. g may be NULL (no gate). lse may be NULL; it is written for the softmax heads.
+// head_acts may be NULL (every head uses act) or hold one activation per head.
 // Returns 0, or -1 for invalid arguments (nothing written). nthreads <= 0 means all cores.
 int gdpa_oracle_fwd(int B, int H, int d, const int64_t* q_off, const int64_t* kv_off,
                     const double* q, const double* k, const double* v, const double* g, int act,
                     double scale, int window_left, int window_right, double* o, double* lse,
-                    int nthreads) {
-  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right};
+                    int nthreads, const int* head_acts) {
+  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right, head_acts};
   if (!valid(p)) return -1;
   if (p.q_off[B] > 0 && (!q || !o)) return -1;
   if (p.kv_off[B] > 0 && (!k || !v)) return -1;
@@ -246,8 +256,9 @@ int gdpa_oracle_fwd(int B, int H, int d, const int64_t* q_off, const int64_t* kv
 int gdpa_oracle_bwd(int B, int H, int d, const int64_t* q_off, const int64_t* kv_off,
                     const double* q, const double* k, const double* v, const double* g, int act,
                     double scale, int window_left, int window_right, const double* dout,
-                    double* dq, double* dk, double* dv, double* dg, int nthreads) {
-  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right};
+                    double* dq, double* dk, double* dv, double* dg, int nthreads,
+                    const int* head_acts) {
+  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right, head_acts};
   if (!valid(p)) return -1;
   if (dg && !g) return -1;
   if (p.q_off[B] > 0 && (!q || !dout || !dq)) return -1;

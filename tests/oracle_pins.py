@@ -66,7 +66,7 @@ def torch_reference(pb, act, scale, window=(-1, -1), need_grad=False):
 
     Element-wise form: act(scale * Q_h K_h^T) V_h with masked entries dropped (the PFFN product
     with W1 = K_h^T, W2 = V_h). Softmax form: scaled_dot_product_attention with an additive
-    float mask log sigmoid(G) (and -inf outside the window)."""
+    float mask log sigmoid(G) (and -inf outside the window). act may list one form per head."""
     tq, h, d = pb["q"].shape
     q = torch.tensor(pb["q"], requires_grad=need_grad)
     k = torch.tensor(pb["k"], requires_grad=need_grad)
@@ -82,7 +82,8 @@ def torch_reference(pb, act, scale, window=(-1, -1), need_grad=False):
             Q = q[q0:q1, hh]
             K = k[k0:k1, hh]
             V = v[k0:k1, hh]
-            if act == "softmax":
+            act_h = act if isinstance(act, str) else act[hh]
+            if act_h == "softmax":
                 bias = torch.zeros(q1 - q0, k1 - k0, dtype=torch.float64)
                 if g is not None:
                     bias = bias + F.logsigmoid(g[k0:k1, hh])[None, :]
@@ -97,7 +98,7 @@ def torch_reference(pb, act, scale, window=(-1, -1), need_grad=False):
                 S = scale * (Q @ K.T)
                 if g is not None:
                     S = S + F.logsigmoid(g[k0:k1, hh])[None, :]
-                fn = F.gelu if act == "gelu" else F.silu
+                fn = F.gelu if act_h == "gelu" else F.silu
                 P = torch.where(m, fn(S), torch.zeros((), dtype=torch.float64))
                 heads.append(P @ V)
         outs[b] = torch.stack(heads, dim=1) if heads else torch.zeros(q1 - q0, 0, d)
@@ -142,7 +143,7 @@ def check_worked_examples(orc):
 def check_forward_vs_library(orc, act, scale, window=(-1, -1), gate=False, seed=0, self_attn=False):
     lq = [5, 0, 1, 9, 3]
     lk = None if self_attn else [7, 4, 0, 6, 2]
-    pb = rand_problem(seed, lq, lk, gate=gate)
+    pb = rand_problem(seed, lq, lk, gate=gate, h=2 if isinstance(act, str) else len(act))
     r = orc.fwd(pb["q"], pb["k"], pb["v"], pb["qo"], pb["ko"], act=act, scale=scale, g=pb["g"],
                 window=window)
     ref = torch_reference(pb, act, scale, window)
@@ -152,7 +153,7 @@ def check_forward_vs_library(orc, act, scale, window=(-1, -1), gate=False, seed=
 def check_backward_vs_autograd(orc, act, scale, window=(-1, -1), gate=False, seed=1, self_attn=False):
     lq = [4, 0, 6, 1]
     lk = None if self_attn else [5, 3, 0, 2]
-    pb = rand_problem(seed, lq, lk, gate=gate)
+    pb = rand_problem(seed, lq, lk, gate=gate, h=2 if isinstance(act, str) else len(act))
     r = orc.bwd(pb["q"], pb["k"], pb["v"], pb["do"], pb["qo"], pb["ko"], act=act, scale=scale,
                 g=pb["g"], window=window, want_dg=gate)
     ref = torch_reference(pb, act, scale, window, need_grad=True)
@@ -310,6 +311,8 @@ FAST_CHECKS = [
     ("bwd silu", lambda o: check_backward_vs_autograd(o, "silu", 0.8)),
     ("bwd softmax gated window", lambda o: check_backward_vs_autograd(o, "softmax", 0.6, (2, 0), True, self_attn=True)),
     ("bwd silu gated window", lambda o: check_backward_vs_autograd(o, "silu", 0.6, (1, 1), True, self_attn=True)),
+    ("fwd per-head acts", lambda o: check_forward_vs_library(o, ["gelu", "softmax", "silu"], 0.7, (3, 1), True, self_attn=True)),
+    ("bwd per-head acts", lambda o: check_backward_vs_autograd(o, ["softmax", "silu", "gelu"], 0.7, gate=True)),
     ("PFFN identity gelu", lambda o: check_pffn_identity(o, "gelu")),
     ("PFFN identity silu", lambda o: check_pffn_identity(o, "silu")),
     ("rows sum to one", lambda o: check_softmax_rows_sum_to_one(o)),

@@ -147,6 +147,14 @@ def test_forward_specific_checks(lib):
     assert _lib.gdpa_bwd(sm, good_tensors(lse=0), FAKE * 16, 1 << 20, 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
 
 
+def test_per_head_activation_needs_lse(lib):
+    # with an activation per head, some heads may be softmax: lse is required in both passes
+    p = good_problem()
+    p.head_acts = FAKE
+    assert _lib.gdpa_fwd(p, good_tensors(), FAKE * 16, 1 << 20, 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
+    assert _lib.gdpa_bwd(p, good_tensors(lse=0), FAKE * 16, 1 << 20, 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
+
+
 def test_workspace_checks(lib):
     for fn in (_lib.gdpa_fwd, _lib.gdpa_bwd):
         assert fn(good_problem(), good_tensors(), 0, 1 << 20, 0) == _lib.GDPA_ERR_WORKSPACE

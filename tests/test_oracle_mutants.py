@@ -36,6 +36,7 @@ MUTANTS = [
     ("head index swapped", "double sij = p.scale * dot(qi, kj, d);",
      "double sij = p.scale * dot(qi, p.k + ((k0 + j) * H + (H - 1 - h)) * d, d);"),
     ("dg missing sigmoid", "+= sigmoid(-p.g[(k0 + j) * H + h]) * dsij", "+= dsij"),
+    ("per-head activation ignored", "return p.head_acts ? p.head_acts[h] : p.act;", "return p.act;"),
     ("v transposed", "oi[c] += pr[j - lo] * vj[c];", "oi[c] += pr[j - lo] * p.v[((k0 + c % (hi - lo + 1)) * H + h) * d + (j % d)];"),
 ]
 

@@ -74,11 +74,14 @@ def compare_workload(w, passes, sample=None, want_dg=True, scale=None):
         ref = oracle.group_fwd(sub)
         o, lse = fwd_outs[gi]
         report[f"g{gi}.o"] = chk(dt, to64(o)[qr], ref["o"], f"{w.name} g{gi} O")
-        if g.spec.act == "softmax":
-            lg = to64(lse)[qr]
-            fin = np.isfinite(ref["lse"])
+        acts = [g.spec.act] * g.spec.num_heads if isinstance(g.spec.act, str) else list(g.spec.act)
+        sm = [h for h, a in enumerate(acts) if a == "softmax"]  # heads whose lse is defined
+        if sm:
+            lg = to64(lse)[qr][:, sm]
+            lr = ref["lse"][:, sm]
+            fin = np.isfinite(lr)
             assert np.array_equal(fin, np.isfinite(lg))
-            assert np.max(np.abs(lg[fin] - ref["lse"][fin]), initial=0.0) < 2e-3 * max(1.0, np.abs(ref["lse"][fin]).max(initial=1.0))
+            assert np.max(np.abs(lg[fin] - lr[fin]), initial=0.0) < 2e-3 * max(1.0, np.abs(lr[fin]).max(initial=1.0))
         if bwd_outs is not None:
             rb = oracle.group_bwd(sub, want_dg=want_dg and g.g is not None)
             gb = bwd_outs[gi]
@@ -241,3 +244,24 @@ def test_sample_independence():
     r1 = slice(int(g.q_offsets[1]), int(g.q_offsets[2]))
     assert torch.equal(o1[r0], o2[r0])
     assert not torch.equal(o1[r1], o2[r1])
+
+
+# ------------------------------------------------------------------------------------------------
+# Activation per head (one launch; heads of one problem use different forms)
+# ------------------------------------------------------------------------------------------------
+
+def test_per_head_activation_causal_gated():
+    acts = ("softmax", "gelu", "silu", "softmax", "gelu", "silu", "softmax", "silu")
+    w = make_workload("causal_gated", 8, num_seqs=4, len_range=(1, 500), act=acts)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+def test_per_head_activation_pffn():
+    acts = ("silu", "gelu", "softmax", "silu")
+    w = make_workload("pffn_train", 9, num_seqs=6, len_range=(1, 300), act=acts, scale=0.125)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+def test_per_head_activation_fp32():
+    w = make_workload("tiny_fp32", 3, act=("softmax", "gelu"))
+    compare_workload(w, ("fwd", "bwd"))
