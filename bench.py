@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hpp", "gdpa_bwd.hip", "gdpa_bwd_sm128.hip",
+KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hpp", "gdpa_bwd.hip", "gdpa_bwd_agpr.hip",
                   "gdpa_sched.hip", "gdpa_api.cpp", "gdpa_launch.hpp"]
 
 WORKLOAD_TEXT = {
@@ -37,6 +37,9 @@ WORKLOAD_TEXT = {
             "scale 1/8, log-sigmoid gate, causal window 128",
     "grouped10": "10 event groups in one launch, bf16 forward+backward: B=64 each, L~U[100,1000], n=32, "
             "groups 0-4 H=8 d=128, groups 5-9 H=2 d=32, GELU",
+    "seed_pool": "seed-query pooling (PMA / hierarchical seed pooling form) bf16 forward+backward: S=256 "
+            "learnable seed queries shared by B=256 sequences of L~U[100,1000] keys, H=4, d=64, softmax, "
+            "scale 1/8, dQ summed over the sequences",
 }
 
 
@@ -128,7 +131,8 @@ def main():
         s = g.spec
         groups.append(ga.make_group(g.q.to(dev), g.k.to(dev), g.v.to(dev), g.q_offsets, g.kv_offsets, act=s.act,
                                     scale=s.scale, window=s.window, g=None if g.g is None else g.g.to(dev),
-                                    self_attention=s.keys_per_seq is None, lengths_q=g.lengths_q.tolist(),
+                                    self_attention=s.keys_per_seq is None and not s.shared_q, shared_q=s.shared_q,
+                                    lengths_q=g.lengths_q.tolist(),
                                     lengths_kv=g.lengths_kv.tolist()))
     douts = [g.dout.to(dev) for g in w.groups]
     ws = ga.workspace(groups, 1 if "bwd" in passes else 0)

@@ -35,14 +35,15 @@ def group_work(group) -> Dict[str, float]:
     e *= h
     esize = 2 if s.dtype == "bf16" else 4
     tq, tk = group.total_q, group.total_kv
+    qrows = int(group.q.shape[0])  # = tq, or S rows of a shared query matrix
     softmax = s.act == "softmax"
     gate_b = 4 * tk * h if s.gate else 0
     lse_b = 4 * tq * h if softmax else 0
     # forward: read Q, K, V (+G); write O (+LSE)
-    fwd_bytes = esize * (2 * tq * h * d + 2 * tk * h * d) + gate_b + lse_b
+    fwd_bytes = esize * ((qrows + tq) * h * d + 2 * tk * h * d) + gate_b + lse_b
     # backward: read Q, K, V, dO (+G; softmax also LSE); write dQ, dK, dV (+dG). The softmax row
     # term D_i = sum_j p_ij dp_ij is formed from P and dP in the kernel, so O is not read.
-    bwd_bytes = esize * (3 * tq * h * d + 4 * tk * h * d) + 2 * gate_b + lse_b
+    bwd_bytes = esize * ((2 * qrows + tq) * h * d + 4 * tk * h * d) + 2 * gate_b + lse_b
     return {
         "entries": float(e),
         "fwd_flops": 4.0 * d * e,

@@ -1,4 +1,4 @@
-"""Seeded input recipe for the five GDPA workloads and their reduced parity variants.
+"""Seeded input recipe for the six GDPA workloads and their reduced parity variants.
 
 Draw order is part of the recipe: ``numpy.random.default_rng(seed)`` (PCG64), lengths first,
 then the tensors in the order each builder lists them. Normal draws are made in float64 (the
@@ -33,6 +33,7 @@ class GroupSpec:
     window: Tuple[int, int] = (-1, -1)  # (left, right); -1 = unbounded side
     gate: bool = False       # per-head, per-key gate G of the gated-softmax form
     dtype: str = "bf16"      # "bf16" | "fp32"
+    shared_q: bool = False   # one [S, H, d] query matrix shared by every sequence (seed pooling)
 
 
 @dataclasses.dataclass
@@ -44,7 +45,7 @@ class Group:
     lengths_kv: np.ndarray   # int64 [B]
     q_offsets: np.ndarray    # int64 [B+1]
     kv_offsets: np.ndarray   # int64 [B+1]
-    q: torch.Tensor          # [total_q, H, d]
+    q: torch.Tensor          # [total_q, H, d] (shared_q: [S, H, d])
     k: torch.Tensor          # [total_kv, H, d]
     v: torch.Tensor          # [total_kv, H, d]
     g: Optional[torch.Tensor]  # float32 [total_kv, H] or None
@@ -78,7 +79,7 @@ class Group:
             lengths_kv=lk.astype(np.int64),
             q_offsets=_offsets(lq),
             kv_offsets=_offsets(lk),
-            q=self.q.index_select(0, qit),
+            q=self.q if self.spec.shared_q else self.q.index_select(0, qit),
             k=self.k.index_select(0, kit),
             v=self.v.index_select(0, kit),
             g=None if self.g is None else self.g.index_select(0, kit),
@@ -137,6 +138,9 @@ CONFIGS: Dict[str, str] = {
             "scale 1/sqrt(d), log sigmoid gate G~N(0,1), causal sliding window 128",
     "grouped10": "10 event groups in one launch, bf16 fwd+bwd: each B=64, L in [100,1000], n=32; "
             "groups 0-4 H=8 d=128, groups 5-9 H=2 d=32; GELU",
+    "seed_pool": "seed-query pooling (PMA / hierarchical seed pooling as GDPA) bf16 fwd+bwd: S=256 "
+            "learnable seed queries shared by B=256 sequences, L in [100,1000] keys each, H=4, d=64, "
+            "softmax, scale 1/sqrt(d); dQ summed over the sequences",
 }
 
 
@@ -190,16 +194,33 @@ def _self_attention(rng, spec: GroupSpec, lengths: np.ndarray) -> Group:
                  _cast(do, spec.dtype))
 
 
+def _seed_pool(rng, spec: GroupSpec, lengths: np.ndarray, seeds: int) -> Group:
+    """Shared seed queries over jagged sequences. Draw order: seed queries E [S,H,d] ~ N(0,1);
+    sequence keys and values K, V [T,H,d] ~ N(0,1); dO [B*S,H,d] ~ N(0,1). Every sequence has
+    S query rows (its pooled outputs) and L_b keys."""
+    b, h, d = spec.num_seqs, spec.num_heads, spec.head_dim
+    t = int(lengths.sum())
+    q = rng.standard_normal((seeds, h, d))
+    k = rng.standard_normal((t, h, d))
+    v = rng.standard_normal((t, h, d))
+    do = rng.standard_normal((b * seeds, h, d))
+    lq = np.full(b, seeds, dtype=np.int64)
+    return Group(spec, lq, lengths, _offsets(lq), _offsets(lengths), _cast(q, spec.dtype),
+                 _cast(k, spec.dtype), _cast(v, spec.dtype), None, _cast(do, spec.dtype))
+
+
 def make_workload(name: str, seed: int = 0, *, num_seqs: Optional[int] = None,
                   len_range: Optional[Tuple[int, int]] = None, scale: Optional[float] = None,
                   act: Optional[str] = None, ctx_dim: int = 512,
                   window: Optional[Tuple[int, int]] = None,
-                  lengths: Optional[List[int]] = None) -> Workload:
+                  lengths: Optional[List[int]] = None, keys: Optional[int] = None,
+                  seeds: Optional[int] = None) -> Workload:
     """Build a workload by config name.
 
     The keyword overrides shrink a config for parity tests (fewer sequences, shorter lengths)
     or change the score scale / activation / window while keeping the recipe's draw order.
-    ``lengths`` replaces the length draw entirely (edge cases: zeros, ones, tile +- 1)."""
+    ``lengths`` replaces the length draw entirely (edge cases: zeros, ones, tile +- 1); ``keys``
+    replaces the PFFN key count n and ``seeds`` the seed-query count S."""
     rng = np.random.default_rng(seed)
 
     def lens(b, lr):
@@ -216,7 +237,7 @@ def make_workload(name: str, seed: int = 0, *, num_seqs: Optional[int] = None,
         return Workload(name, CONFIGS[name], [grp], ("fwd",), seed)
     if name in ("pffn_fwd", "pffn_train"):
         b = num_seqs or 256
-        spec = GroupSpec(name, b, 4, 64, len_range or (100, 1000), 256, act or "silu",
+        spec = GroupSpec(name, b, 4, 64, len_range or (100, 1000), keys or 256, act or "silu",
                          1.0 / 1000 if scale is None else scale)
         L = lens(b, spec.len_range)
         grp = _pffn_context(rng, dataclasses.replace(spec, num_seqs=len(L)), L, ctx_dim)
@@ -244,4 +265,11 @@ def make_workload(name: str, seed: int = 0, *, num_seqs: Optional[int] = None,
                              1.0 / 1000 if scale is None else scale)
             groups.append(_pffn_plain(rng, spec, all_l[e], 1.0))
         return Workload(name, CONFIGS[name], groups, ("fwd", "bwd"), seed)
+    if name == "seed_pool":
+        b = num_seqs or 256
+        spec = GroupSpec("seed_pool", b, 4, 64, len_range or (100, 1000), None, act or "softmax",
+                         1.0 / 8 if scale is None else scale, shared_q=True)
+        L = lens(b, spec.len_range)
+        grp = _seed_pool(rng, dataclasses.replace(spec, num_seqs=len(L)), L, seeds or 256)
+        return Workload(name, CONFIGS[name], [grp], ("fwd", "bwd"), seed)
     raise KeyError(f"unknown workload {name!r}; known: {sorted(CONFIGS)}")

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgdpa.so")
 
-SOURCES = ["gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_bwd_sm128.hip", "gdpa_fp32.hip"]
+SOURCES = ["gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_bwd_agpr.hip", "gdpa_fp32.hip"]
 # Per-source options. The backward kernels keep MFMA results in the VGPR form (no register-class
 # copies between the score accumulators and the element-wise code); one kernel variant that this
 # compiler cannot build that way lives in its own source.

@@ -17,10 +17,13 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t items = 0, keys = 0, delta = 0, total = 0;
-  int64_t n_items = 0, n_seqs = 0, delta_rows = 0;
+  size_t items = 0, keys = 0, delta = 0, dq32 = 0, total = 0;
+  int64_t n_items = 0, n_seqs = 0, delta_rows = 0, dq32_floats = 0;
   int64_t delta_base[GDPA_MAX_GROUPS] = {};
+  int64_t dq32_base[GDPA_MAX_GROUPS] = {};
 };
+
+bool shared_q(const gdpa_problem& p) { return (p.flags & GDPA_FLAG_SHARED_Q) != 0; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -32,7 +35,9 @@ int check_problem(const gdpa_problem& p) {
   if (p.act < GDPA_ACT_GELU || p.act > GDPA_ACT_SOFTMAX) return GDPA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p.scale)) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.window_left < -1 || p.window_right < -1) return GDPA_ERR_INVALID_ARGUMENT;
-  if ((p.flags & ~GDPA_FLAG_PLANNED) != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((p.flags & ~(GDPA_FLAG_PLANNED | GDPA_FLAG_SHARED_Q)) != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if (shared_q(p) && p.self_attention) return GDPA_ERR_INVALID_ARGUMENT;
+  if (shared_q(p) && p.dtype != GDPA_DTYPE_BF16) return GDPA_ERR_UNSUPPORTED;
   if (p.self_attention != 0 && p.self_attention != 1) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.total_q < 0 || p.total_kv < 0 || p.max_seqlen_q < 0 || p.max_seqlen_kv < 0)
     return GDPA_ERR_INVALID_ARGUMENT;
@@ -43,17 +48,17 @@ int check_problem(const gdpa_problem& p) {
     return GDPA_ERR_INVALID_ARGUMENT;
   if (p.num_seqs > 0 && (!p.q_offsets || !p.kv_offsets)) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.num_seqs == 0 && (p.total_q != 0 || p.total_kv != 0)) return GDPA_ERR_INVALID_ARGUMENT;
-  if ((int64_t)p.max_seqlen_q > p.total_q || (int64_t)p.max_seqlen_kv > p.total_kv)
+  // (a shared query matrix has max_seqlen_q rows of its own, whatever the sequences use)
+  if ((!shared_q(p) && (int64_t)p.max_seqlen_q > p.total_q) || (int64_t)p.max_seqlen_kv > p.total_kv)
     return GDPA_ERR_INVALID_ARGUMENT;
-  if (p.dtype == GDPA_DTYPE_BF16 &&
-      !fwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv))
-    return GDPA_ERR_UNSUPPORTED;
   return GDPA_OK;
 }
 
-int check_backward_capacity(const gdpa_problem& p) {
-  if (p.dtype != GDPA_DTYPE_BF16) return GDPA_OK;
-  return bwd_shape_ok(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv) ? GDPA_OK : GDPA_ERR_UNSUPPORTED;
+// bf16 backward in key chunks (long key ranges, or a shared query matrix): fp32 dQ rows and, for
+// softmax, the row term D_i live in the workspace.
+bool bwd_chunked(const gdpa_problem& p) {
+  return p.dtype == GDPA_DTYPE_BF16 &&
+         (shared_q(p) || bwd_may_chunk(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv));
 }
 
 // The problem may contain softmax heads (its own act, or any head when the activation is per head).
@@ -61,7 +66,8 @@ bool may_softmax(const gdpa_problem& p) { return p.act == GDPA_ACT_SOFTMAX || p.
 
 int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
   const bool rows = p.total_q > 0, keys = p.total_kv > 0;
-  if (rows && (!t.q || !aligned16(t.q))) return GDPA_ERR_INVALID_ARGUMENT;
+  const bool qrows = shared_q(p) ? p.max_seqlen_q > 0 : rows;  // rows of q and dq
+  if (qrows && (!t.q || !aligned16(t.q))) return GDPA_ERR_INVALID_ARGUMENT;
   if (keys && (!t.k || !t.v || !aligned16(t.k) || !aligned16(t.v))) return GDPA_ERR_INVALID_ARGUMENT;
   if (t.dg && !t.g) return GDPA_ERR_INVALID_ARGUMENT;
   if ((t.g && !aligned16(t.g)) || (t.lse && ((uintptr_t)t.lse & 3u))) return GDPA_ERR_INVALID_ARGUMENT;
@@ -70,7 +76,8 @@ int check_tensors(const gdpa_problem& p, const gdpa_tensors& t, int pass) {
     if (rows && may_softmax(p) && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
     if (t.dg) return GDPA_ERR_INVALID_ARGUMENT;
   } else {
-    if (rows && (!t.dout || !t.dq || !aligned16(t.dout) || !aligned16(t.dq))) return GDPA_ERR_INVALID_ARGUMENT;
+    if (rows && (!t.dout || !aligned16(t.dout))) return GDPA_ERR_INVALID_ARGUMENT;
+    if (qrows && (!t.dq || !aligned16(t.dq))) return GDPA_ERR_INVALID_ARGUMENT;
     if (keys && (!t.dk || !t.dv || !aligned16(t.dk) || !aligned16(t.dv))) return GDPA_ERR_INVALID_ARGUMENT;
     if (rows && may_softmax(p) && !t.lse) return GDPA_ERR_INVALID_ARGUMENT;
   }
@@ -83,20 +90,26 @@ int layout(const gdpa_problem* ps, int n_groups, int pass, WsLayout* L) {
   for (int g = 0; g < n_groups; ++g) {
     int rc = check_problem(ps[g]);
     if (rc != GDPA_OK) return rc;
-    if (pass == 1 && (rc = check_backward_capacity(ps[g])) != GDPA_OK) return rc;
-    if (ps[g].dtype != ps[0].dtype || ps[g].flags != ps[0].flags) return GDPA_ERR_INVALID_ARGUMENT;
+    if (ps[g].dtype != ps[0].dtype || (ps[g].flags & GDPA_FLAG_PLANNED) != (ps[0].flags & GDPA_FLAG_PLANNED))
+      return GDPA_ERR_INVALID_ARGUMENT;
     L->n_items += (int64_t)ps[g].num_seqs * ps[g].num_heads;
     L->n_seqs += ps[g].num_seqs;
     L->delta_base[g] = L->delta_rows;
-    // fp32 softmax backward: per-row D_i between its two kernels
-    if (pass == 1 && may_softmax(ps[g]) && ps[g].dtype == GDPA_DTYPE_FP32)
+    // softmax backward: per-row D_i (fp32: between its two kernels; bf16: across key chunks)
+    if (pass == 1 && may_softmax(ps[g]) && (ps[g].dtype == GDPA_DTYPE_FP32 || bwd_chunked(ps[g])))
       L->delta_rows += ps[g].total_q * ps[g].num_heads;
+    L->dq32_base[g] = L->dq32_floats;
+    if (pass == 1 && bwd_chunked(ps[g])) {
+      const int64_t rows = shared_q(ps[g]) ? (int64_t)ps[g].num_seqs * ps[g].max_seqlen_q : ps[g].total_q;
+      L->dq32_floats += rows * ps[g].num_heads * ps[g].head_dim;
+    }
   }
   if (L->n_items >= ((int64_t)1 << 31) || L->n_seqs >= ((int64_t)1 << 31)) return GDPA_ERR_UNSUPPORTED;
   L->items = 0;
   L->keys = align_up((size_t)L->n_items * 4);
   L->delta = L->keys + align_up((size_t)L->n_seqs * 4);
-  L->total = L->delta + align_up((size_t)L->delta_rows * 4);
+  L->dq32 = L->delta + align_up((size_t)L->delta_rows * 4);
+  L->total = L->dq32 + align_up((size_t)L->dq32_floats * 4);
   if (L->total == 0) L->total = kAlign;
   return GDPA_OK;
 }
@@ -125,6 +138,8 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
     gd.q = t.q; gd.k = t.k; gd.v = t.v; gd.g = t.g; gd.o = t.o; gd.lse = t.lse;
     gd.dout = t.dout; gd.dq = t.dq; gd.dk = t.dk; gd.dv = t.dv; gd.dg = t.dg;
     gd.delta = reinterpret_cast<float*>(base + L.delta) + L.delta_base[g];
+    gd.dq32 = reinterpret_cast<float*>(base + L.dq32) + L.dq32_base[g];
+    gd.shared_q = shared_q(p) ? p.max_seqlen_q : 0;
     gd.q_off = p.q_offsets;
     gd.kv_off = p.kv_offsets;
     gd.num_seqs = p.num_seqs;
@@ -164,7 +179,9 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
   for (int g = 0; g < n_groups; ++g)
     if ((rc = check_tensors(ps[g], ts[g], pass)) != GDPA_OK) return rc;
   if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < L.total) return GDPA_ERR_WORKSPACE;
-  if (L.n_items == 0) return GDPA_OK;  // nothing to compute
+  bool shared_rows = false;  // a shared query matrix still gets its (zero) dq rows
+  for (int g = 0; g < n_groups; ++g) shared_rows |= pass == 1 && shared_q(ps[g]) && ps[g].max_seqlen_q > 0;
+  if (L.n_items == 0 && !shared_rows) return GDPA_OK;  // nothing to compute
 
   LaunchDesc d;
   fill_desc(ps, ts, n_groups, ws, L, &d);
@@ -190,6 +207,8 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
                                 : 1 << ps[g].act;
       e = pass == 0 ? launch_fwd_bf16(d, dims, acts, s) : launch_bwd_bf16(d, dims, acts, s);
     }
+    for (int g = 0; g < n_groups && e == hipSuccess; ++g)
+      if (pass == 1 && shared_q(ps[g])) e = launch_reduce_shared_dq(d.grp[g], s);
   }
   return e == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
 }

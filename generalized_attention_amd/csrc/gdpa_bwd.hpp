@@ -169,11 +169,13 @@ struct QTileRegs {
   u32x4 q[BwdGeo<D>::NPF];
   u32x4 d[BwdGeo<D>::NPF];
   float lse;
+  float dsum;  // key-chunked softmax: the row term D_i from the workspace
 };
 
-template <int D, bool SOFTMAX>
+// DSUM: also load the row term D_i (key-chunked softmax main pass).
+template <int D, bool SOFTMAX, bool DSUM = false>
 __device__ void prefetch_qtile(QTileRegs<D>& pf, const bf16* qseq, const bf16* doseq, const float* lseseq,
-                               size_t rs, int H, int r0, int L) {
+                               size_t rs, int H, int r0, int L, const float* dsumseq = nullptr) {
   using G = BwdGeo<D>;
 #pragma unroll
   for (int i = 0; i < G::NPF; ++i) {
@@ -191,10 +193,11 @@ __device__ void prefetch_qtile(QTileRegs<D>& pf, const bf16* qseq, const bf16* d
   if constexpr (SOFTMAX) {
     const int row = r0 + (int)threadIdx.x;
     pf.lse = (threadIdx.x < G::QT && row < L) ? lseseq[(size_t)row * H] * kLog2e : __builtin_inff();
+    if constexpr (DSUM) pf.dsum = (threadIdx.x < G::QT && row < L) ? dsumseq[(size_t)row * H] : 0.0f;
   }
 }
 
-template <int D, bool SOFTMAX>
+template <int D, bool SOFTMAX, bool DSUM = false>
 __device__ void store_qtile(char* lds, const QTileRegs<D>& pf) {
   using G = BwdGeo<D>;
 #pragma unroll
@@ -207,7 +210,10 @@ __device__ void store_qtile(char* lds, const QTileRegs<D>& pf) {
     }
   }
   if constexpr (SOFTMAX)
-    if (threadIdx.x < G::QT) reinterpret_cast<float*>(lds + G::OFF_ROW)[threadIdx.x] = pf.lse;
+    if (threadIdx.x < G::QT) {
+      reinterpret_cast<float*>(lds + G::OFF_ROW)[threadIdx.x] = pf.lse;
+      if constexpr (DSUM) reinterpret_cast<float*>(lds + G::OFF_DPART)[threadIdx.x] = pf.dsum;
+    }
 }
 
 // A operand (M = d, K = query) of a 32x32x16 product, read from a row-major [query][d] LDS tile
@@ -267,16 +273,35 @@ struct BwdItem {
   bf16* dkseq;
   bf16* dvseq;
   float* dgseq;
+  float* dq32seq;      // key chunks: fp32 dQ rows of this item (row stride rs)
+  float* dsumseq;      // key chunks, softmax: D_i of this item's rows (row stride H)
   size_t rs;
   int H, L, n, wl, wr;
+  int kofs;            // sequence position of the item's first key (key chunk start)
+  int ntot;            // keys of the whole sequence
+  int t0, t1;          // query tiles [t0, t1) swept
+  bool shared_q;       // dQ rows are per-sequence partials of a shared query matrix
 };
+
+// Key chunks of kchunk keys: which chunks a query row's keys fall in (first, last), under the
+// window; a row sees no key when first > last.
+__device__ inline void row_chunks(int row, int ntot, int wl, int wr, int kchunk, int& first, int& last) {
+  const int lo = (wl >= 0 && row - wl > 0) ? row - wl : 0;
+  const int hi = (wr >= 0 && row + wr < ntot - 1) ? row + wr : ntot - 1;
+  first = lo / kchunk;
+  last = hi >= lo ? hi / kchunk : first - 1;
+}
 
 // The sweep over the query tiles of one item. KACT: owned blocks processed per wave (KB, or 1
 // when every key of the item fits in one block per wave). The per-block work runs without
 // branches around the MFMA accumulations (a skipped block contributes zero operands), which keeps
 // the dK / dV accumulators in place in the register file; only the element-wise work is skipped.
 // GATED: the problem has a gate G (then dG may also be requested).
-template <int D, int ACT, bool GATED, int KACT, bool WINDOWED>
+// WINDOWED: bounded window whose keys stream through the ring slots as the tiles advance.
+// CHUNK: 0 = the item's keys are all resident; 1 = one chunk of CAP keys starting at it.kofs, dQ
+// accumulated over the chunks in fp32 workspace rows (softmax: D_i read from the workspace);
+// 2 = softmax row-term pass over one chunk: only D_i, accumulated into the workspace.
+template <int D, int ACT, bool GATED, int KACT, bool WINDOWED, int CHUNK = 0>
 __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const BwdItem& it) {
   using G = BwdGeo<D>;
   constexpr int NS = G::NW * KACT;  // ring slots in use
@@ -284,11 +309,16 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   const size_t rs = it.rs;
   const int w = wave_id(), lane = lane_id(), lc = lane & 31, g = lane >> 5;
   constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
-  // entries need explicit masks in the softmax form or inside a window; without a window every
-  // block is resident for the whole sweep (taken once, before it)
-  constexpr bool MASKED = softmax || WINDOWED;
+  static_assert(CHUNK != 2 || softmax, "row-term pass is softmax only");
+  static_assert(CHUNK == 0 || (!WINDOWED && KACT == G::KB), "key chunks hold every block");
+  // entries need explicit masks in the softmax form, inside a window or in a key chunk; without
+  // a window every block is resident for the whole sweep (taken once, before it)
+  constexpr bool MASKED = softmax || WINDOWED || CHUNK != 0;
+  constexpr bool DSUM = CHUNK == 1 && softmax;  // D_i comes from the workspace
+  // keys are chunk-local below; masks compare sequence positions kofs + key with the rows
+  const int kofs = CHUNK ? it.kofs : 0;
   const int nkb = (n + kBwdKeyBlock - 1) / kBwdKeyBlock;
-  const int ntiles = (L + G::QT - 1) / G::QT;
+  const int t0 = it.t0, t1 = it.t1;
 
   BwdWave<D> st;
 #pragma unroll
@@ -327,10 +357,11 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   for (int idx = threadIdx.x; idx < D * (G::KTROW / 16); idx += G::THREADS)
     reinterpret_cast<u32x4*>(lds + G::OFF_KT)[idx] = u32x4{0u, 0u, 0u, 0u};
   QTileRegs<D> pf;
-  prefetch_qtile<D, softmax>(pf, it.qseq, it.doseq, it.lseseq, rs, H, 0, L);
+  prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, t0 * G::QT, L, it.dsumseq);
   __syncthreads();  // K^T staging zeroed
-  store_qtile<D, softmax>(lds, pf);  // tile 0
-  if (ntiles > 1) prefetch_qtile<D, softmax>(pf, it.qseq, it.doseq, it.lseseq, rs, H, G::QT, L);
+  store_qtile<D, softmax, DSUM>(lds, pf);  // first tile
+  if (t0 + 1 < t1)
+    prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, (t0 + 1) * G::QT, L, it.dsumseq);
   if constexpr (!WINDOWED) {
     // every block of the sequence is resident for the whole sweep: take them once
 #pragma unroll
@@ -343,16 +374,14 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     }
   }
 
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = t0; j < t1; ++j) {
     const int r0 = j * G::QT;
-    // blocks touched by this query tile
-    int kmin = 0, kmax = nkb - 1;
-    if (wl >= 0) kmin = (r0 - wl > 0 ? r0 - wl : 0) / kBwdKeyBlock;
-    if (wr >= 0) {
-      const int hi = r0 + G::QT - 1 + wr < n - 1 ? r0 + G::QT - 1 + wr : n - 1;
-      kmax = hi / kBwdKeyBlock;
-    }
-    const bool any_keys = kmin <= kmax;
+    // (local) key blocks touched by this query tile
+    int klo = 0, khi = n - 1;
+    if (wl >= 0 && r0 - wl - kofs > 0) klo = r0 - wl - kofs;
+    if (wr >= 0 && r0 + G::QT - 1 + wr - kofs < n - 1) khi = r0 + G::QT - 1 + wr - kofs;
+    const bool any_keys = klo <= khi;
+    const int kmin = klo / kBwdKeyBlock, kmax = any_keys ? khi / kBwdKeyBlock : -1;
 
     // ---- 1. take the blocks entering the window (all LDS readers of the previous tile are done)
     int blk[KACT];
@@ -370,12 +399,12 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         }
       }
     }
-    if (WINDOWED || j == 0) __syncthreads();  // tile, lse, K^T staging and gate terms visible
+    if (WINDOWED || j == t0) __syncthreads();  // tile, lse, K^T staging and gate terms visible
 
     // ---- 2. softmax: D_i = sum_j p_ij dp_ij, exactly as defined (not <dO_i, O_i> of the rounded
     // forward output). S^T = K Q^T and dP^T = V dO^T put the query on the lane; the waves' partial
     // sums are combined in a fixed order (deterministic).
-    if constexpr (softmax) {
+    if constexpr (softmax && !DSUM) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         float part = 0.0f;
@@ -391,7 +420,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
 #pragma unroll
         for (int kb = 0; kb < KACT; ++kb) {
           const int kf = blk[kb] * kBwdKeyBlock;
-          const BlockMask bm = block_mask(kf, rf, n, L, wl, wr);
+          const BlockMask bm = block_mask(kofs + kf, rf, kofs + n, L, wl, wr);
           if (!act[kb] || bm.empty) continue;
           const int s = kb * G::NW + w;
           f32x16 st_ = f32x16{}, dpt = f32x16{};
@@ -403,10 +432,10 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kloc = c_row(r, g);
-            const int key = kf + kloc;
+            const int key = kofs + kf + kloc;
             float x = st_[r] * sc;
             if constexpr (has_gate) x += gl[s * kBwdKeyBlock + kloc];
-            const bool ok = (key < n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+            const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
             part += ok ? fast_exp2(x - l2) * dpt[r] : 0.0f;
           }
         }
@@ -414,12 +443,28 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         if (g == 0) dpart[w * G::QT + qs * 32 + lc] = part;
       }
       __syncthreads();
+      if constexpr (CHUNK == 2) {
+        // this chunk's share of D_i into the workspace row (the first chunk a row sees writes it)
+        const int row = r0 + (int)threadIdx.x;
+        if (threadIdx.x < G::QT && row < L) {
+          int cf, cl;
+          row_chunks(row, it.ntot, wl, wr, G::CAP, cf, cl);
+          const int c = kofs / G::CAP;
+          if (c >= cf && c <= cl) {
+            float v = dpart[threadIdx.x];
+#pragma unroll
+            for (int ww = 1; ww < G::NW; ++ww) v += dpart[ww * G::QT + threadIdx.x];
+            float* dst = it.dsumseq + (size_t)row * H;
+            *dst = c == cf ? v : *dst + v;
+          }
+        }
+      }
     }
 
     // ---- 3. S, dP, P, dS; dV, dK; dS^T to LDS. Iteration it = (query half qs, owned block kb);
     // the S / dP products of iteration it+1 are issued before the element-wise work of it, so the
     // MFMA pipe runs while the VALU works.
-    {
+    if constexpr (CHUNK != 2) {
       constexpr int NIT = 2 * KACT;
       f32x16 sacc[2], dpacc[2];
       bf16x8 qa[G::KK], da[G::KK];
@@ -467,8 +512,9 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
               const int rr = qs * 32 + a * 8 + g * 4;
               const f32x4 lv = *reinterpret_cast<const f32x4*>(lse2 + rr);
               f32x4 dsum = *reinterpret_cast<const f32x4*>(dpart + rr);
+              if constexpr (!DSUM)
 #pragma unroll
-              for (int ww = 1; ww < G::NW; ++ww) dsum += *reinterpret_cast<const f32x4*>(dpart + ww * G::QT + rr);
+                for (int ww = 1; ww < G::NW; ++ww) dsum += *reinterpret_cast<const f32x4*>(dpart + ww * G::QT + rr);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 lrow[4 * a + e] = lv[e];
@@ -478,8 +524,8 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           }
         }
         const int s = kb * G::NW + w;
-        const int kf = blk[kb] * kBwdKeyBlock;
-        const int key = kf + lc;  // this lane's key
+        const int kf = kofs + blk[kb] * kBwdKeyBlock;  // sequence position of the block
+        const int key = kf + lc;                       // this lane's key (sequence position)
         const int spos = (s * kBwdKeyBlock + lc) * G::SXROW;
         // P and dS as bf16 B operands (k-tile t = registers 8t..8t+7); zero for a block outside
         // the tile. The softmax form also carries the rounding remainder as a second bf16 term
@@ -508,11 +554,11 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
             }
           }
           if constexpr (MASKED) {
-            if (!block_mask(kf, rf, n, L, wl, wr).full) {
+            if (!block_mask(kf, rf, kofs + n, L, wl, wr).full) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int row = rf + c_row(r, g);
-                const bool ok = (key < n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+                const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
                 p[r] = ok ? p[r] : 0.0f;
                 ds[r] = ok ? ds[r] : 0.0f;
               }
@@ -539,7 +585,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         if constexpr (MASKED) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) pu[t] = du[t] = plu[t] = dlu[t] = u32x4{0u, 0u, 0u, 0u};
-          if (act[kb] && !block_mask(kf, rf, n, L, wl, wr).empty) elementwise();
+          if (act[kb] && !block_mask(kf, rf, kofs + n, L, wl, wr).empty) elementwise();
         } else {
           // no mask: keys and rows past the ends meet zero operands, and phi(0) = 0
           elementwise();
@@ -567,16 +613,17 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       }
     }
     __syncthreads();  // dS^T tile complete; this tile's Q / dO / lse no longer read
-    if (j + 1 < ntiles) {
+    if (j + 1 < t1) {
       // next tile into LDS (while dQ runs), then the loads of the one after it: issued before this
       // tile's dQ stores, so waiting for them never waits for those stores
-      store_qtile<D, softmax>(lds, pf);
-      if (j + 2 < ntiles) prefetch_qtile<D, softmax>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L);
+      store_qtile<D, softmax, DSUM>(lds, pf);
+      if (j + 2 < t1)
+        prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
     }
 
     // ---- 4. dQ^T = K^T dS^T over the ring slots in use (a slot outside the tile holds zero dS);
     // register r of lane (query, g) is d = dtile*32 + g*16 + r (out_perm order of the K^T rows)
-    if (dq_role) {
+    if (CHUNK != 2 && dq_role) {
       const int drow = dtile * 32 + out_perm(lc);  // K^T row carried by this lane's A-operand row
 #pragma unroll
       for (int qi = 0; qi < G::QH; ++qi) {
@@ -601,7 +648,38 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         }
         const f32x16 acc = acc2[0] + acc2[1];
         const int row = r0 + qh * 32 + lc;
-        if (row < L) {
+        if constexpr (CHUNK == 1) {
+          // this chunk's share of the row's dQ: the first chunk the row sees writes the fp32 row,
+          // later ones add to it, the last converts it (a shared query matrix keeps fp32 partials)
+          int cf = 0, cl = -1;
+          if (row < L) row_chunks(row, it.ntot, wl, wr, G::CAP, cf, cl);
+          const int c = kofs / G::CAP;
+          if (c >= cf && c <= cl) {
+            float* p32 = it.dq32seq + row * rs + dtile * 32 + g * 16;
+            f32x4 v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = f32x4{acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]};
+              if (c != cf) v[e] += *reinterpret_cast<const f32x4*>(p32 + 4 * e);
+            }
+            if (c == cl && !it.shared_q) {
+              u32x4 u0, u1;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                u0[2 * e] = pack_bf16x2(v[e][0] * gd.scale, v[e][1] * gd.scale);
+                u0[2 * e + 1] = pack_bf16x2(v[e][2] * gd.scale, v[e][3] * gd.scale);
+                u1[2 * e] = pack_bf16x2(v[2 + e][0] * gd.scale, v[2 + e][1] * gd.scale);
+                u1[2 * e + 1] = pack_bf16x2(v[2 + e][2] * gd.scale, v[2 + e][3] * gd.scale);
+              }
+              bf16* dst = it.dqseq + row * rs + dtile * 32 + g * 16;
+              *reinterpret_cast<u32x4*>(dst) = u0;
+              *reinterpret_cast<u32x4*>(dst + 8) = u1;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) *reinterpret_cast<f32x4*>(p32 + 4 * e) = v[e];
+            }
+          }
+        } else if (row < L) {
           u32x4 u0, u1;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -614,11 +692,12 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         }
       }
     }
-    if (j + 1 < ntiles) __syncthreads();  // next tile staged; dS^T and K^T staging free
+    if (j + 1 < t1) __syncthreads();  // next tile staged; dS^T and K^T staging free
   }
+  if constexpr (CHUNK != 2)
 #pragma unroll
-  for (int kb = 0; kb < KACT; ++kb)
-    if (st.cur[kb] >= 0) flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
+    for (int kb = 0; kb < KACT; ++kb)
+      if (st.cur[kb] >= 0) flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
 }
 
 template <int D, int ACT, bool GATED>
@@ -633,23 +712,41 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   it.wl = gd.wl;
   it.wr = gd.wr;
   const int H = it.H;
-  it.qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
+  it.shared_q = gd.shared_q > 0;
+  // a shared query matrix: every sequence reads its rows from row 0; its dQ rows are fp32
+  // partials of sequence b at rows [b * shared_q, ...) of the workspace
+  const size_t qrow = it.shared_q ? 0 : (size_t)q0;
+  const size_t dqrow = it.shared_q ? (size_t)b * gd.shared_q : (size_t)q0;
+  it.qseq = reinterpret_cast<const bf16*>(gd.q) + (qrow * H + h) * D;
   it.doseq = reinterpret_cast<const bf16*>(gd.dout) + ((size_t)q0 * H + h) * D;
   it.lseseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
   it.dqseq = reinterpret_cast<bf16*>(gd.dq) + ((size_t)q0 * H + h) * D;
+  it.dq32seq = gd.dq32 ? gd.dq32 + (dqrow * H + h) * D : nullptr;
+  it.dsumseq = gd.delta ? gd.delta + (size_t)q0 * H + h : nullptr;
   it.kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
   it.vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;
   it.gseq = gd.g ? gd.g + (size_t)k0 * H + h : nullptr;
   it.dkseq = reinterpret_cast<bf16*>(gd.dk) + ((size_t)k0 * H + h) * D;
   it.dvseq = reinterpret_cast<bf16*>(gd.dv) + ((size_t)k0 * H + h) * D;
   it.dgseq = gd.dg ? gd.dg + (size_t)k0 * H + h : nullptr;
+  it.kofs = 0;
+  it.ntot = it.n;
+  it.t0 = 0;
+  it.t1 = (it.L + G::QT - 1) / G::QT;
   const int L = it.L, n = it.n;
   const size_t rs = it.rs;
 
-  if (n <= 0) {  // no keys: dQ = 0
-    for (int idx = threadIdx.x; idx < L * G::CPR; idx += G::THREADS) {
-      const int r = idx / G::CPR, c = idx % G::CPR;
-      *reinterpret_cast<u32x4*>(it.dqseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+  if (n <= 0) {  // no keys: dQ = 0 (a shared query matrix: zero partial rows)
+    if (it.shared_q) {
+      for (int idx = threadIdx.x; idx < L * (D / 4); idx += G::THREADS) {
+        const int r = idx / (D / 4), c = idx % (D / 4);
+        *reinterpret_cast<f32x4*>(it.dq32seq + r * rs + c * 4) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < L * G::CPR; idx += G::THREADS) {
+        const int r = idx / G::CPR, c = idx % G::CPR;
+        *reinterpret_cast<u32x4*>(it.dqseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     return;
   }
@@ -663,11 +760,47 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
       for (int r = threadIdx.x; r < n; r += G::THREADS) it.dgseq[(size_t)r * H] = 0.0f;
     return;
   }
+  const bool windowed = it.wl >= 0 || it.wr >= 0;
+  if (it.shared_q || (n > G::CAP && !bwd_ring_ok(D, it.wl, it.wr))) {
+    // key chunks of CAP keys, one after the other; each sweeps the query tiles whose rows see it.
+    // Softmax first accumulates D_i over every chunk (a pass of its own), then the main passes.
+    const int nch = (n + G::CAP - 1) / G::CAP;
+    auto chunk_item = [&](int c) {
+      BwdItem ci = it;
+      ci.kofs = c * G::CAP;
+      ci.n = n - ci.kofs < G::CAP ? n - ci.kofs : G::CAP;
+      ci.kseq = it.kseq + (size_t)ci.kofs * rs;
+      ci.vseq = it.vseq + (size_t)ci.kofs * rs;
+      ci.gseq = it.gseq ? it.gseq + (size_t)ci.kofs * H : nullptr;
+      ci.dkseq = it.dkseq + (size_t)ci.kofs * rs;
+      ci.dvseq = it.dvseq + (size_t)ci.kofs * rs;
+      ci.dgseq = it.dgseq ? it.dgseq + (size_t)ci.kofs * H : nullptr;
+      // rows whose window reaches the chunk's keys [kofs, kofs + n)
+      int rlo = 0, rhi = L - 1;
+      if (it.wr >= 0 && ci.kofs - it.wr > 0) rlo = ci.kofs - it.wr;
+      if (it.wl >= 0 && ci.kofs + ci.n - 1 + it.wl < L - 1) rhi = ci.kofs + ci.n - 1 + it.wl;
+      ci.t0 = rlo / G::QT;
+      ci.t1 = rhi >= rlo ? rhi / G::QT + 1 : ci.t0;
+      return ci;
+    };
+    if constexpr (ACT == GDPA_ACT_SOFTMAX) {
+      for (int c = 0; c < nch; ++c) {
+        const BwdItem ci = chunk_item(c);
+        __syncthreads();  // previous pass done with LDS
+        bwd_sweep<D, ACT, GATED, G::KB, false, 2>(lds, gd, ci);
+      }
+    }
+    for (int c = 0; c < nch; ++c) {
+      const BwdItem ci = chunk_item(c);
+      __syncthreads();
+      bwd_sweep<D, ACT, GATED, G::KB, false, 1>(lds, gd, ci);
+    }
+    return;
+  }
   // One owned block per wave suffices when all keys fit in NW blocks. Zero padding makes the
   // entries past the ends vanish for the element-wise forms (phi(0) = 0; dO and V rows past the
   // ends are zero), so only the softmax form and windows need explicit masks.
   const bool few_keys = (n + kBwdKeyBlock - 1) / kBwdKeyBlock <= G::NW;
-  const bool windowed = it.wl >= 0 || it.wr >= 0;
   if (windowed) {
     if (G::KB > 1 && few_keys) bwd_sweep<D, ACT, GATED, 1, true>(lds, gd, it);
     else bwd_sweep<D, ACT, GATED, G::KB, true>(lds, gd, it);

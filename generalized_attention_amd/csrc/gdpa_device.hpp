@@ -36,7 +36,8 @@ struct GroupDesc {
   void* dk;
   void* dv;
   float* dg;
-  float* delta;  // softmax backward: D_i = <dO_i, O_i> per (row, head), in the workspace
+  float* delta;  // softmax backward: D_i = sum_j p_ij dp_ij per (row, head), in the workspace
+  float* dq32;   // backward in key chunks: fp32 dQ accumulation rows (workspace), row stride H*d
   const int32_t* q_off;
   const int32_t* kv_off;
   const int32_t* head_acts;  // activation per head, or null (act for every head)
@@ -48,6 +49,7 @@ struct GroupDesc {
   int32_t wl;
   int32_t wr;
   int32_t seq_base;   // index of this group's first sequence in the global sequence numbering
+  int32_t shared_q;   // rows of a query matrix shared by every sequence (0: per-sequence queries)
 };
 
 struct LaunchDesc {

@@ -17,8 +17,9 @@
 //     of O^T = V^T P^T (A = V^T rows from LDS), so P never leaves registers.
 //   * Epilogue: each lane holds 16 consecutive d of one row of O: two 16-byte stores.
 // Short key ranges (personalized-FFN form: n keys per sample) are staged once and the waves sweep
-// all query tiles of the sequence; a bounded sliding window is swept in chunks of 128 rows whose
-// key range [r0 - left, r0 + 128 + right) is restaged per chunk.
+// all query tiles of the sequence. Longer ranges are swept in row groups of 128 rows: the group's
+// keys (under a window only [r0 - left, r0 + 128 + right)) pass through LDS in chunks, with the
+// O accumulators and the online-softmax state carried across chunks in registers.
 #include "gdpa_device.hpp"
 #include "gdpa_launch.hpp"
 
@@ -54,7 +55,8 @@ __device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
 // memory latency. K rows are copied as 16-byte chunks; V is transposed in units of 4 consecutive
 // keys x 8 d: the 4 keys of one d are adjacent in the V^T slot order, so each d is one 8-byte
 // write.
-template <int D, int NT>
+// SERIAL: keep the rounds in order (the caller holds accumulators in registers across the staging).
+template <int D, int NT, bool SERIAL = false>
 __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
                          int span, int span_pad, bool softmax) {
   using G = FwdGeo<D>;
@@ -73,8 +75,7 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
     gv[i] = 0.0f;
     if (gb != nullptr && r < span) gv[i] = gb[(size_t)r * hstride];
   }
-#pragma unroll
-  for (int round = 0; round < ROUNDS; ++round) {
+  auto stage_round = [&](int round) {
     constexpr int KR = KI / ROUNDS, VR = (VI + ROUNDS - 1) / ROUNDS;
     u32x4 kbuf[KR], vbuf[VR][4];
 #pragma unroll
@@ -119,6 +120,13 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
         }
       }
     }
+  };
+  if constexpr (SERIAL) {
+#pragma unroll 1
+    for (int round = 0; round < ROUNDS; ++round) stage_round(round);
+  } else {
+#pragma unroll
+    for (int round = 0; round < ROUNDS; ++round) stage_round(round);
   }
   float* gl = reinterpret_cast<float*>(lds + G::OFF_G);
 #pragma unroll
@@ -174,33 +182,45 @@ __device__ inline void scores_block(const char* lds, const QFrags<D, QS>& q, int
   }
 }
 
+// Running state of one wave's query tile: the O accumulators and, for softmax, the running row
+// maximum (log2 units) and the lane's partial row sum.
+template <int D, int QS>
+struct FwdAcc {
+  f32x16 o[QS][D / 32];
+  float m[QS], lsum[QS];
+};
+
+template <int D, int QS>
+__device__ __forceinline__ void acc_init(FwdAcc<D, QS>& a) {
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    a.m[qs] = -__builtin_inff();
+    a.lsum[qs] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) a.o[qs][dt] = f32x16{};
+  }
+}
+
+// Adds the staged key blocks [kb0, kb1) to the wave's tile state.
 // GATED: the problem has a gate. MASKED: entries may need an explicit mask (the softmax form, or
 // a window); without it, keys past the end meet zero K and V rows in LDS and phi(0) = 0.
 template <int D, int ACT, int QS, bool GATED, bool MASKED>
-__device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
-                                         float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
+__device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf,
+                                               FwdAcc<D, QS>& acc, int row0, int klo, int span, int kb0,
+                                               int kb1) {
   using G = FwdGeo<D>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
-  const int H = gd.num_heads;
-  const size_t rs = (size_t)H * D;
   constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
   const float* gl = reinterpret_cast<const float*>(lds + G::OFF_G);
-  f32x16 o[QS][G::DT];
-  float m[QS], lsum[QS];
-#pragma unroll
-  for (int qs = 0; qs < QS; ++qs) {
-    m[qs] = -__builtin_inff();
-    lsum[qs] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < G::DT; ++dt) o[qs][dt] = f32x16{};
-  }
+  auto& o = acc.o;
+  auto& m = acc.m;
+  auto& lsum = acc.lsum;
   const float sc = softmax ? gd.scale * kLog2e : gd.scale;
   const int wl = gd.wl, wr = gd.wr;
   // element-wise forms: without a gate p' = s g(scale s) = phi(scale s) / scale and O is scaled
   // once in the epilogue; with a gate the argument scale s + log sigmoid(G) is formed first.
   float c1 = 0.0f, c3 = 0.0f;
   if constexpr (!softmax) PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
-  const float out_scale = (!softmax && !GATED) ? gd.scale : 1.0f;
 
   // Element-wise stage and P V for block kb whose scores are in s: register r of lane (qc, g) is
   // key kb*32 + c_row(r, g), row qs*32 + qc.
@@ -300,15 +320,27 @@ __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, c
     process(kb, sa);
   }
 
-  // epilogue
+}
+
+// Epilogue of one wave tile: softmax normalisation and lse, or the deferred score scale of the
+// element-wise forms; each lane stores 16 consecutive d of one row.
+template <int D, int ACT, int QS, bool GATED>
+__device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, QS>& acc, bf16* oseq, float* lseq,
+                                           int L, int row0) {
+  using G = FwdGeo<D>;
+  const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
+  const int H = gd.num_heads;
+  const size_t rs = (size_t)H * D;
+  constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
+  const float out_scale = (!softmax && !GATED) ? gd.scale : 1.0f;
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
     const int row = row0 + qs * 32 + qc;
     float inv = out_scale, lse = 0.0f;
     if (softmax) {
-      const float ltot = lsum[qs] + __shfl_xor(lsum[qs], 32);
+      const float ltot = acc.lsum[qs] + __shfl_xor(acc.lsum[qs], 32);
       inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-      lse = ltot > 0.0f ? (m[qs] + __log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
+      lse = ltot > 0.0f ? (acc.m[qs] + __log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
     }
     if (row < L) {
 #pragma unroll
@@ -316,8 +348,8 @@ __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, c
         u32x4 u0, u1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          u0[e] = pack_bf16x2(o[qs][dt][2 * e] * inv, o[qs][dt][2 * e + 1] * inv);
-          u1[e] = pack_bf16x2(o[qs][dt][8 + 2 * e] * inv, o[qs][dt][8 + 2 * e + 1] * inv);
+          u0[e] = pack_bf16x2(acc.o[qs][dt][2 * e] * inv, acc.o[qs][dt][2 * e + 1] * inv);
+          u1[e] = pack_bf16x2(acc.o[qs][dt][8 + 2 * e] * inv, acc.o[qs][dt][8 + 2 * e + 1] * inv);
         }
         bf16* dst = oseq + row * rs + dt * 32 + g * 16;
         *reinterpret_cast<u32x4*>(dst) = u0;
@@ -326,6 +358,16 @@ __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, c
       if (softmax && g == 0) lseq[(size_t)row * H] = lse;
     }
   }
+}
+
+// One wave tile against staged key blocks [kb0, kb1), then its epilogue.
+template <int D, int ACT, int QS, bool GATED, bool MASKED>
+__device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
+                                         float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
+  FwdAcc<D, QS> acc;
+  acc_init(acc);
+  fwd_accumulate<D, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, klo, span, kb0, kb1);
+  fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
 }
 
 // One work item: all query rows of one (sequence, head).
@@ -337,7 +379,9 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
   if (L <= 0) return;
   const int H = gd.num_heads;
   const size_t rs = (size_t)H * D;
-  const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
+  // a shared query matrix (seed queries): every sequence reads its query rows from row 0
+  const size_t qrow = gd.shared_q ? 0 : (size_t)q0;
+  const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + (qrow * H + h) * D;
   bf16* oseq = reinterpret_cast<bf16*>(gd.o) + ((size_t)q0 * H + h) * D;
   float* lseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
   const bf16* kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
@@ -369,31 +413,47 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       if (kPrefetchQ) qcur = qnext;
     }
   } else {
-    // bounded window (both sides >= 0, checked on the host): chunks of kFwdChunkRows rows
-    if (gd.wl < 0 || gd.wr < 0 || gd.wl + gd.wr + kFwdChunkRows > G::NKV) return;  // host-rejected shape
-    for (int r0 = 0; r0 < L; r0 += kFwdChunkRows) {
-      const int klo = r0 - gd.wl > 0 ? r0 - gd.wl : 0;
-      int khi = r0 + kFwdChunkRows + gd.wr;
-      if (khi > N) khi = N;
-      const int span = khi - klo;
-      __syncthreads();  // previous chunk done with LDS
-      stage_kv<D, NW * kWave>(lds, kseq + (size_t)klo * H * D, vseq + (size_t)klo * H * D,
-                  gseq ? gseq + (size_t)klo * H : nullptr, H, span, (span + 31) & ~31, softmax);
-      __syncthreads();
-      for (int row0 = r0 + w * RW; row0 < r0 + kFwdChunkRows && row0 < L; row0 += NW * RW) {
-        int lo = row0 - gd.wl > klo ? row0 - gd.wl : klo;
-        int hi = row0 + RW - 1 + gd.wr < khi - 1 ? row0 + RW - 1 + gd.wr : khi - 1;
-        const int kb0 = (lo - klo) / 32, kb1 = hi >= lo ? (hi - klo) / 32 + 1 : kb0;
-        QFrags<D, QS> qf;
-        load_q<D, QS>(qf, qseq, rs, row0, L);
-        fwd_tile<D, ACT, QS, GATED, MASKED>(lds, gd, qf, oseq, lseq, L, row0, klo, span, kb0, kb1);
+    // long key range: row groups of NW * RW rows; for each, the group's key range (all keys, or
+    // [r0 - left, r0 + NW * RW + right) under a window) is staged in chunks of NKV keys and every
+    // wave carries its tile's O and softmax state across the chunks.
+    for (int r0 = 0; r0 < L; r0 += NW * RW) {
+      const int row0 = r0 + w * RW;
+      const bool active = row0 < L;
+      int glo = 0, ghi = N;
+      if (gd.wl >= 0) glo = r0 - gd.wl > 0 ? r0 - gd.wl : 0;
+      if (gd.wr >= 0 && r0 + NW * RW + gd.wr < N) ghi = r0 + NW * RW + gd.wr;
+      // the wave's own key range [lo, hi]
+      int lo = 0, hi = N - 1;
+      if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
+      if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
+      // d <= 64: Q stays in registers across the chunks; d = 128 reloads it per chunk (from L2)
+      // to keep the register file free for the staging
+      constexpr bool kHoldQ = D < 128;
+      QFrags<D, QS> qf;
+      if (kHoldQ && active) load_q<D, QS>(qf, qseq, rs, row0, L);
+      FwdAcc<D, QS> acc;
+      acc_init(acc);
+      for (int kc = glo; kc < ghi; kc += G::NKV) {
+        const int span = ghi - kc < G::NKV ? ghi - kc : G::NKV;
+        __syncthreads();  // previous chunk done with LDS
+        stage_kv<D, NW * kWave, true>(lds, kseq + (size_t)kc * H * D, vseq + (size_t)kc * H * D,
+                    gseq ? gseq + (size_t)kc * H : nullptr, H, span, (span + 31) & ~31, softmax);
+        __syncthreads();
+        const int clo = lo > kc ? lo : kc;
+        const int chi = hi < kc + span - 1 ? hi : kc + span - 1;
+        if (active && chi >= clo) {
+          if (!kHoldQ) load_q<D, QS>(qf, qseq, rs, row0, L);
+          fwd_accumulate<D, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, kc, span, (clo - kc) / 32,
+                                                    (chi - kc) / 32 + 1);
+        }
       }
+      if (active) fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
     }
   }
 }
 
-// Gate and mask variants of one activation: the chunked window path and the softmax form are
-// masked; a problem without window or softmax runs the mask-free body.
+// Gate and mask variants of one activation: a window and the softmax form are masked; a problem
+// without window or softmax runs the mask-free body.
 template <int D, int NW, int ACT, int QS>
 __device__ __forceinline__ void fwd_dispatch_variant(char* lds, const GroupDesc& gd, int b, int h) {
   const bool masked = ACT == GDPA_ACT_SOFTMAX || gd.wl >= 0 || gd.wr >= 0;
@@ -408,25 +468,12 @@ __device__ __forceinline__ void fwd_dispatch_variant(char* lds, const GroupDesc&
 
 template <int D, int NW, int ASET>
 __device__ __forceinline__ void fwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
-  const bool chunked = (gd.kv_off[b + 1] - gd.kv_off[b]) > FwdGeo<D>::NKV;
-  constexpr int QS2 = 1;
   if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
-    if (gd.act == GDPA_ACT_GELU) {
-      if (chunked) fwd_dispatch_variant<D, NW, GDPA_ACT_GELU, 1>(lds, gd, b, h);
-      else fwd_dispatch_variant<D, NW, GDPA_ACT_GELU, QS2>(lds, gd, b, h);
-      return;
-    }
+    if (gd.act == GDPA_ACT_GELU) { fwd_dispatch_variant<D, NW, GDPA_ACT_GELU, 1>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
-    if (gd.act == GDPA_ACT_SILU) {
-      if (chunked) fwd_dispatch_variant<D, NW, GDPA_ACT_SILU, 1>(lds, gd, b, h);
-      else fwd_dispatch_variant<D, NW, GDPA_ACT_SILU, QS2>(lds, gd, b, h);
-      return;
-    }
+    if (gd.act == GDPA_ACT_SILU) { fwd_dispatch_variant<D, NW, GDPA_ACT_SILU, 1>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
-    if (gd.act == GDPA_ACT_SOFTMAX) {
-      if (chunked) fwd_dispatch_variant<D, NW, GDPA_ACT_SOFTMAX, 1>(lds, gd, b, h);
-      else fwd_dispatch_variant<D, NW, GDPA_ACT_SOFTMAX, QS2>(lds, gd, b, h);
-    }
+    if (gd.act == GDPA_ACT_SOFTMAX) fwd_dispatch_variant<D, NW, GDPA_ACT_SOFTMAX, 1>(lds, gd, b, h);
 }
 
 template <int DSET, int ASET>
@@ -464,8 +511,7 @@ hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStr
     case kDim32: GDPA_LAUNCH_ACTS(kDim32); break;
     case kDim64: GDPA_LAUNCH_ACTS(kDim64); break;
     case kDim128: GDPA_LAUNCH_ACTS(kDim128); break;
-    case kDim32 | kDim128: GDPA_LAUNCH(kDim32 | kDim128, kAll); break;
-    default: GDPA_LAUNCH(kDim32 | kDim64 | kDim128, kAll); break;
+    default: GDPA_LAUNCH_ACTS(kDim32 | kDim64 | kDim128); break;  // several head dims
   }
 #undef GDPA_LAUNCH_ACTS
 #undef GDPA_LAUNCH

@@ -26,15 +26,6 @@ hipError_t launch_bwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t 
 
 // Keys of one (sequence, head) whose K and V^T fit in the forward kernel's LDS at once.
 inline constexpr int fwd_kv_capacity(int d) { return 16384 / d; }
-// Rows per window chunk of the forward kernel (4 waves x 32 rows).
-constexpr int kFwdChunkRows = 128;
-// Forward: either every sequence's keys fit at once, or a bounded window whose per-chunk key
-// range [r0 - left, r0 + 128 + right) fits.
-inline bool fwd_shape_ok(int d, int wl, int wr, int max_kv) {
-  const int cap = fwd_kv_capacity(d);
-  if (max_kv <= cap) return true;
-  return wl >= 0 && wr >= 0 && wl + wr + kFwdChunkRows <= cap;
-}
 // Backward: 4 waves per workgroup; each wave owns 64 keys (two blocks of 32; 32 keys at d = 128)
 // for the whole sweep over query tiles of 64 rows.
 constexpr int kBwdWaves = 4;
@@ -42,12 +33,18 @@ constexpr int kBwdKeyBlock = 32;
 constexpr int kBwdQueryTile = 64;
 inline constexpr int bwd_keys_per_wave(int d) { return d == 128 ? 32 : 64; }
 inline constexpr int bwd_capacity(int d) { return kBwdWaves * bwd_keys_per_wave(d); }
-// Either all keys of a sequence are resident at once, or a bounded window whose key span for one
-// query tile fits in the ring of resident blocks with one block to spare (misalignment).
-inline bool bwd_shape_ok(int d, int wl, int wr, int max_kv) {
-  const int cap = bwd_capacity(d);
-  if (max_kv <= cap) return true;
-  return wl >= 0 && wr >= 0 && kBwdQueryTile - 1 + wl + wr <= cap - kBwdKeyBlock;
+// A bounded window whose key span for one query tile fits in the ring of resident blocks with one
+// block to spare (misalignment): keys stream through the ring as the tiles advance.
+inline __host__ __device__ bool bwd_ring_ok(int d, int wl, int wr) {
+  return wl >= 0 && wr >= 0 && kBwdQueryTile - 1 + wl + wr <= bwd_capacity(d) - kBwdKeyBlock;
 }
+// Otherwise a sequence with more keys than are resident is processed in key chunks, one after the
+// other, with dQ (and the softmax row term) accumulated in fp32 workspace rows.
+inline bool bwd_may_chunk(int d, int wl, int wr, int max_kv) {
+  return max_kv > bwd_capacity(d) && !bwd_ring_ok(d, wl, wr);
+}
+
+// Shared-query groups: sum the per-sequence fp32 dQ rows into dq (bf16).
+hipError_t launch_reduce_shared_dq(const GroupDesc& gd, hipStream_t stream);
 
 }  // namespace gdpa

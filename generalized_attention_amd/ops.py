@@ -21,7 +21,7 @@ _DTYPES = {torch.bfloat16: _lib.GDPA_DTYPE_BF16, torch.float32: _lib.GDPA_DTYPE_
 class GroupArgs:
     """One GDPA problem: device tensors plus the shape hints the library needs."""
 
-    q: torch.Tensor            # [total_q, H, d]
+    q: torch.Tensor            # [total_q, H, d]; with shared_q one [S, H, d] matrix
     k: torch.Tensor            # [total_kv, H, d]
     v: torch.Tensor            # [total_kv, H, d]
     q_offsets: torch.Tensor    # int32 [B+1] on the device
@@ -35,6 +35,12 @@ class GroupArgs:
     self_attention: bool = False
     planned: bool = False  # the workspace holds a gdpa_plan() work list for this shape
     head_acts: Optional[torch.Tensor] = None  # int32 [H] on the device: activation per head
+    shared_q: bool = False  # q is one query matrix shared by every sequence (rows of o: total_q)
+    total_q: Optional[int] = None  # rows of o / lse / dout (default: rows of q)
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0] if self.total_q is None else int(self.total_q)
 
     @property
     def may_softmax(self) -> bool:
@@ -49,12 +55,12 @@ class GroupArgs:
         p.act = _ACTS[self.act]
         p.scale = float(self.scale)
         p.window_left, p.window_right = int(self.window[0]), int(self.window[1])
-        p.total_q = self.q.shape[0]
+        p.total_q = self.rows
         p.total_kv = self.k.shape[0]
         p.max_seqlen_q = int(self.max_seqlen_q)
         p.max_seqlen_kv = int(self.max_seqlen_kv)
         p.self_attention = 1 if self.self_attention else 0
-        p.flags = _lib.GDPA_FLAG_PLANNED if self.planned else 0
+        p.flags = (_lib.GDPA_FLAG_PLANNED if self.planned else 0) | (_lib.GDPA_FLAG_SHARED_Q if self.shared_q else 0)
         p.q_offsets = self.q_offsets.data_ptr()
         p.kv_offsets = self.kv_offsets.data_ptr()
         p.head_acts = 0 if self.head_acts is None else self.head_acts.data_ptr()
@@ -62,10 +68,12 @@ class GroupArgs:
 
 
 def make_group(q, k, v, q_offsets, kv_offsets, *, act, scale: float, window=(-1, -1), g=None,
-               self_attention: Optional[bool] = None, lengths_q=None, lengths_kv=None) -> GroupArgs:
+               self_attention: Optional[bool] = None, lengths_q=None, lengths_kv=None,
+               shared_q: bool = False) -> GroupArgs:
     """Build GroupArgs from device tensors. Offsets may be given on the host (int64 numpy/torch)
     or the device; the max lengths come from host lengths when given (no device sync).
-    act: an activation name, or a sequence with one name per head."""
+    act: an activation name, or a sequence with one name per head. shared_q: q is one [S, H, d]
+    query matrix whose row i is query row i of every sequence (each sequence has <= S rows)."""
     dev = q.device
     head_acts = None
     if not isinstance(act, str):
@@ -88,9 +96,11 @@ def make_group(q, k, v, q_offsets, kv_offsets, *, act, scale: float, window=(-1,
         lengths_kv = (lk[1:] - lk[:-1]).tolist()
     if self_attention is None:
         self_attention = window != (-1, -1)
+    max_q = q.shape[0] if shared_q else int(max(lengths_q, default=0))
     return GroupArgs(q=q, k=k, v=v, q_offsets=qo, kv_offsets=ko, act=act, scale=scale,
-                     max_seqlen_q=int(max(lengths_q, default=0)), max_seqlen_kv=int(max(lengths_kv, default=0)),
-                     window=tuple(window), g=g, self_attention=bool(self_attention), head_acts=head_acts)
+                     max_seqlen_q=max_q, max_seqlen_kv=int(max(lengths_kv, default=0)),
+                     window=tuple(window), g=g, self_attention=bool(self_attention), head_acts=head_acts,
+                     shared_q=bool(shared_q), total_q=int(sum(lengths_q)) if shared_q else None)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> int:
@@ -123,10 +133,10 @@ def _fwd_tensors(grp: GroupArgs, o, lse) -> _lib.gdpa_tensors:
 
 
 def _alloc_fwd(grp: GroupArgs):
-    o = torch.empty_like(grp.q)
+    o = torch.empty((grp.rows,) + tuple(grp.q.shape[1:]), dtype=grp.q.dtype, device=grp.q.device)
     lse = None
     if grp.may_softmax:
-        lse = torch.empty(grp.q.shape[0], grp.q.shape[1], dtype=torch.float32, device=grp.q.device)
+        lse = torch.empty(grp.rows, grp.q.shape[1], dtype=torch.float32, device=grp.q.device)
     return o, lse
 
 

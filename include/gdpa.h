@@ -23,7 +23,9 @@
  *     at 0; sequence b owns rows [offsets[b], offsets[b+1]). They are trusted (not re-validated on
  *     the device); the host-side hints max_seqlen_q / max_seqlen_kv must bound the real lengths.
  *   - The workspace `ws` (device memory of at least gdpa_workspace_size() bytes, 256-byte aligned)
- *     is scratch for the call's work list; its contents on entry are ignored.
+ *     is scratch for the call's work list and, in the backward, for fp32 row accumulators (long
+ *     key ranges that are processed in chunks, shared query matrices); its contents on entry are
+ *     ignored.
  *   - The library keeps no state between calls; distinct calls may run concurrently on different
  *     streams as long as they use distinct workspaces and outputs.
  *
@@ -49,6 +51,14 @@ extern "C" {
  * is a permutation of (group, head, sequence) items, so a list built from older offsets of the
  * same shape is still complete (only its longest-first order may be stale). */
 #define GDPA_FLAG_PLANNED 1
+
+/* gdpa_problem.flags: one query matrix shared by every sequence (learnable seed or summary-token
+ * queries attending over each jagged sequence: the PMA / hierarchical seed pooling use of the
+ * operator, Kunlun review, sections 2.3 and 2.4). q and dq are then [max_seqlen_q, H, d]: query row
+ * i of every sequence is row i of q, and dq is the sum of the per-sequence gradients. o, lse and
+ * dout keep their [total_q, ...] rows at q_offsets, and every q_offsets[b+1]-q_offsets[b] must be
+ * at most max_seqlen_q. bf16 only; not with self_attention (hence no window). */
+#define GDPA_FLAG_SHARED_Q 2
 
 typedef enum gdpa_status {
   GDPA_OK = 0,
@@ -84,7 +94,7 @@ typedef struct gdpa_problem {
   int32_t max_seqlen_q;  /* upper bound on any q_offsets[b+1]-q_offsets[b] */
   int32_t max_seqlen_kv; /* upper bound on any kv_offsets[b+1]-kv_offsets[b] */
   int32_t self_attention;/* 1: kv_offsets equal q_offsets (same sequences); 0: cross-attention */
-  int32_t flags;         /* 0 or GDPA_FLAG_PLANNED (same value in every problem of a call) */
+  int32_t flags;         /* GDPA_FLAG_* bits; GDPA_FLAG_PLANNED must agree across a call */
   const int32_t* q_offsets;  /* device [B+1] */
   const int32_t* kv_offsets; /* device [B+1] */
   /* Optional DEVICE array [num_heads] of gdpa_act: head h uses head_acts[h] instead of act (the

@@ -46,9 +46,9 @@ def load(path: str = LIB_PATH):
     lib.gdpa_oracle_phi_grad.restype = d
     lib.gdpa_oracle_log_sigmoid.argtypes = [d]
     lib.gdpa_oracle_log_sigmoid.restype = d
-    lib.gdpa_oracle_fwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, i, p]
+    lib.gdpa_oracle_fwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, i, p, i]
     lib.gdpa_oracle_fwd.restype = i
-    lib.gdpa_oracle_bwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, p, p, p, i, p]
+    lib.gdpa_oracle_bwd.argtypes = [i, i, i, p, p, p, p, p, p, i, d, i, i, p, p, p, p, p, i, p, i]
     lib.gdpa_oracle_bwd.restype = i
     if path == LIB_PATH:
         _lib = lib
@@ -74,20 +74,23 @@ def _acts(act, h):
 
 
 def fwd(q, k, v, q_offsets, kv_offsets, *, act, scale: float, g=None,
-        window=(-1, -1), nthreads: int = 0, lib=None) -> Dict[str, np.ndarray]:
+        window=(-1, -1), shared_q: bool = False, nthreads: int = 0, lib=None) -> Dict[str, np.ndarray]:
     """Forward of the plain definition. Arrays: q [Tq,H,d], k/v [Tk,H,d], g [Tk,H] or None.
-    act: an activation name, or a list with one name per head."""
+    act: an activation name, or a list with one name per head. shared_q: q is one [S,H,d] query
+    matrix whose row i is query row i of every sequence (o and lse still have Tq rows)."""
     lib = lib or load()
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
     qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
     ko = np.ascontiguousarray(kv_offsets, dtype=np.int64)
-    tq, h, d = q.shape
+    _, h, d = q.shape
+    tq = int(qo[-1])
     code, heads = _acts(act, h)
-    o = np.zeros_like(q)
+    o = np.zeros((tq, h, d), dtype=np.float64)
     lse = np.zeros((tq, h), dtype=np.float64)
     rc = lib.gdpa_oracle_fwd(len(qo) - 1, h, d, _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                              _ptr(g), code, float(scale), int(window[0]),
-                             int(window[1]), _ptr(o), _ptr(lse), int(nthreads), _ptr(heads))
+                             int(window[1]), _ptr(o), _ptr(lse), int(nthreads), _ptr(heads),
+                             q.shape[0] if shared_q else 0)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     out = {"o": o}
@@ -97,8 +100,10 @@ def fwd(q, k, v, q_offsets, kv_offsets, *, act, scale: float, g=None,
 
 
 def bwd(q, k, v, dout, q_offsets, kv_offsets, *, act, scale: float, g=None,
-        window=(-1, -1), want_dg: bool = False, nthreads: int = 0, lib=None) -> Dict[str, np.ndarray]:
-    """Gradients of sum(dout * o) with respect to q, k, v (and the gate G if want_dg)."""
+        window=(-1, -1), want_dg: bool = False, shared_q: bool = False, nthreads: int = 0,
+        lib=None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dout * o) with respect to q, k, v (and the gate G if want_dg); with
+    shared_q, dq is the [S,H,d] gradient of the shared query matrix."""
     lib = lib or load()
     q, k, v, g, dout = _f64(q), _f64(k), _f64(v), _f64(g), _f64(dout)
     qo = np.ascontiguousarray(q_offsets, dtype=np.int64)
@@ -112,7 +117,7 @@ def bwd(q, k, v, dout, q_offsets, kv_offsets, *, act, scale: float, g=None,
     rc = lib.gdpa_oracle_bwd(len(qo) - 1, h, d, _ptr(qo), _ptr(ko), _ptr(q), _ptr(k), _ptr(v),
                              _ptr(g), code, float(scale), int(window[0]),
                              int(window[1]), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
-                             int(nthreads), _ptr(heads))
+                             int(nthreads), _ptr(heads), q.shape[0] if shared_q else 0)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     out = {"dq": dq, "dk": dk, "dv": dv}
@@ -125,7 +130,7 @@ def group_fwd(group, nthreads: int = 0, **overrides):
     """Forward on a ``gdpa_workloads.Group`` (inputs widened exactly to float64)."""
     from gdpa_workloads import widen
     s = group.spec
-    kw = dict(act=s.act, scale=s.scale, window=s.window)
+    kw = dict(act=s.act, scale=s.scale, window=s.window, shared_q=getattr(s, "shared_q", False))
     kw.update(overrides)
     return fwd(widen(group.q), widen(group.k), widen(group.v), group.q_offsets, group.kv_offsets,
                g=widen(group.g), nthreads=nthreads, **kw)
@@ -134,7 +139,7 @@ def group_fwd(group, nthreads: int = 0, **overrides):
 def group_bwd(group, nthreads: int = 0, want_dg: bool = False, **overrides):
     from gdpa_workloads import widen
     s = group.spec
-    kw = dict(act=s.act, scale=s.scale, window=s.window)
+    kw = dict(act=s.act, scale=s.scale, window=s.window, shared_q=getattr(s, "shared_q", False))
     kw.update(overrides)
     return bwd(widen(group.q), widen(group.k), widen(group.v), widen(group.dout), group.q_offsets,
                group.kv_offsets, g=widen(group.g), want_dg=want_dg, nthreads=nthreads, **kw)

@@ -30,6 +30,10 @@
 // Layouts: q, o, dout, dq are [total_q, H, d]; k, v, dk, dv are [total_kv, H, d]; g, dg are
 // [total_kv, H]; lse is [total_q, H]; all row-major float64. Offsets are int64 [B+1]. The
 // position of query row i and key row j inside their sequence (0-based) defines the window.
+//
+// Shared queries (PMA-style pooling: one learnable query matrix attends over every sequence;
+// review, sections 2.3-2.4): q and dq are then [S, H, d] and query row i of every sequence is
+// row i of q, so that o_bi uses q_i and dq_i = sum over sequences b of the gradient through o_bi.
 
 #include <atomic>
 #include <cmath>
@@ -82,7 +86,14 @@ struct Problem {
   double scale;
   int wl, wr;  // window sides, -1 = unbounded
   const int* head_acts;  // activation of each head, or NULL: every head uses act
+  int shared_q;          // S > 0: one [S, H, d] query matrix for every sequence; 0: per sequence
 };
+
+// Query row i of sequence b, head h.
+const double* query_row(const Problem& p, int b, int64_t i, int h) {
+  const int64_t row = (p.shared_q > 0 ? 0 : p.q_off[b]) + i;
+  return p.q + (row * p.H + h) * p.d;
+}
 
 // Activation of head h (heads may each use their own; review section 2.3 lets phi vary by head).
 int act_of(const Problem& p, int h) { return p.head_acts ? p.head_acts[h] : p.act; }
@@ -107,8 +118,8 @@ double dot(const double* x, const double* y, int n) {
 double score_row(const Problem& p, int b, int h, int64_t i, int64_t lo, int64_t hi,
                  std::vector<double>& s, std::vector<double>& pr) {
   const int H = p.H, d = p.d;
-  const int64_t q0 = p.q_off[b], k0 = p.kv_off[b];
-  const double* qi = p.q + ((q0 + i) * H + h) * d;
+  const int64_t k0 = p.kv_off[b];
+  const double* qi = query_row(p, b, i, h);
   int64_t n = hi - lo + 1;
   s.assign(n > 0 ? n : 0, 0.0);
   pr.assign(n > 0 ? n : 0, 0.0);
@@ -151,8 +162,9 @@ void fwd_item(const Problem& p, int b, int h, double* o, double* lse) {
   }
 }
 
-void bwd_item(const Problem& p, int b, int h, const double* dout, double* dq, double* dk,
-              double* dv, double* dg) {
+// dq receives the gradient of query row i at ((dq_row0 + i) * H + h) * d.
+void bwd_item(const Problem& p, int b, int h, const double* dout, double* dq, int64_t dq_row0,
+              double* dk, double* dv, double* dg) {
   const int H = p.H, d = p.d;
   const int64_t q0 = p.q_off[b], lq = p.q_off[b + 1] - q0;
   const int64_t k0 = p.kv_off[b], lk = p.kv_off[b + 1] - k0;
@@ -168,7 +180,7 @@ void bwd_item(const Problem& p, int b, int h, const double* dout, double* dq, do
     allowed_range(p, i, lk, &lo, &hi);
     score_row(p, b, h, i, lo, hi, s, pr);
     const int64_t n = hi >= lo ? hi - lo + 1 : 0;
-    const double* qi = p.q + ((q0 + i) * H + h) * d;
+    const double* qi = query_row(p, b, i, h);
     const double* doi = dout + ((q0 + i) * H + h) * d;
     dp.assign(n, 0.0);
     ds.assign(n, 0.0);
@@ -181,7 +193,7 @@ void bwd_item(const Problem& p, int b, int h, const double* dout, double* dq, do
     } else {
       for (int64_t t = 0; t < n; ++t) ds[t] = dp[t] * phi_grad(act, s[t]);
     }
-    double* dqi = dq + ((q0 + i) * H + h) * d;
+    double* dqi = dq + ((dq_row0 + i) * H + h) * d;
     for (int c = 0; c < d; ++c) dqi[c] = 0.0;
     for (int64_t j = lo; j <= hi; ++j) {
       const double* kj = p.k + ((k0 + j) * H + h) * d;
@@ -209,6 +221,10 @@ bool valid(const Problem& p) {
   if (p.q_off[0] != 0 || p.kv_off[0] != 0) return false;
   for (int b = 0; b < p.B; ++b)
     if (p.q_off[b + 1] < p.q_off[b] || p.kv_off[b + 1] < p.kv_off[b]) return false;
+  if (p.shared_q < 0) return false;
+  if (p.shared_q > 0)
+    for (int b = 0; b < p.B; ++b)
+      if (p.q_off[b + 1] - p.q_off[b] > p.shared_q) return false;
   return true;
 }
 
@@ -238,13 +254,14 @@ double gdpa_oracle_phi_grad(int act, double x) { return phi_grad(act, x); }
 double gdpa_oracle_log_sigmoid(double x) { return log_sigmoid(x); }
 
 // Forward. g may be NULL (no gate). lse may be NULL; it is written for the softmax heads.
-// head_acts may be NULL (every head uses act) or hold one activation per head.
+// head_acts may be NULL (every head uses act) or hold one activation per head. shared_q > 0:
+// q is one [shared_q, H, d] matrix for every sequence (each sequence has at most shared_q rows).
 // Returns 0, or -1 for invalid arguments (nothing written). nthreads <= 0 means all cores.
 int gdpa_oracle_fwd(int B, int H, int d, const int64_t* q_off, const int64_t* kv_off,
                     const double* q, const double* k, const double* v, const double* g, int act,
                     double scale, int window_left, int window_right, double* o, double* lse,
-                    int nthreads, const int* head_acts) {
-  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right, head_acts};
+                    int nthreads, const int* head_acts, int shared_q) {
+  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right, head_acts, shared_q};
   if (!valid(p)) return -1;
   if (p.q_off[B] > 0 && (!q || !o)) return -1;
   if (p.kv_off[B] > 0 && (!k || !v)) return -1;
@@ -253,17 +270,32 @@ int gdpa_oracle_fwd(int B, int H, int d, const int64_t* q_off, const int64_t* kv
 }
 
 // Backward: gradients of sum(dout * o) with respect to q, k, v (and G when dg != NULL).
+// With shared queries, dq is [shared_q, H, d]: each sequence's query gradients are formed apart,
+// then added over the sequences.
 int gdpa_oracle_bwd(int B, int H, int d, const int64_t* q_off, const int64_t* kv_off,
                     const double* q, const double* k, const double* v, const double* g, int act,
                     double scale, int window_left, int window_right, const double* dout,
                     double* dq, double* dk, double* dv, double* dg, int nthreads,
-                    const int* head_acts) {
-  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right, head_acts};
+                    const int* head_acts, int shared_q) {
+  Problem p{B, H, d, q_off, kv_off, q, k, v, g, act, scale, window_left, window_right, head_acts, shared_q};
   if (!valid(p)) return -1;
   if (dg && !g) return -1;
-  if (p.q_off[B] > 0 && (!q || !dout || !dq)) return -1;
+  if ((p.q_off[B] > 0 || shared_q > 0) && (!q || !dq)) return -1;
+  if (p.q_off[B] > 0 && !dout) return -1;
   if (p.kv_off[B] > 0 && (!k || !v || !dk || !dv)) return -1;
-  parallel_items(B, H, nthreads, [&](int b, int h) { bwd_item(p, b, h, dout, dq, dk, dv, dg); });
+  if (shared_q == 0) {
+    parallel_items(B, H, nthreads, [&](int b, int h) { bwd_item(p, b, h, dout, dq, p.q_off[b], dk, dv, dg); });
+    return 0;
+  }
+  // per-sequence query gradients: rows [b * S, b * S + L_b) of part
+  const int64_t S = shared_q;
+  std::vector<double> part((size_t)B * S * H * d, 0.0);
+  parallel_items(B, H, nthreads, [&](int b, int h) { bwd_item(p, b, h, dout, part.data(), b * S, dk, dv, dg); });
+  for (int64_t x = 0; x < S * H * d; ++x) {
+    double acc = 0.0;
+    for (int b = 0; b < B; ++b) acc += part[(size_t)b * S * H * d + x];
+    dq[x] = acc;
+  }
   return 0;
 }
 

@@ -26,7 +26,8 @@ def device_group(grp, dev="cuda:0"):
     v = grp.v.to(dev)
     g = None if grp.g is None else grp.g.to(dev)
     return ga.make_group(q, k, v, grp.q_offsets, grp.kv_offsets, act=s.act, scale=s.scale, window=s.window, g=g,
-                         self_attention=s.keys_per_seq is None, lengths_q=grp.lengths_q.tolist(),
+                         self_attention=s.keys_per_seq is None and not s.shared_q, shared_q=s.shared_q,
+                         lengths_q=grp.lengths_q.tolist(),
                          lengths_kv=grp.lengths_kv.tolist())
 
 

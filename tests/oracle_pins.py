@@ -36,12 +36,13 @@ def offsets(lengths):
     return o
 
 
-def rand_problem(seed, lq, lk=None, h=2, d=8, std=1.0, gate=False):
-    """Small jagged problem with float64 entries; lk=None means self-attention (lk = lq)."""
+def rand_problem(seed, lq, lk=None, h=2, d=8, std=1.0, gate=False, shared_rows=0):
+    """Small jagged problem with float64 entries; lk=None means self-attention (lk = lq).
+    shared_rows > 0: q is one [shared_rows, h, d] query matrix shared by every sequence."""
     rng = np.random.default_rng(seed)
     lk = lq if lk is None else lk
     tq, tk = int(sum(lq)), int(sum(lk))
-    q = rng.standard_normal((tq, h, d)) * std
+    q = rng.standard_normal((shared_rows if shared_rows else tq, h, d)) * std
     k = rng.standard_normal((tk, h, d)) * std
     v = rng.standard_normal((tk, h, d))
     g = rng.standard_normal((tk, h)) * 2.0 if gate else None
@@ -61,13 +62,15 @@ def _mask(lq, lk, window):
     return m
 
 
-def torch_reference(pb, act, scale, window=(-1, -1), need_grad=False):
+def torch_reference(pb, act, scale, window=(-1, -1), need_grad=False, shared=False):
     """Per (sequence, head) dense evaluation with torch library routines in float64.
 
     Element-wise form: act(scale * Q_h K_h^T) V_h with masked entries dropped (the PFFN product
     with W1 = K_h^T, W2 = V_h). Softmax form: scaled_dot_product_attention with an additive
-    float mask log sigmoid(G) (and -inf outside the window). act may list one form per head."""
-    tq, h, d = pb["q"].shape
+    float mask log sigmoid(G) (and -inf outside the window). act may list one form per head.
+    shared: every sequence takes its query rows from the top of the one query matrix; autograd
+    then sums that matrix's gradient over the sequences."""
+    _, h, d = pb["q"].shape
     q = torch.tensor(pb["q"], requires_grad=need_grad)
     k = torch.tensor(pb["k"], requires_grad=need_grad)
     v = torch.tensor(pb["v"], requires_grad=need_grad)
@@ -79,7 +82,7 @@ def torch_reference(pb, act, scale, window=(-1, -1), need_grad=False):
         m = _mask(q1 - q0, k1 - k0, window)
         heads = []
         for hh in range(h):
-            Q = q[q0:q1, hh]
+            Q = q[0:q1 - q0, hh] if shared else q[q0:q1, hh]
             K = k[k0:k1, hh]
             V = v[k0:k1, hh]
             act_h = act if isinstance(act, str) else act[hh]
@@ -159,6 +162,21 @@ def check_backward_vs_autograd(orc, act, scale, window=(-1, -1), gate=False, see
     ref = torch_reference(pb, act, scale, window, need_grad=True)
     for name in ("dq", "dk", "dv") + (("dg",) if gate else ()):
         close(r[name], ref[name], rtol=1e-10, atol=1e-12, what=f"bwd {name} {act} {window}")
+
+
+def check_shared_queries(orc, act, scale, gate=False, seed=5):
+    """One query matrix (6 rows) attending over five jagged sequences of keys: forward and all
+    gradients against torch autograd, which sums the shared matrix's gradient by itself."""
+    lq = [5, 0, 3, 5, 1]
+    lk = [7, 4, 0, 9, 2]
+    pb = rand_problem(seed, lq, lk, gate=gate, shared_rows=6)
+    r = orc.fwd(pb["q"], pb["k"], pb["v"], pb["qo"], pb["ko"], act=act, scale=scale, g=pb["g"], shared_q=True)
+    rb = orc.bwd(pb["q"], pb["k"], pb["v"], pb["do"], pb["qo"], pb["ko"], act=act, scale=scale, g=pb["g"],
+                 want_dg=gate, shared_q=True)
+    ref = torch_reference(pb, act, scale, need_grad=True, shared=True)
+    close(r["o"], ref["o"], what=f"shared-query fwd {act}")
+    for name in ("dq", "dk", "dv") + (("dg",) if gate else ()):
+        close(rb[name], ref[name], rtol=1e-10, atol=1e-12, what=f"shared-query bwd {name} {act}")
 
 
 def check_finite_differences(orc, act, scale, window=(-1, -1), gate=False, seed=2, self_attn=True):
@@ -319,4 +337,6 @@ FAST_CHECKS = [
     ("gate inf is sdpa", lambda o: check_gate_infinity_is_sdpa(o)),
     ("window covering sequence", lambda o: check_window_covering_sequence_is_full(o)),
     ("invariants", lambda o: check_invariants(o)),
+    ("shared queries softmax gated", lambda o: check_shared_queries(o, "softmax", 0.6, gate=True)),
+    ("shared queries silu", lambda o: check_shared_queries(o, "silu", 0.9)),
 ]

@@ -101,6 +101,27 @@ def test_workspace_size(lib):
     assert _lib.gdpa_workspace_size([good_problem()], 2) == 0
 
 
+def test_workspace_size_key_chunks(lib):
+    """Backward workspace grows by the fp32 dQ rows (and softmax row terms) exactly when some
+    sequence may have more keys than a workgroup holds, or the queries are shared."""
+    base = _lib.gdpa_workspace_size([good_problem()], 1)
+    long_kv = good_problem(max_seqlen_kv=600, total_kv=1200)
+    n = _lib.gdpa_workspace_size([long_kv], 1)
+    assert n - base >= 100 * 4 * 64 * 4  # total_q x H x d floats
+    assert _lib.gdpa_workspace_size([long_kv], 0) == _lib.gdpa_workspace_size([good_problem()], 0)
+    sm = _lib.gdpa_workspace_size([good_problem(max_seqlen_kv=600, total_kv=1200, act=_lib.GDPA_ACT_SOFTMAX)], 1)
+    assert sm - n >= 100 * 4 * 4  # plus D_i per (row, head)
+    shared = good_problem(flags=_lib.GDPA_FLAG_SHARED_Q, max_seqlen_q=64)
+    assert _lib.gdpa_workspace_size([shared], 1) - base >= 2 * 64 * 4 * 64 * 4  # B x S x H x d floats
+    # a causal window narrow enough for the resident ring needs no chunk rows
+    ring = good_problem(self_attention=1, total_q=1200, total_kv=1200, max_seqlen_q=600, max_seqlen_kv=600,
+                        window_left=127, window_right=0)
+    assert _lib.gdpa_workspace_size([ring], 1) == base
+    wide = good_problem(self_attention=1, total_q=1200, total_kv=1200, max_seqlen_q=600, max_seqlen_kv=600,
+                        window_left=300, window_right=0)
+    assert _lib.gdpa_workspace_size([wide], 1) - base >= 1200 * 4 * 64 * 4
+
+
 INVALID_PROBLEMS = [
     ("negative seqs", dict(num_seqs=-1), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("zero heads", dict(num_heads=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
@@ -110,11 +131,13 @@ INVALID_PROBLEMS = [
     ("nan scale", dict(scale=float("nan")), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window below -1", dict(window_left=-2), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window on cross-attention", dict(window_left=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
-    ("unknown flag", dict(flags=2), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("unknown flag", dict(flags=4), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("shared queries in self-attention", dict(flags=_lib.GDPA_FLAG_SHARED_Q, self_attention=1, total_kv=100,
+                                              max_seqlen_kv=60), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("shared queries in fp32", dict(flags=_lib.GDPA_FLAG_SHARED_Q, dtype=_lib.GDPA_DTYPE_FP32), _lib.GDPA_ERR_UNSUPPORTED),
     ("null offsets", dict(q_offsets=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("max len above total", dict(max_seqlen_q=101), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("self-attention with unequal totals", dict(self_attention=1), _lib.GDPA_ERR_INVALID_ARGUMENT),
-    ("too many keys for bf16", dict(max_seqlen_kv=257, total_kv=600), _lib.GDPA_ERR_UNSUPPORTED),
 ]
 
 
@@ -162,18 +185,16 @@ def test_workspace_checks(lib):
         assert fn(good_problem(), good_tensors(), FAKE * 16, 16, 0) == _lib.GDPA_ERR_WORKSPACE
 
 
-def test_window_capacity_rules(lib):
-    # bounded causal window on long self-attention sequences is supported (d=64: left+right <= 128)
-    p = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000, max_seqlen_kv=2000,
-                     window_left=127, window_right=0, act=_lib.GDPA_ACT_SOFTMAX)
-    assert _lib.gdpa_workspace_size([p], 0) > 0
-    assert _lib.gdpa_workspace_size([p], 1) > 0
-    wide = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000, max_seqlen_kv=2000,
-                        window_left=200, window_right=0)
-    assert _lib.gdpa_workspace_size([wide], 0) == 0
-    unbounded = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000,
-                             max_seqlen_kv=2000, window_left=-1, window_right=0)
-    assert _lib.gdpa_workspace_size([unbounded], 0) == 0
+def test_any_key_length_accepted(lib):
+    # every window and key length is accepted: a narrow window streams keys through the resident
+    # ring; wider windows and unbounded long key ranges run in key chunks
+    for wl, wr in ((127, 0), (200, 0), (-1, 0), (-1, -1), (300, 300)):
+        p = good_problem(self_attention=1, total_q=5000, total_kv=5000, max_seqlen_q=2000, max_seqlen_kv=2000,
+                         window_left=wl, window_right=wr, act=_lib.GDPA_ACT_SOFTMAX)
+        assert _lib.gdpa_workspace_size([p], 0) > 0
+        assert _lib.gdpa_workspace_size([p], 1) > 0
+    cross = good_problem(total_kv=50000, max_seqlen_kv=30000)
+    assert _lib.gdpa_workspace_size([cross], 1) > 0
 
 
 def test_grouped_requires_same_dtype(lib):

@@ -31,8 +31,10 @@ MUTANTS = [
      "if (p.wl >= 0 && i - p.wl - 1 > a) a = i - p.wl - 1;"),
     ("window right ignored", "if (p.wr >= 0 && i + p.wr < b) b = i + p.wr;", ""),
     ("lse without log", "return m + std::log(l);", "return m + l;"),
-    ("query row of the key sequence", "const double* qi = p.q + ((q0 + i) * H + h) * d;\n  int64_t n",
-     "const double* qi = p.q + ((k0 + i) * H + h) * d;\n  int64_t n"),
+    ("query row of the key sequence", "(p.shared_q > 0 ? 0 : p.q_off[b]) + i;",
+     "(p.shared_q > 0 ? 0 : p.kv_off[b]) + i;"),
+    ("shared query rows shifted", "(p.shared_q > 0 ? 0 : p.q_off[b]) + i;", "(p.shared_q > 0 ? 1 : p.q_off[b]) + i;"),
+    ("shared query gradient not summed", "acc += part[", "acc = part["),
     ("head index swapped", "double sij = p.scale * dot(qi, kj, d);",
      "double sij = p.scale * dot(qi, p.k + ((k0 + j) * H + (H - 1 - h)) * d, d);"),
     ("dg missing sigmoid", "+= sigmoid(-p.g[(k0 + j) * H + h]) * dsij", "+= dsij"),

@@ -85,7 +85,12 @@ def compare_workload(w, passes, sample=None, want_dg=True, scale=None):
         if bwd_outs is not None:
             rb = oracle.group_bwd(sub, want_dg=want_dg and g.g is not None)
             gb = bwd_outs[gi]
-            report[f"g{gi}.dq"] = chk(dt, to64(gb["dq"])[qr], rb["dq"], f"{w.name} g{gi} dQ")
+            if g.spec.shared_q:
+                # the shared query matrix's gradient sums over every sequence: compare it whole
+                assert sample is None, "shared-query dQ needs every sequence"
+                report[f"g{gi}.dq"] = chk(dt, to64(gb["dq"]), rb["dq"], f"{w.name} g{gi} dQ (shared)")
+            else:
+                report[f"g{gi}.dq"] = chk(dt, to64(gb["dq"])[qr], rb["dq"], f"{w.name} g{gi} dQ")
             report[f"g{gi}.dk"] = chk(dt, to64(gb["dk"])[kr], rb["dk"], f"{w.name} g{gi} dK")
             report[f"g{gi}.dv"] = chk(dt, to64(gb["dv"])[kr], rb["dv"], f"{w.name} g{gi} dV")
             if "dg" in gb:
@@ -260,6 +265,42 @@ def test_per_head_activation_pffn():
     acts = ("silu", "gelu", "softmax", "silu")
     w = make_workload("pffn_train", 9, num_seqs=6, len_range=(1, 300), act=acts, scale=0.125)
     compare_workload(w, ("fwd", "bwd"))
+
+
+# ------------------------------------------------------------------------------------------------
+# Long key ranges (more keys than one workgroup holds: key chunks in both passes)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("keys,act", [(600, "silu"), (1000, "softmax"), (257, "gelu")])
+def test_long_keys_pffn(keys, act):
+    w = make_workload("pffn_train", 10, num_seqs=4, len_range=(1, 300), keys=keys, act=act, scale=0.125)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu"])
+@pytest.mark.parametrize("window", [(-1, 0), (300, 0), (-1, -1), (200, 200)])
+def test_long_keys_self_attention(window, act):
+    w = make_workload("causal_gated", 11, lengths=[1, 300, 700, 257, 0, 520], act=act, window=window)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+# ------------------------------------------------------------------------------------------------
+# Shared seed queries (PMA / hierarchical seed pooling form)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_seed_pool_reduced(seed):
+    compare_workload(make_workload("seed_pool", seed, num_seqs=6, len_range=(1, 900)), ("fwd", "bwd"))
+
+
+@pytest.mark.parametrize("act,seeds", [("silu", 100), ("softmax", 33), ("gelu", 256)])
+def test_seed_pool_edge_lengths(act, seeds):
+    w = make_workload("seed_pool", 3, lengths=[0, 1, 255, 256, 257, 512, 513], act=act, seeds=seeds)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+def test_seed_pool_full_size():
+    compare_workload(make_workload("seed_pool", 0), ("fwd", "bwd"))
 
 
 def test_per_head_activation_fp32():
