@@ -25,8 +25,11 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["gdpa_device.hpp", "gdpa_fwd.hip", "gdpa_bwd.hpp", "gdpa_bwd.hip", "gdpa_bwd_agpr.hip",
-                  "gdpa_sched.hip", "gdpa_api.cpp", "gdpa_launch.hpp"]
+# Sources of each main kernel: the HBM-traffic counters of a kernel stay valid while these hash alike.
+KERNEL_SOURCES = {
+    "fwd": ["gdpa_device.hpp", "gdpa_launch.hpp", "gdpa_fwd.hip"],
+    "bwd": ["gdpa_device.hpp", "gdpa_launch.hpp", "gdpa_bwd.hpp", "gdpa_bwd.hip", "gdpa_bwd_agpr.hip"],
+}
 
 WORKLOAD_TEXT = {
     "pffn_fwd": "PFFN-form GDPA bf16 forward: B=256, L~U[100,1000], H=4, d=64, n=256 context-generated "
@@ -43,9 +46,9 @@ WORKLOAD_TEXT = {
 }
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "generalized_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -60,7 +63,7 @@ def load_traffic(workload: str, kernel: str):
     except (OSError, ValueError):
         return None
     e = t.get(workload, {}).get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
