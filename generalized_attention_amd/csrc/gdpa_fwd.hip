@@ -17,9 +17,11 @@
 //     of O^T = V^T P^T (A = V^T rows from LDS), so P never leaves registers.
 //   * Epilogue: each lane holds 16 consecutive d of one row of O: two 16-byte stores.
 // Short key ranges (personalized-FFN form: n keys per sample) are staged once and the waves sweep
-// all query tiles of the sequence. Longer ranges are swept in row groups of 128 rows: the group's
-// keys (under a window only [r0 - left, r0 + 128 + right)) pass through LDS in chunks, with the
-// O accumulators and the online-softmax state carried across chunks in registers.
+// all query tiles of the sequence. A bounded window over a longer sequence keeps a ring of key
+// blocks in LDS: each group of 128 rows stages only the blocks entering its key range
+// [r0 - left, r0 + 128 + right). Other long ranges are swept in row groups of 128 rows whose keys
+// pass through LDS in chunks, with the O accumulators and the online-softmax state
+// carried across chunks in registers.
 #include "gdpa_device.hpp"
 #include "gdpa_launch.hpp"
 
@@ -55,10 +57,11 @@ __device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
 // memory latency. K rows are copied as 16-byte chunks; V is transposed in units of 4 consecutive
 // keys x 8 d: the 4 keys of one d are adjacent in the V^T slot order, so each d is one 8-byte
 // write.
+// The keys land at LDS key positions dst + (0 .. span_pad-1) (dst a multiple of 32).
 // SERIAL: keep the rounds in order (the caller holds accumulators in registers across the staging).
 template <int D, int NT, bool SERIAL = false>
 __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
-                         int span, int span_pad, bool softmax) {
+                         int span, int span_pad, bool softmax, int dst = 0) {
   using G = FwdGeo<D>;
   constexpr int CPR = D / 8;                                  // 16-byte chunks per row
   constexpr int KI = (G::NKV * CPR + NT - 1) / NT;           // K chunks per thread (at most)
@@ -100,14 +103,14 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
     for (int i = 0; i < KR; ++i) {
       const int idx = threadIdx.x + (round * KR + i) * NT;
       const int r = idx / CPR, c = idx % CPR;
-      if (idx < span_pad * CPR) *reinterpret_cast<u32x4*>(lds + r * G::KROW + c * 16) = kbuf[i];
+      if (idx < span_pad * CPR) *reinterpret_cast<u32x4*>(lds + (dst + r) * G::KROW + c * 16) = kbuf[i];
     }
 #pragma unroll
     for (int i = 0; i < VR; ++i) {
       const int u = threadIdx.x + (round * VR + i) * NT;
       const int r4 = (u / CPR) * 4, c = u % CPR;
       if (u < span_pad / 4 * CPR) {
-        char* vt = lds + G::OFF_V + vt_pos(r4) * 2;
+        char* vt = lds + G::OFF_V + (dst + vt_pos(r4)) * 2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           // d = 8c + e of keys r4 .. r4+3: 16-bit half (e & 1) of word e / 2 of each key's chunk
@@ -128,7 +131,7 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
 #pragma unroll
     for (int round = 0; round < ROUNDS; ++round) stage_round(round);
   }
-  float* gl = reinterpret_cast<float*>(lds + G::OFF_G);
+  float* gl = reinterpret_cast<float*>(lds + G::OFF_G) + dst;
 #pragma unroll
   for (int i = 0; i < GI; ++i) {
     const int r = threadIdx.x + i * NT;
@@ -201,12 +204,13 @@ __device__ __forceinline__ void acc_init(FwdAcc<D, QS>& a) {
   }
 }
 
-// Adds the staged key blocks [kb0, kb1) to the wave's tile state.
+// Adds key blocks [kb0, kb1) to the wave's tile state. Block b holds keys kbase + 32 b + (0..31)
+// (keys from kend on are invalid) and sits in LDS block slot b, or b mod NKV / 32 (RING).
 // GATED: the problem has a gate. MASKED: entries may need an explicit mask (the softmax form, or
 // a window); without it, keys past the end meet zero K and V rows in LDS and phi(0) = 0.
-template <int D, int ACT, int QS, bool GATED, bool MASKED>
+template <int D, int ACT, int QS, bool GATED, bool MASKED, bool RING = false>
 __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf,
-                                               FwdAcc<D, QS>& acc, int row0, int klo, int span, int kb0,
+                                               FwdAcc<D, QS>& acc, int row0, int kbase, int kend, int kb0,
                                                int kb1) {
   using G = FwdGeo<D>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
@@ -217,27 +221,29 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
   auto& lsum = acc.lsum;
   const float sc = softmax ? gd.scale * kLog2e : gd.scale;
   const int wl = gd.wl, wr = gd.wr;
+  constexpr int smask = RING ? G::NKV / 32 - 1 : -1;  // block -> LDS slot
   // element-wise forms: without a gate p' = s g(scale s) = phi(scale s) / scale and O is scaled
   // once in the epilogue; with a gate the argument scale s + log sigmoid(G) is formed first.
   float c1 = 0.0f, c3 = 0.0f;
   if constexpr (!softmax) PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
 
   // Element-wise stage and P V for block kb whose scores are in s: register r of lane (qc, g) is
-  // key kb*32 + c_row(r, g), row qs*32 + qc.
+  // key kbase + kb*32 + c_row(r, g), row qs*32 + qc.
   auto process = [&](int kb, const f32x16 (&s)[QS]) {
+    const int slot = kb & smask;  // LDS block slot
     float p[QS][16];
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x;
-        if constexpr (GATED) x = __builtin_fmaf(s[qs][r], sc, gl[kb * 32 + c_row(r, g)]);
+        if constexpr (GATED) x = __builtin_fmaf(s[qs][r], sc, gl[slot * 32 + c_row(r, g)]);
         if constexpr (softmax) p[qs][r] = GATED ? x : s[qs][r] * sc;
         else p[qs][r] = GATED ? PointAct<ACT>::value(x, c1, c3) : PointAct<ACT>::value(s[qs][r], c1, c3);
       }
     if constexpr (MASKED) {
-      bool full_block = (kb * 32 + 32 <= span);
-      const int kfirst = klo + kb * 32, klast = kfirst + 31;
+      const int kfirst = kbase + kb * 32, klast = kfirst + 31;
+      bool full_block = klast < kend;
       const int rfirst = row0, rlast = row0 + QS * 32 - 1;
       if (wl >= 0 && kfirst < rlast - wl) full_block = false;
       if (wr >= 0 && klast > rfirst + wr) full_block = false;
@@ -247,9 +253,8 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
           const int row = row0 + qs * 32 + qc;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kl = kb * 32 + c_row(r, g);
-            const int kpos = klo + kl;
-            const bool ok = (kl < span) & ((wl < 0) | (kpos >= row - wl)) & ((wr < 0) | (kpos <= row + wr));
+            const int kpos = kfirst + c_row(r, g);
+            const bool ok = (kpos < kend) & ((wl < 0) | (kpos >= row - wl)) & ((wr < 0) | (kpos <= row + wr));
             p[qs][r] = ok ? p[qs][r] : (softmax ? -__builtin_inff() : 0.0f);
           }
         }
@@ -293,7 +298,7 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const u32x4 vu = *reinterpret_cast<const u32x4*>(lds + G::OFF_V + (dt * 32 + out_perm(qc)) * G::VROW +
-                                                         (kb * 32 + t * 16 + g * 8) * 2);
+                                                         (slot * 32 + t * 16 + g * 8) * 2);
         const bf16x8 vf = as_bf16x8(vu);
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) o[qs][dt] = mfma32(vf, pf[qs][t], o[qs][dt]);
@@ -305,15 +310,15 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
   // while the vector units evaluate the activation; the loop body has no branches.
   f32x16 sa[QS], sb[QS];
   int kb = kb0;
-  if (kb < kb1) scores_block<D, QS>(lds, qf, kb, sa);
+  if (kb < kb1) scores_block<D, QS>(lds, qf, kb & smask, sa);
   for (; kb + 2 < kb1; kb += 2) {
-    scores_block<D, QS>(lds, qf, kb + 1, sb);
+    scores_block<D, QS>(lds, qf, (kb + 1) & smask, sb);
     process(kb, sa);
-    scores_block<D, QS>(lds, qf, kb + 2, sa);
+    scores_block<D, QS>(lds, qf, (kb + 2) & smask, sa);
     process(kb + 1, sb);
   }
   if (kb + 1 < kb1) {
-    scores_block<D, QS>(lds, qf, kb + 1, sb);
+    scores_block<D, QS>(lds, qf, (kb + 1) & smask, sb);
     process(kb, sa);
     process(kb + 1, sb);
   } else if (kb < kb1) {
@@ -366,12 +371,20 @@ __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, c
                                          float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   FwdAcc<D, QS> acc;
   acc_init(acc);
-  fwd_accumulate<D, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, klo, span, kb0, kb1);
+  fwd_accumulate<D, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, klo, klo + span, kb0, kb1);
   fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
 }
 
-// One work item: all query rows of one (sequence, head).
-template <int D, int NW, int ACT, int QS, bool GATED, bool MASKED>
+// Whether a bounded window's key range for a group of NW * 32 rows fits in the ring of LDS blocks.
+template <int D>
+__device__ __forceinline__ bool fwd_ring_fits(int wl, int wr, int group_rows) {
+  if (wl < 0 || wr < 0) return false;
+  return (group_rows - 1 + wr) / 32 + (wl + 31) / 32 + 1 <= FwdGeo<D>::NKV / 32;
+}
+
+// One work item: all query rows of one (sequence, head). QS: 32-row tiles per wave while the keys
+// are resident or pass through the ring; QL: the same in the key-chunked sweep.
+template <int D, int NW, int ACT, int QS, int QL, bool GATED, bool MASKED>
 __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   using G = FwdGeo<D>;
   const int q0 = gd.q_off[b], L = gd.q_off[b + 1] - q0;
@@ -412,26 +425,69 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       fwd_tile<D, ACT, QS, GATED, MASKED>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       if (kPrefetchQ) qcur = qnext;
     }
-  } else {
-    // long key range: row groups of NW * RW rows; for each, the group's key range (all keys, or
-    // [r0 - left, r0 + NW * RW + right) under a window) is staged in chunks of NKV keys and every
-    // wave carries its tile's O and softmax state across the chunks.
+  } else if (D < 128 && fwd_ring_fits<D>(gd.wl, gd.wr, NW * RW)) {
+    // bounded window over a long sequence: the keys pass through a ring of NKV / 32 LDS blocks
+    // (block b in slot b mod NKV / 32); each group of NW * RW rows stages only the blocks that
+    // enter its key range [r0 - left, r0 + NW * RW + right), so every key is read once
+    constexpr int NSLOT = G::NKV / 32;
+    constexpr bool kHoldQ = D < 128;
+    int staged = 0;  // blocks [.., staged) are in the ring
     for (int r0 = 0; r0 < L; r0 += NW * RW) {
       const int row0 = r0 + w * RW;
       const bool active = row0 < L;
+      QFrags<D, QS> qf;
+      if (kHoldQ && active) load_q<D, QS>(qf, qseq, rs, row0, L);  // in flight during the staging
+      const int glo = r0 - gd.wl > 0 ? r0 - gd.wl : 0;
+      const int ghi = r0 + NW * RW + gd.wr < N ? r0 + NW * RW + gd.wr : N;  // exclusive
+      const int blast = (ghi - 1) / 32;
+      int bnext = glo / 32 > staged ? glo / 32 : staged;
+      if (bnext <= blast) {
+        __syncthreads();  // the slots about to be replaced are no longer read
+        while (bnext <= blast) {
+          const int slot = bnext & (NSLOT - 1);
+          const int nblk = blast - bnext + 1 < NSLOT - slot ? blast - bnext + 1 : NSLOT - slot;
+          const int k0 = bnext * 32;
+          const int span = N - k0 < nblk * 32 ? N - k0 : nblk * 32;
+          stage_kv<D, NW * kWave>(lds, kseq + (size_t)k0 * H * D, vseq + (size_t)k0 * H * D,
+                                           gseq ? gseq + (size_t)k0 * H : nullptr, H, span, nblk * 32, softmax,
+                                           slot * 32);
+          bnext += nblk;
+        }
+        staged = blast + 1;
+        __syncthreads();
+      }
+      if (active) {
+        int lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
+        int hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
+        if (!kHoldQ) load_q<D, QS>(qf, qseq, rs, row0, L);
+        FwdAcc<D, QS> acc;
+        acc_init(acc);
+        if (hi >= lo)
+          fwd_accumulate<D, ACT, QS, GATED, MASKED, true>(lds, gd, qf, acc, row0, 0, N, lo / 32, hi / 32 + 1);
+        fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
+      }
+    }
+  } else {
+    // long key range: row groups of NW * QL * 32 rows; for each, the group's key range (all keys,
+    // or [r0 - left, r0 + rows + right) under a window) is staged in chunks of NKV keys and every
+    // wave carries its tile's O and softmax state across the chunks.
+    constexpr int RL = QL * 32;
+    for (int r0 = 0; r0 < L; r0 += NW * RL) {
+      const int row0 = r0 + w * RL;
+      const bool active = row0 < L;
       int glo = 0, ghi = N;
       if (gd.wl >= 0) glo = r0 - gd.wl > 0 ? r0 - gd.wl : 0;
-      if (gd.wr >= 0 && r0 + NW * RW + gd.wr < N) ghi = r0 + NW * RW + gd.wr;
+      if (gd.wr >= 0 && r0 + NW * RL + gd.wr < N) ghi = r0 + NW * RL + gd.wr;
       // the wave's own key range [lo, hi]
       int lo = 0, hi = N - 1;
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
-      if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
+      if (gd.wr >= 0) hi = row0 + RL - 1 + gd.wr < N - 1 ? row0 + RL - 1 + gd.wr : N - 1;
       // d <= 64: Q stays in registers across the chunks; d = 128 reloads it per chunk (from L2)
       // to keep the register file free for the staging
       constexpr bool kHoldQ = D < 128;
-      QFrags<D, QS> qf;
-      if (kHoldQ && active) load_q<D, QS>(qf, qseq, rs, row0, L);
-      FwdAcc<D, QS> acc;
+      QFrags<D, QL> qf;
+      if (kHoldQ && active) load_q<D, QL>(qf, qseq, rs, row0, L);
+      FwdAcc<D, QL> acc;
       acc_init(acc);
       for (int kc = glo; kc < ghi; kc += G::NKV) {
         const int span = ghi - kc < G::NKV ? ghi - kc : G::NKV;
@@ -442,12 +498,12 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
         const int clo = lo > kc ? lo : kc;
         const int chi = hi < kc + span - 1 ? hi : kc + span - 1;
         if (active && chi >= clo) {
-          if (!kHoldQ) load_q<D, QS>(qf, qseq, rs, row0, L);
-          fwd_accumulate<D, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, kc, span, (clo - kc) / 32,
+          if (!kHoldQ) load_q<D, QL>(qf, qseq, rs, row0, L);
+          fwd_accumulate<D, ACT, QL, GATED, MASKED>(lds, gd, qf, acc, row0, kc, kc + span, (clo - kc) / 32,
                                                     (chi - kc) / 32 + 1);
         }
       }
-      if (active) fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
+      if (active) fwd_finish<D, ACT, QL, GATED>(gd, acc, oseq, lseq, L, row0);
     }
   }
 }
@@ -456,13 +512,14 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
 // without window or softmax runs the mask-free body.
 template <int D, int NW, int ACT, int QS>
 __device__ __forceinline__ void fwd_dispatch_variant(char* lds, const GroupDesc& gd, int b, int h) {
+  constexpr int QL = 1;  // (two tiles per wave in the key-chunked sweep spill registers)
   const bool masked = ACT == GDPA_ACT_SOFTMAX || gd.wl >= 0 || gd.wr >= 0;
   if (gd.g != nullptr) {
-    if (masked) fwd_item<D, NW, ACT, QS, true, true>(lds, gd, b, h);
-    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, true, false>(lds, gd, b, h);
+    if (masked) fwd_item<D, NW, ACT, QS, QL, true, true>(lds, gd, b, h);
+    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, QL, true, false>(lds, gd, b, h);
   } else {
-    if (masked) fwd_item<D, NW, ACT, QS, false, true>(lds, gd, b, h);
-    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, false, false>(lds, gd, b, h);
+    if (masked) fwd_item<D, NW, ACT, QS, QL, false, true>(lds, gd, b, h);
+    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, QL, false, false>(lds, gd, b, h);
   }
 }
 

@@ -278,7 +278,7 @@ def test_long_keys_pffn(keys, act):
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu"])
-@pytest.mark.parametrize("window", [(-1, 0), (300, 0), (-1, -1), (200, 200)])
+@pytest.mark.parametrize("window", [(-1, 0), (300, 0), (-1, -1), (200, 200), (64, 64), (0, 100)])
 def test_long_keys_self_attention(window, act):
     w = make_workload("causal_gated", 11, lengths=[1, 300, 700, 257, 0, 520], act=act, window=window)
     compare_workload(w, ("fwd", "bwd"))
