@@ -72,6 +72,8 @@ constexpr int bwd_lds_bytes() {
 template <int N>
 __device__ inline int pmod(int x) { return ((x % N) + N) % N; }
 
+__device__ inline u32x4 as_u32x4(const bf16x8& b) { return __builtin_bit_cast(u32x4, b); }
+
 // Per-wave state of its owned blocks.
 template <int D>
 struct BwdWave {
@@ -86,27 +88,49 @@ struct BwdWave {
   int cur[G::KB];      // block held in each owned slot (-1: none); uniform
 };
 
-// Take block `blk` into owned slot kb (ring slot s): K/V rows into registers, K^T into the LDS
-// staging area, gate terms; zero the block's accumulators.
-template <int D, int ACT>
-__device__ __forceinline__ void take_block(BwdWave<D>& st, int kb, char* lds, const GroupDesc& gd, const bf16* kseq,
-                           const bf16* vseq, const float* gseq, int blk, int n, int s) {
+// A block's K and V rows (this lane's 8-value pieces) and raw gate between the global loads and
+// their commit into an owned slot.
+template <int D>
+struct TakeRegs {
+  u32x4 k[BwdGeo<D>::KK];
+  u32x4 v[BwdGeo<D>::KK];
+  float graw;
+};
+
+template <int D>
+__device__ __forceinline__ void take_load(TakeRegs<D>& tr, const GroupDesc& gd, const bf16* kseq, const bf16* vseq,
+                                          const float* gseq, int blk, int n) {
   using G = BwdGeo<D>;
   const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)gd.num_heads * D;
   const int key = blk * kBwdKeyBlock + kc;
   const bool ok = key < n;
+#pragma unroll
+  for (int kk = 0; kk < G::KK; ++kk) {
+    tr.k[kk] = u32x4{0u, 0u, 0u, 0u};
+    tr.v[kk] = u32x4{0u, 0u, 0u, 0u};
+    if (ok) {
+      tr.k[kk] = *reinterpret_cast<const u32x4*>(kseq + key * rs + g * (D / 2) + kk * 8);
+      tr.v[kk] = *reinterpret_cast<const u32x4*>(vseq + key * rs + g * (D / 2) + kk * 8);
+    }
+  }
+  tr.graw = (gseq != nullptr && ok) ? gseq[(size_t)key * gd.num_heads] : 0.0f;
+}
+
+// Commit loaded rows into owned slot kb (ring slot s): K/V rows into registers, K^T into the LDS
+// staging area, gate terms; zero the block's accumulators.
+template <int D, int ACT>
+__device__ __forceinline__ void take_commit(BwdWave<D>& st, int kb, char* lds, const TakeRegs<D>& tr, bool gated,
+                                            int s) {
+  using G = BwdGeo<D>;
+  const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
   const int pos = s * kBwdKeyBlock + kc;
 #pragma unroll
   for (int kk = 0; kk < G::KK; ++kk) {
-    u32x4 ku = {0u, 0u, 0u, 0u}, vu = {0u, 0u, 0u, 0u};
-    if (ok) {
-      ku = *reinterpret_cast<const u32x4*>(kseq + key * rs + g * (D / 2) + kk * 8);
-      vu = *reinterpret_cast<const u32x4*>(vseq + key * rs + g * (D / 2) + kk * 8);
-    }
+    const u32x4 ku = tr.k[kk];
     st.kreg[kb][kk] = as_bf16x8(ku);
-    st.vreg[kb][kk] = as_bf16x8(vu);
-    // K^T staging: this lane's 8 d values of `key` (d = g*D/2 + kk*8 + e), keys in ring order
+    st.vreg[kb][kk] = as_bf16x8(tr.v[kk]);
+    // K^T staging: this lane's 8 d values of its key (d = g*D/2 + kk*8 + e), keys in ring order
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int d0 = g * (D / 2) + kk * 8 + 2 * e;
@@ -114,14 +138,13 @@ __device__ __forceinline__ void take_block(BwdWave<D>& st, int kb, char* lds, co
       *reinterpret_cast<uint16_t*>(lds + G::OFF_KT + (d0 + 1) * G::KTROW + pos * 2) = (uint16_t)(ku[e] >> 16);
     }
   }
-  float t = 0.0f, gr = 0.0f;
-  if (gseq != nullptr && ok) {
-    gr = gseq[(size_t)key * gd.num_heads];
-    t = log_sigmoid_f(gr);
+  float t = 0.0f;
+  if (gated) {
+    t = log_sigmoid_f(tr.graw);
     if (ACT == GDPA_ACT_SOFTMAX) t *= kLog2e;
   }
   st.gate[kb] = t;
-  st.graw[kb] = gr;
+  st.graw[kb] = tr.graw;
   st.dgs[kb] = 0.0f;
   if (g == 0) reinterpret_cast<float*>(lds + G::OFF_GATE)[pos] = t;
 #pragma unroll
@@ -131,35 +154,107 @@ __device__ __forceinline__ void take_block(BwdWave<D>& st, int kb, char* lds, co
   }
 }
 
-// Write dK, dV (and dG) of owned slot kb. Accumulator register r of lane (key, g) in d-tile dt
-// is d = dt*32 + c_row(r, g): four runs of 4 consecutive d per lane.
+// Load block `blk`'s K and V rows straight into owned slot kb's registers (the slot's previous
+// block must no longer be read) and its raw gate into graw_next; take_commit_regs completes it.
 template <int D>
-__device__ __forceinline__ void flush_block(BwdWave<D>& st, int kb, const GroupDesc& gd, bf16* dkseq, bf16* dvseq, float* dgseq,
-                            int n, float dv_scale) {
+__device__ __forceinline__ void take_load_regs(BwdWave<D>& st, int kb, float& graw_next, const GroupDesc& gd,
+                                               const bf16* kseq, const bf16* vseq, const float* gseq, int blk,
+                                               int n) {
   using G = BwdGeo<D>;
   const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)gd.num_heads * D;
-  const int key = st.cur[kb] * kBwdKeyBlock + kc;
+  const int key = blk * kBwdKeyBlock + kc;
+  const bool ok = key < n;
+#pragma unroll
+  for (int kk = 0; kk < G::KK; ++kk) {
+    u32x4 ku = {0u, 0u, 0u, 0u}, vu = {0u, 0u, 0u, 0u};
+    if (ok) {
+      ku = *reinterpret_cast<const u32x4*>(kseq + key * rs + g * (D / 2) + kk * 8);
+      vu = *reinterpret_cast<const u32x4*>(vseq + key * rs + g * (D / 2) + kk * 8);
+    }
+    st.kreg[kb][kk] = as_bf16x8(ku);
+    st.vreg[kb][kk] = as_bf16x8(vu);
+  }
+  graw_next = (gseq != nullptr && ok) ? gseq[(size_t)key * gd.num_heads] : 0.0f;
+}
+
+template <int D, int ACT>
+__device__ __forceinline__ void take_commit_regs(BwdWave<D>& st, int kb, char* lds, float graw, bool gated, int s) {
+  TakeRegs<D> tr;
+#pragma unroll
+  for (int kk = 0; kk < BwdGeo<D>::KK; ++kk) {
+    tr.k[kk] = as_u32x4(st.kreg[kb][kk]);
+    tr.v[kk] = as_u32x4(st.vreg[kb][kk]);
+  }
+  tr.graw = graw;
+  take_commit<D, ACT>(st, kb, lds, tr, gated, s);
+}
+
+// Take block `blk` into owned slot kb (ring slot s).
+template <int D, int ACT>
+__device__ __forceinline__ void take_block(BwdWave<D>& st, int kb, char* lds, const GroupDesc& gd, const bf16* kseq,
+                           const bf16* vseq, const float* gseq, int blk, int n, int s) {
+  TakeRegs<D> tr;
+  take_load<D>(tr, gd, kseq, vseq, gseq, blk, n);
+  take_commit<D, ACT>(st, kb, lds, tr, gseq != nullptr, s);
+}
+
+// dK, dV (and dG) of an owned slot, packed to their output types, between the slot's last
+// accumulation and the stores. Accumulator register r of lane (key, g) in d-tile dt is
+// d = dt*32 + c_row(r, g): four runs of 4 consecutive d per lane.
+template <int D>
+struct FlushRegs {
+  u32x2 k[BwdGeo<D>::DT][4];
+  u32x2 v[BwdGeo<D>::DT][4];
+  float dg;
+  int key;  // sequence-local key of this lane (>= n: nothing to write)
+};
+
+template <int D>
+__device__ __forceinline__ void flush_pack(FlushRegs<D>& fr, const BwdWave<D>& st, int kb, float scale,
+                                           float dv_scale) {
+  using G = BwdGeo<D>;
+  const int lane = lane_id(), kc = lane & 31;
+  fr.key = st.cur[kb] * kBwdKeyBlock + kc;
   const float dgsum = st.dgs[kb] + __shfl_xor(st.dgs[kb], 32);
-  if (key < n) {
+  fr.dg = (1.0f / (1.0f + __expf(st.graw[kb]))) * dgsum;  // sigmoid(-G) * sum_i ds_ij
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      fr.k[dt][a][0] = pack_bf16x2(st.dk[kb][dt][4 * a] * scale, st.dk[kb][dt][4 * a + 1] * scale);
+      fr.k[dt][a][1] = pack_bf16x2(st.dk[kb][dt][4 * a + 2] * scale, st.dk[kb][dt][4 * a + 3] * scale);
+      fr.v[dt][a][0] = pack_bf16x2(st.dv[kb][dt][4 * a] * dv_scale, st.dv[kb][dt][4 * a + 1] * dv_scale);
+      fr.v[dt][a][1] = pack_bf16x2(st.dv[kb][dt][4 * a + 2] * dv_scale, st.dv[kb][dt][4 * a + 3] * dv_scale);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void flush_store(const FlushRegs<D>& fr, const GroupDesc& gd, bf16* dkseq, bf16* dvseq,
+                                            float* dgseq, int n) {
+  using G = BwdGeo<D>;
+  const int g = lane_id() >> 5;
+  const size_t rs = (size_t)gd.num_heads * D;
+  if (fr.key < n) {
 #pragma unroll
     for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d = dt * 32 + a * 8 + g * 4;
-        u32x2 uk, uv;
-        uk[0] = pack_bf16x2(st.dk[kb][dt][4 * a] * gd.scale, st.dk[kb][dt][4 * a + 1] * gd.scale);
-        uk[1] = pack_bf16x2(st.dk[kb][dt][4 * a + 2] * gd.scale, st.dk[kb][dt][4 * a + 3] * gd.scale);
-        uv[0] = pack_bf16x2(st.dv[kb][dt][4 * a] * dv_scale, st.dv[kb][dt][4 * a + 1] * dv_scale);
-        uv[1] = pack_bf16x2(st.dv[kb][dt][4 * a + 2] * dv_scale, st.dv[kb][dt][4 * a + 3] * dv_scale);
-        *reinterpret_cast<u32x2*>(dkseq + key * rs + d) = uk;
-        *reinterpret_cast<u32x2*>(dvseq + key * rs + d) = uv;
+        *reinterpret_cast<u32x2*>(dkseq + fr.key * rs + d) = fr.k[dt][a];
+        *reinterpret_cast<u32x2*>(dvseq + fr.key * rs + d) = fr.v[dt][a];
       }
-    if (dgseq != nullptr && g == 0) {
-      const float sg = 1.0f / (1.0f + __expf(st.graw[kb]));  // sigmoid(-G)
-      dgseq[(size_t)key * gd.num_heads] = sg * dgsum;
-    }
+    if (dgseq != nullptr && g == 0) dgseq[(size_t)fr.key * gd.num_heads] = fr.dg;
   }
+}
+
+// Write dK, dV (and dG) of owned slot kb.
+template <int D>
+__device__ __forceinline__ void flush_block(BwdWave<D>& st, int kb, const GroupDesc& gd, bf16* dkseq, bf16* dvseq, float* dgseq,
+                            int n, float dv_scale) {
+  FlushRegs<D> fr;
+  flush_pack<D>(fr, st, kb, gd.scale, dv_scale);
+  flush_store<D>(fr, gd, dkseq, dvseq, dgseq, n);
 }
 
 // Registers holding the next query tile of Q and dO (and its lse) between the global load and
@@ -374,27 +469,48 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     }
   }
 
-  for (int j = t0; j < t1; ++j) {
-    const int r0 = j * G::QT;
-    // (local) key blocks touched by this query tile
+  // windowed sweep: the rows of a block entering at the next tile are loaded into its slot's
+  // registers at the end of this tile's main pass (before this tile's dQ and dK / dV stores, so
+  // waiting for them never waits for a store); the next tile commits them
+  int pend[KACT];
+  float gnext[KACT];
+#pragma unroll
+  for (int kb = 0; kb < KACT; ++kb) {
+    pend[kb] = -1;
+    gnext[kb] = 0.0f;
+  }
+  // blocks of tile jj: block held by owned slot kb, and whether the tile touches it
+  auto tile_blocks = [&](int jj, int (&bl)[KACT], bool (&ac)[KACT]) {
+    const int rr = jj * G::QT;
     int klo = 0, khi = n - 1;
-    if (wl >= 0 && r0 - wl - kofs > 0) klo = r0 - wl - kofs;
-    if (wr >= 0 && r0 + G::QT - 1 + wr - kofs < n - 1) khi = r0 + G::QT - 1 + wr - kofs;
-    const bool any_keys = klo <= khi;
-    const int kmin = klo / kBwdKeyBlock, kmax = any_keys ? khi / kBwdKeyBlock : -1;
-
-    // ---- 1. take the blocks entering the window (all LDS readers of the previous tile are done)
-    int blk[KACT];
-    bool act[KACT];
+    if (wl >= 0 && rr - wl - kofs > 0) klo = rr - wl - kofs;
+    if (wr >= 0 && rr + G::QT - 1 + wr - kofs < n - 1) khi = rr + G::QT - 1 + wr - kofs;
+    const bool any = klo <= khi;
+    const int kmn = klo / kBwdKeyBlock, kmx = any ? khi / kBwdKeyBlock : -1;
 #pragma unroll
     for (int kb = 0; kb < KACT; ++kb) {
       const int s = kb * G::NW + w;
-      blk[kb] = kmax - pmod<NS>(kmax - s);
-      act[kb] = any_keys && blk[kb] >= kmin && blk[kb] >= 0;
-      if constexpr (WINDOWED) {
-        if (act[kb] && blk[kb] != st.cur[kb]) {
-          if (st.cur[kb] >= 0) flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
-          take_block<D, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, blk[kb], n, s);
+      bl[kb] = kmx - pmod<NS>(kmx - s);
+      ac[kb] = any && bl[kb] >= kmn && bl[kb] >= 0;
+    }
+  };
+
+  for (int j = t0; j < t1; ++j) {
+    const int r0 = j * G::QT;
+    // ---- 1. take the blocks entering the window (all LDS readers of the previous tile are done)
+    int blk[KACT];
+    bool act[KACT];
+    tile_blocks(j, blk, act);
+    if constexpr (WINDOWED) {
+#pragma unroll
+      for (int kb = 0; kb < KACT; ++kb) {
+        if (pend[kb] >= 0) {
+          // rows loaded during the previous tile: K^T staging, gate, fresh accumulators
+          take_commit_regs<D, ACT>(st, kb, lds, gnext[kb], it.gseq != nullptr, kb * G::NW + w);
+          st.cur[kb] = pend[kb];
+          pend[kb] = -1;
+        } else if (act[kb] && blk[kb] != st.cur[kb]) {  // first tile of the sweep
+          take_block<D, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, blk[kb], n, kb * G::NW + w);
           st.cur[kb] = blk[kb];
         }
       }
@@ -405,42 +521,68 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     // forward output). S^T = K Q^T and dP^T = V dO^T put the query on the lane; the waves' partial
     // sums are combined in a fixed order (deterministic).
     if constexpr (softmax && !DSUM) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float part = 0.0f;
-        const int rf = r0 + qs * 32;
-        const int row = rf + lc;
-        bf16x8 qb[G::KK], db[G::KK];
+      // iteration it = (query half qs, owned block kb); the products of it+1 are issued before the
+      // element-wise work of it (the main pass's registers are free here)
+      constexpr int NIT = 2 * KACT;
+      bf16x8 qb[G::KK], db[G::KK];
+      f32x16 st2[2], dp2[2];
+      auto load_b = [&](int qs) {
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
           qb[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_QN + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
           db[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_DON + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
         }
-        const float l2 = lse2[qs * 32 + lc];
+      };
+      auto issue = [&](int kb, int slot) {
+        st2[slot] = f32x16{};
+        dp2[slot] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < KACT; ++kb) {
-          const int kf = blk[kb] * kBwdKeyBlock;
-          const BlockMask bm = block_mask(kofs + kf, rf, kofs + n, L, wl, wr);
-          if (!act[kb] || bm.empty) continue;
+        for (int kk = 0; kk < G::KK; ++kk) {
+          st2[slot] = mfma32(st.kreg[kb][kk], qb[kk], st2[slot]);
+          dp2[slot] = mfma32(st.vreg[kb][kk], db[kk], dp2[slot]);
+        }
+      };
+      load_b(0);
+      issue(0, 0);
+      float part = 0.0f, l2 = lse2[lc];
+#pragma unroll
+      for (int it2 = 0; it2 < NIT; ++it2) {
+        const int qs = it2 / KACT, kb = it2 % KACT, cs = it2 & 1;
+        if (it2 + 1 < NIT) {
+          if ((it2 + 1) / KACT != qs) load_b((it2 + 1) / KACT);
+          issue((it2 + 1) % KACT, cs ^ 1);
+        }
+        const int rf = r0 + qs * 32;
+        const int row = rf + lc;
+        const int kf = blk[kb] * kBwdKeyBlock;
+        const BlockMask bm = block_mask(kofs + kf, rf, kofs + n, L, wl, wr);
+        if (act[kb] && !bm.empty) {
           const int s = kb * G::NW + w;
-          f32x16 st_ = f32x16{}, dpt = f32x16{};
+          if (bm.full) {
 #pragma unroll
-          for (int kk = 0; kk < G::KK; ++kk) {
-            st_ = mfma32(st.kreg[kb][kk], qb[kk], st_);
-            dpt = mfma32(st.vreg[kb][kk], db[kk], dpt);
-          }
+            for (int r = 0; r < 16; ++r) {
+              float x = st2[cs][r] * sc;
+              if constexpr (has_gate) x += gl[s * kBwdKeyBlock + c_row(r, g)];
+              part += fast_exp2(x - l2) * dp2[cs][r];
+            }
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kloc = c_row(r, g);
-            const int key = kofs + kf + kloc;
-            float x = st_[r] * sc;
-            if constexpr (has_gate) x += gl[s * kBwdKeyBlock + kloc];
-            const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
-            part += ok ? fast_exp2(x - l2) * dpt[r] : 0.0f;
+            for (int r = 0; r < 16; ++r) {
+              const int kloc = c_row(r, g);
+              const int key = kofs + kf + kloc;
+              float x = st2[cs][r] * sc;
+              if constexpr (has_gate) x += gl[s * kBwdKeyBlock + kloc];
+              const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+              part += ok ? fast_exp2(x - l2) * dp2[cs][r] : 0.0f;
+            }
           }
         }
-        part += __shfl_xor(part, 32);
-        if (g == 0) dpart[w * G::QT + qs * 32 + lc] = part;
+        if (kb == KACT - 1) {
+          part += __shfl_xor(part, 32);
+          if (g == 0) dpart[w * G::QT + qs * 32 + lc] = part;
+          part = 0.0f;
+          if (qs == 0) l2 = lse2[32 + lc];
+        }
       }
       __syncthreads();
       if constexpr (CHUNK == 2) {
@@ -619,6 +761,25 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       store_qtile<D, softmax, DSUM>(lds, pf);
       if (j + 2 < t1)
         prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
+      if constexpr (WINDOWED) {
+        // blocks entering at the next tile: their rows into the slot registers (the leaving
+        // block's K and V are no longer read), then the leaving blocks' dK, dV, dG go out
+        int bn[KACT];
+        bool an[KACT];
+        tile_blocks(j + 1, bn, an);
+#pragma unroll
+        for (int kb = 0; kb < KACT; ++kb)
+          if (an[kb] && bn[kb] != st.cur[kb]) {
+            take_load_regs<D>(st, kb, gnext[kb], gd, it.kseq, it.vseq, it.gseq, bn[kb], n);
+            pend[kb] = bn[kb];
+          }
+#pragma unroll
+        for (int kb = 0; kb < KACT; ++kb)
+          if (pend[kb] >= 0 && st.cur[kb] >= 0) {
+            flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
+            st.cur[kb] = -1;
+          }
+      }
     }
 
     // ---- 4. dQ^T = K^T dS^T over the ring slots in use (a slot outside the tile holds zero dS);
