@@ -19,7 +19,7 @@ hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStr
   constexpr int kDimAll = kDim32 | kDim64 | kDim128;
   constexpr int kGelu = 1 << GDPA_ACT_GELU, kSilu = 1 << GDPA_ACT_SILU, kSoftmax = 1 << GDPA_ACT_SOFTMAX;
 #define GDPA_LAUNCH(DS, AS) \
-  hipLaunchKernelGGL((bwd_bf16_kernel<DS, AS>), grid, dim3(kBwdWaves * kWave), bwd_lds_bytes<DS>(), stream, d)
+  hipLaunchKernelGGL((bwd_bf16_kernel<DS, AS>), grid, dim3((bwd_waves<DS, AS>() * kWave)), (bwd_lds_bytes<DS, AS>()), stream, d)
 #define GDPA_LAUNCH_DIMS(AS)                            \
   switch (dim_set) {                                    \
     case kDim32: GDPA_LAUNCH(kDim32, AS); break;        \

@@ -1,4 +1,5 @@
-// GDPA backward for bf16 on gfx950: one workgroup (4 waves, one per SIMD) per (sequence, head).
+// GDPA backward for bf16 on gfx950: one workgroup per (sequence, head): 8 waves (two per SIMD) for
+// the element-wise forms at d <= 64, else 4 (one per SIMD).
 //
 //   dp_ij = <dO_i, V_j>;   ds_ij = dp_ij phi'(s_ij)   or   p_ij (dp_ij - D_i), D_i = sum_j p_ij dp_ij
 //   dQ = scale dS K;   dK = scale dS^T Q;   dV = P^T dO;   dG_j = sigmoid(-G_j) sum_i ds_ij
@@ -32,11 +33,14 @@
 
 namespace gdpa {
 
-template <int D>
+// NWAVES waves per workgroup: 4 (one per SIMD; 64 keys per wave, 32 at d = 128) or 8 (two per
+// SIMD, 32 keys each; element-wise forms at d <= 64). Either way the workgroup holds
+// bwd_capacity(D) keys.
+template <int D, int NWAVES>
 struct BwdGeo {
-  static constexpr int NW = kBwdWaves;
+  static constexpr int NW = NWAVES;
   static constexpr int THREADS = NW * kWave;
-  static constexpr int KPW = bwd_keys_per_wave(D);
+  static constexpr int KPW = NW == 8 ? kBwdKeyBlock : bwd_keys_per_wave(D);
   static constexpr int KB = KPW / kBwdKeyBlock;    // blocks per wave
   static constexpr int NB = NW * KB;               // ring slots
   static constexpr int CAP = NB * kBwdKeyBlock;    // resident keys
@@ -60,13 +64,16 @@ struct BwdGeo {
   static constexpr int OFF_GATE = OFF_DPART + NW * QT * 4;  // gate term per ring position [CAP]
   static constexpr int BYTES = OFF_GATE + CAP * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
+  static_assert(CAP == bwd_capacity(D), "resident keys per workgroup");
+  static_assert(NW == 4 || D <= 64, "8 waves only for d <= 64");
 };
 
 constexpr int max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
-template <int DSET>
+template <int DSET, int ASET>
 constexpr int bwd_lds_bytes() {
-  return max3((DSET & kDim32) ? BwdGeo<32>::BYTES : 0, (DSET & kDim64) ? BwdGeo<64>::BYTES : 0,
-              (DSET & kDim128) ? BwdGeo<128>::BYTES : 0);
+  constexpr int NW = bwd_waves<DSET, ASET>();
+  return max3((DSET & kDim32) ? BwdGeo<32, NW>::BYTES : 0, (DSET & kDim64) ? BwdGeo<64, NW>::BYTES : 0,
+              (DSET & kDim128) ? BwdGeo<128, 4>::BYTES : 0);
 }
 
 template <int N>
@@ -75,9 +82,9 @@ __device__ inline int pmod(int x) { return ((x % N) + N) % N; }
 __device__ inline u32x4 as_u32x4(const bf16x8& b) { return __builtin_bit_cast(u32x4, b); }
 
 // Per-wave state of its owned blocks.
-template <int D>
+template <int D, int NW>
 struct BwdWave {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   bf16x8 kreg[G::KB][G::KK];
   bf16x8 vreg[G::KB][G::KK];
   f32x16 dk[G::KB][G::DT];
@@ -90,17 +97,17 @@ struct BwdWave {
 
 // A block's K and V rows (this lane's 8-value pieces) and raw gate between the global loads and
 // their commit into an owned slot.
-template <int D>
+template <int D, int NW>
 struct TakeRegs {
-  u32x4 k[BwdGeo<D>::KK];
-  u32x4 v[BwdGeo<D>::KK];
+  u32x4 k[BwdGeo<D, NW>::KK];
+  u32x4 v[BwdGeo<D, NW>::KK];
   float graw;
 };
 
-template <int D>
-__device__ __forceinline__ void take_load(TakeRegs<D>& tr, const GroupDesc& gd, const bf16* kseq, const bf16* vseq,
+template <int D, int NW>
+__device__ __forceinline__ void take_load(TakeRegs<D, NW>& tr, const GroupDesc& gd, const bf16* kseq, const bf16* vseq,
                                           const float* gseq, int blk, int n) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)gd.num_heads * D;
   const int key = blk * kBwdKeyBlock + kc;
@@ -119,10 +126,10 @@ __device__ __forceinline__ void take_load(TakeRegs<D>& tr, const GroupDesc& gd, 
 
 // Commit loaded rows into owned slot kb (ring slot s): K/V rows into registers, K^T into the LDS
 // staging area, gate terms; zero the block's accumulators.
-template <int D, int ACT>
-__device__ __forceinline__ void take_commit(BwdWave<D>& st, int kb, char* lds, const TakeRegs<D>& tr, bool gated,
+template <int D, int NW, int ACT>
+__device__ __forceinline__ void take_commit(BwdWave<D, NW>& st, int kb, char* lds, const TakeRegs<D, NW>& tr, bool gated,
                                             int s) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
   const int pos = s * kBwdKeyBlock + kc;
 #pragma unroll
@@ -156,11 +163,11 @@ __device__ __forceinline__ void take_commit(BwdWave<D>& st, int kb, char* lds, c
 
 // Load block `blk`'s K and V rows straight into owned slot kb's registers (the slot's previous
 // block must no longer be read) and its raw gate into graw_next; take_commit_regs completes it.
-template <int D>
-__device__ __forceinline__ void take_load_regs(BwdWave<D>& st, int kb, float& graw_next, const GroupDesc& gd,
+template <int D, int NW>
+__device__ __forceinline__ void take_load_regs(BwdWave<D, NW>& st, int kb, float& graw_next, const GroupDesc& gd,
                                                const bf16* kseq, const bf16* vseq, const float* gseq, int blk,
                                                int n) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)gd.num_heads * D;
   const int key = blk * kBwdKeyBlock + kc;
@@ -178,42 +185,42 @@ __device__ __forceinline__ void take_load_regs(BwdWave<D>& st, int kb, float& gr
   graw_next = (gseq != nullptr && ok) ? gseq[(size_t)key * gd.num_heads] : 0.0f;
 }
 
-template <int D, int ACT>
-__device__ __forceinline__ void take_commit_regs(BwdWave<D>& st, int kb, char* lds, float graw, bool gated, int s) {
-  TakeRegs<D> tr;
+template <int D, int NW, int ACT>
+__device__ __forceinline__ void take_commit_regs(BwdWave<D, NW>& st, int kb, char* lds, float graw, bool gated, int s) {
+  TakeRegs<D, NW> tr;
 #pragma unroll
-  for (int kk = 0; kk < BwdGeo<D>::KK; ++kk) {
+  for (int kk = 0; kk < BwdGeo<D, NW>::KK; ++kk) {
     tr.k[kk] = as_u32x4(st.kreg[kb][kk]);
     tr.v[kk] = as_u32x4(st.vreg[kb][kk]);
   }
   tr.graw = graw;
-  take_commit<D, ACT>(st, kb, lds, tr, gated, s);
+  take_commit<D, NW, ACT>(st, kb, lds, tr, gated, s);
 }
 
 // Take block `blk` into owned slot kb (ring slot s).
-template <int D, int ACT>
-__device__ __forceinline__ void take_block(BwdWave<D>& st, int kb, char* lds, const GroupDesc& gd, const bf16* kseq,
+template <int D, int NW, int ACT>
+__device__ __forceinline__ void take_block(BwdWave<D, NW>& st, int kb, char* lds, const GroupDesc& gd, const bf16* kseq,
                            const bf16* vseq, const float* gseq, int blk, int n, int s) {
-  TakeRegs<D> tr;
-  take_load<D>(tr, gd, kseq, vseq, gseq, blk, n);
-  take_commit<D, ACT>(st, kb, lds, tr, gseq != nullptr, s);
+  TakeRegs<D, NW> tr;
+  take_load<D, NW>(tr, gd, kseq, vseq, gseq, blk, n);
+  take_commit<D, NW, ACT>(st, kb, lds, tr, gseq != nullptr, s);
 }
 
 // dK, dV (and dG) of an owned slot, packed to their output types, between the slot's last
 // accumulation and the stores. Accumulator register r of lane (key, g) in d-tile dt is
 // d = dt*32 + c_row(r, g): four runs of 4 consecutive d per lane.
-template <int D>
+template <int D, int NW>
 struct FlushRegs {
-  u32x2 k[BwdGeo<D>::DT][4];
-  u32x2 v[BwdGeo<D>::DT][4];
+  u32x2 k[BwdGeo<D, NW>::DT][4];
+  u32x2 v[BwdGeo<D, NW>::DT][4];
   float dg;
   int key;  // sequence-local key of this lane (>= n: nothing to write)
 };
 
-template <int D>
-__device__ __forceinline__ void flush_pack(FlushRegs<D>& fr, const BwdWave<D>& st, int kb, float scale,
+template <int D, int NW>
+__device__ __forceinline__ void flush_pack(FlushRegs<D, NW>& fr, const BwdWave<D, NW>& st, int kb, float scale,
                                            float dv_scale) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   const int lane = lane_id(), kc = lane & 31;
   fr.key = st.cur[kb] * kBwdKeyBlock + kc;
   const float dgsum = st.dgs[kb] + __shfl_xor(st.dgs[kb], 32);
@@ -229,10 +236,10 @@ __device__ __forceinline__ void flush_pack(FlushRegs<D>& fr, const BwdWave<D>& s
     }
 }
 
-template <int D>
-__device__ __forceinline__ void flush_store(const FlushRegs<D>& fr, const GroupDesc& gd, bf16* dkseq, bf16* dvseq,
+template <int D, int NW>
+__device__ __forceinline__ void flush_store(const FlushRegs<D, NW>& fr, const GroupDesc& gd, bf16* dkseq, bf16* dvseq,
                                             float* dgseq, int n) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   const int g = lane_id() >> 5;
   const size_t rs = (size_t)gd.num_heads * D;
   if (fr.key < n) {
@@ -249,29 +256,29 @@ __device__ __forceinline__ void flush_store(const FlushRegs<D>& fr, const GroupD
 }
 
 // Write dK, dV (and dG) of owned slot kb.
-template <int D>
-__device__ __forceinline__ void flush_block(BwdWave<D>& st, int kb, const GroupDesc& gd, bf16* dkseq, bf16* dvseq, float* dgseq,
+template <int D, int NW>
+__device__ __forceinline__ void flush_block(BwdWave<D, NW>& st, int kb, const GroupDesc& gd, bf16* dkseq, bf16* dvseq, float* dgseq,
                             int n, float dv_scale) {
-  FlushRegs<D> fr;
-  flush_pack<D>(fr, st, kb, gd.scale, dv_scale);
-  flush_store<D>(fr, gd, dkseq, dvseq, dgseq, n);
+  FlushRegs<D, NW> fr;
+  flush_pack<D, NW>(fr, st, kb, gd.scale, dv_scale);
+  flush_store<D, NW>(fr, gd, dkseq, dvseq, dgseq, n);
 }
 
 // Registers holding the next query tile of Q and dO (and its lse) between the global load and
 // the LDS store.
-template <int D>
+template <int D, int NW>
 struct QTileRegs {
-  u32x4 q[BwdGeo<D>::NPF];
-  u32x4 d[BwdGeo<D>::NPF];
+  u32x4 q[BwdGeo<D, NW>::NPF];
+  u32x4 d[BwdGeo<D, NW>::NPF];
   float lse;
   float dsum;  // key-chunked softmax: the row term D_i from the workspace
 };
 
 // DSUM: also load the row term D_i (key-chunked softmax main pass).
-template <int D, bool SOFTMAX, bool DSUM = false>
-__device__ void prefetch_qtile(QTileRegs<D>& pf, const bf16* qseq, const bf16* doseq, const float* lseseq,
+template <int D, int NW, bool SOFTMAX, bool DSUM = false>
+__device__ void prefetch_qtile(QTileRegs<D, NW>& pf, const bf16* qseq, const bf16* doseq, const float* lseseq,
                                size_t rs, int H, int r0, int L, const float* dsumseq = nullptr) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
 #pragma unroll
   for (int i = 0; i < G::NPF; ++i) {
     const int idx = threadIdx.x + i * G::THREADS;
@@ -292,9 +299,9 @@ __device__ void prefetch_qtile(QTileRegs<D>& pf, const bf16* qseq, const bf16* d
   }
 }
 
-template <int D, bool SOFTMAX, bool DSUM = false>
-__device__ void store_qtile(char* lds, const QTileRegs<D>& pf) {
-  using G = BwdGeo<D>;
+template <int D, int NW, bool SOFTMAX, bool DSUM = false>
+__device__ void store_qtile(char* lds, const QTileRegs<D, NW>& pf) {
+  using G = BwdGeo<D, NW>;
 #pragma unroll
   for (int i = 0; i < G::NPF; ++i) {
     const int idx = threadIdx.x + i * G::THREADS;
@@ -396,9 +403,9 @@ __device__ inline void row_chunks(int row, int ntot, int wl, int wr, int kchunk,
 // CHUNK: 0 = the item's keys are all resident; 1 = one chunk of CAP keys starting at it.kofs, dQ
 // accumulated over the chunks in fp32 workspace rows (softmax: D_i read from the workspace);
 // 2 = softmax row-term pass over one chunk: only D_i, accumulated into the workspace.
-template <int D, int ACT, bool GATED, int KACT, bool WINDOWED, int CHUNK = 0>
+template <int D, int NW, int ACT, bool GATED, int KACT, bool WINDOWED, int CHUNK = 0>
 __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const BwdItem& it) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   constexpr int NS = G::NW * KACT;  // ring slots in use
   const int L = it.L, n = it.n, wl = it.wl, wr = it.wr, H = it.H;
   const size_t rs = it.rs;
@@ -415,7 +422,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   const int nkb = (n + kBwdKeyBlock - 1) / kBwdKeyBlock;
   const int t0 = it.t0, t1 = it.t1;
 
-  BwdWave<D> st;
+  BwdWave<D, NW> st;
 #pragma unroll
   for (int kb = 0; kb < G::KB; ++kb) {
     st.cur[kb] = -1;
@@ -451,19 +458,19 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   // K^T staging of slots never taken must hold finite values (they meet zero dS in dQ)
   for (int idx = threadIdx.x; idx < D * (G::KTROW / 16); idx += G::THREADS)
     reinterpret_cast<u32x4*>(lds + G::OFF_KT)[idx] = u32x4{0u, 0u, 0u, 0u};
-  QTileRegs<D> pf;
-  prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, t0 * G::QT, L, it.dsumseq);
+  QTileRegs<D, NW> pf;
+  prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, t0 * G::QT, L, it.dsumseq);
   __syncthreads();  // K^T staging zeroed
-  store_qtile<D, softmax, DSUM>(lds, pf);  // first tile
+  store_qtile<D, NW, softmax, DSUM>(lds, pf);  // first tile
   if (t0 + 1 < t1)
-    prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, (t0 + 1) * G::QT, L, it.dsumseq);
+    prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, (t0 + 1) * G::QT, L, it.dsumseq);
   if constexpr (!WINDOWED) {
     // every block of the sequence is resident for the whole sweep: take them once
 #pragma unroll
     for (int kb = 0; kb < KACT; ++kb) {
       const int s = kb * G::NW + w;
       if (s < nkb) {
-        take_block<D, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, s, n, s);
+        take_block<D, NW, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, s, n, s);
         st.cur[kb] = s;
       }
     }
@@ -506,11 +513,11 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       for (int kb = 0; kb < KACT; ++kb) {
         if (pend[kb] >= 0) {
           // rows loaded during the previous tile: K^T staging, gate, fresh accumulators
-          take_commit_regs<D, ACT>(st, kb, lds, gnext[kb], it.gseq != nullptr, kb * G::NW + w);
+          take_commit_regs<D, NW, ACT>(st, kb, lds, gnext[kb], it.gseq != nullptr, kb * G::NW + w);
           st.cur[kb] = pend[kb];
           pend[kb] = -1;
         } else if (act[kb] && blk[kb] != st.cur[kb]) {  // first tile of the sweep
-          take_block<D, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, blk[kb], n, kb * G::NW + w);
+          take_block<D, NW, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, blk[kb], n, kb * G::NW + w);
           st.cur[kb] = blk[kb];
         }
       }
@@ -628,26 +635,27 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           dpacc[slot] = mfma32(da[kk], st.vreg[kb][kk], dpacc[slot]);
         }
       };
-      load_a(0);
-      issue_sdp(0, 0);
+      // the products of iteration it+1 are issued before the element-wise work of it (the dO^T / Q^T
+      // operands of dV / dK are read only after it, which keeps their registers free meanwhile)
+      constexpr bool PIPE = true;
+      if constexpr (PIPE) {
+        load_a(0);
+        issue_sdp(0, 0);
+      }
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const int qs = it / KACT, kb = it % KACT, cs = it & 1;
-        if (it + 1 < NIT) {
-          if ((it + 1) / KACT != qs) load_a((it + 1) / KACT);
-          issue_sdp((it + 1) % KACT, cs ^ 1);
+        const int qs = it / KACT, kb = it % KACT, cs = PIPE ? (it & 1) : 0;
+        if constexpr (PIPE) {
+          if (it + 1 < NIT) {
+            if ((it + 1) / KACT != qs) load_a((it + 1) / KACT);
+            issue_sdp((it + 1) % KACT, cs ^ 1);
+          }
+        } else {
+          if (kb == 0) load_a(qs);
+          issue_sdp(kb, 0);
         }
         const int rf = r0 + qs * 32;
         if (kb == 0) {
-          // per half: dO^T / Q^T operands of dV^T, dK^T (shared by the owned blocks) and, for
-          // softmax, the rows' lse and D (register group a = rows qs*32 + a*8 + g*4 + 0..3)
-#pragma unroll
-          for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              dota[dt][t] = tr_operand<G::NROW>(lds, G::OFF_DON, qs, t, dt);
-              qta[dt][t] = tr_operand<G::NROW>(lds, G::OFF_QN, qs, t, dt);
-            }
           if constexpr (softmax) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -741,6 +749,15 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           if constexpr (softmax)
             *reinterpret_cast<u32x2*>(lds + G::OFF_SXL + spos + qo) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
         }
+        if (kb == 0) {
+#pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              dota[dt][t] = tr_operand<G::NROW>(lds, G::OFF_DON, qs, t, dt);
+              qta[dt][t] = tr_operand<G::NROW>(lds, G::OFF_QN, qs, t, dt);
+            }
+        }
 #pragma unroll
         for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
@@ -758,9 +775,9 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     if (j + 1 < t1) {
       // next tile into LDS (while dQ runs), then the loads of the one after it: issued before this
       // tile's dQ stores, so waiting for them never waits for those stores
-      store_qtile<D, softmax, DSUM>(lds, pf);
+      store_qtile<D, NW, softmax, DSUM>(lds, pf);
       if (j + 2 < t1)
-        prefetch_qtile<D, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
+        prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
       if constexpr (WINDOWED) {
         // blocks entering at the next tile: their rows into the slot registers (the leaving
         // block's K and V are no longer read), then the leaving blocks' dK, dV, dG go out
@@ -770,13 +787,13 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
 #pragma unroll
         for (int kb = 0; kb < KACT; ++kb)
           if (an[kb] && bn[kb] != st.cur[kb]) {
-            take_load_regs<D>(st, kb, gnext[kb], gd, it.kseq, it.vseq, it.gseq, bn[kb], n);
+            take_load_regs<D, NW>(st, kb, gnext[kb], gd, it.kseq, it.vseq, it.gseq, bn[kb], n);
             pend[kb] = bn[kb];
           }
 #pragma unroll
         for (int kb = 0; kb < KACT; ++kb)
           if (pend[kb] >= 0 && st.cur[kb] >= 0) {
-            flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
+            flush_block<D, NW>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
             st.cur[kb] = -1;
           }
       }
@@ -858,12 +875,12 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   if constexpr (CHUNK != 2)
 #pragma unroll
     for (int kb = 0; kb < KACT; ++kb)
-      if (st.cur[kb] >= 0) flush_block<D>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
+      if (st.cur[kb] >= 0) flush_block<D, NW>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
 }
 
-template <int D, int ACT, bool GATED>
+template <int D, int NW, int ACT, bool GATED>
 __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
-  using G = BwdGeo<D>;
+  using G = BwdGeo<D, NW>;
   BwdItem it;
   const int q0 = gd.q_off[b], k0 = gd.kv_off[b];
   it.L = gd.q_off[b + 1] - q0;
@@ -948,13 +965,13 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
       for (int c = 0; c < nch; ++c) {
         const BwdItem ci = chunk_item(c);
         __syncthreads();  // previous pass done with LDS
-        bwd_sweep<D, ACT, GATED, G::KB, false, 2>(lds, gd, ci);
+        bwd_sweep<D, NW, ACT, GATED, G::KB, false, 2>(lds, gd, ci);
       }
     }
     for (int c = 0; c < nch; ++c) {
       const BwdItem ci = chunk_item(c);
       __syncthreads();
-      bwd_sweep<D, ACT, GATED, G::KB, false, 1>(lds, gd, ci);
+      bwd_sweep<D, NW, ACT, GATED, G::KB, false, 1>(lds, gd, ci);
     }
     return;
   }
@@ -963,32 +980,32 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   // ends are zero), so only the softmax form and windows need explicit masks.
   const bool few_keys = (n + kBwdKeyBlock - 1) / kBwdKeyBlock <= G::NW;
   if (windowed) {
-    if (G::KB > 1 && few_keys) bwd_sweep<D, ACT, GATED, 1, true>(lds, gd, it);
-    else bwd_sweep<D, ACT, GATED, G::KB, true>(lds, gd, it);
+    if (G::KB > 1 && few_keys) bwd_sweep<D, NW, ACT, GATED, 1, true>(lds, gd, it);
+    else bwd_sweep<D, NW, ACT, GATED, G::KB, true>(lds, gd, it);
   } else {
-    if (G::KB > 1 && few_keys) bwd_sweep<D, ACT, GATED, 1, false>(lds, gd, it);
-    else bwd_sweep<D, ACT, GATED, G::KB, false>(lds, gd, it);
+    if (G::KB > 1 && few_keys) bwd_sweep<D, NW, ACT, GATED, 1, false>(lds, gd, it);
+    else bwd_sweep<D, NW, ACT, GATED, G::KB, false>(lds, gd, it);
   }
 }
 
-template <int D, int ACT>
+template <int D, int NW, int ACT>
 __device__ __forceinline__ void bwd_dispatch_gate(char* lds, const GroupDesc& gd, int b, int h) {
-  if (gd.g != nullptr) bwd_item<D, ACT, true>(lds, gd, b, h);
-  else bwd_item<D, ACT, false>(lds, gd, b, h);
+  if (gd.g != nullptr) bwd_item<D, NW, ACT, true>(lds, gd, b, h);
+  else bwd_item<D, NW, ACT, false>(lds, gd, b, h);
 }
 
-template <int D, int ASET>
+template <int D, int NW, int ASET>
 __device__ __forceinline__ void bwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
   if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
-    if (gd.act == GDPA_ACT_GELU) { bwd_dispatch_gate<D, GDPA_ACT_GELU>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_GELU) { bwd_dispatch_gate<D, NW, GDPA_ACT_GELU>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
-    if (gd.act == GDPA_ACT_SILU) { bwd_dispatch_gate<D, GDPA_ACT_SILU>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_SILU) { bwd_dispatch_gate<D, NW, GDPA_ACT_SILU>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
-    if (gd.act == GDPA_ACT_SOFTMAX) bwd_dispatch_gate<D, GDPA_ACT_SOFTMAX>(lds, gd, b, h);
+    if (gd.act == GDPA_ACT_SOFTMAX) bwd_dispatch_gate<D, NW, GDPA_ACT_SOFTMAX>(lds, gd, b, h);
 }
 
 template <int DSET, int ASET>
-__global__ void __launch_bounds__(kBwdWaves * kWave, 1) bwd_bf16_kernel(LaunchDesc d) {
+__global__ void __launch_bounds__((bwd_waves<DSET, ASET>() * kWave), 1) bwd_bf16_kernel(LaunchDesc d) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if ((int)blockIdx.x >= d.n_items) return;
   int g, h, b;
@@ -997,12 +1014,13 @@ __global__ void __launch_bounds__(kBwdWaves * kWave, 1) bwd_bf16_kernel(LaunchDe
   GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
   if (gd.head_acts != nullptr) gd.act = gd.head_acts[h];  // activation of this item's head
+  constexpr int NW = bwd_waves<DSET, ASET>();
   if constexpr ((DSET & kDim32) != 0)
-    if (gd.head_dim == 32) { bwd_dispatch_act<32, ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 32) { bwd_dispatch_act<32, NW, ASET>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim64) != 0)
-    if (gd.head_dim == 64) { bwd_dispatch_act<64, ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 64) { bwd_dispatch_act<64, NW, ASET>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim128) != 0)
-    if (gd.head_dim == 128) { bwd_dispatch_act<128, ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 128) { bwd_dispatch_act<128, NW, ASET>(lds, gd, b, h); return; }
 }
 
 }  // namespace gdpa

@@ -11,7 +11,7 @@ hipError_t launch_bwd_bf16_agpr(const LaunchDesc& d, int dim_set, int act_set, h
   constexpr int kAll = (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX);
   constexpr int kDimAll = kDim32 | kDim64 | kDim128;
 #define GDPA_LAUNCH(DS, AS) \
-  hipLaunchKernelGGL((bwd_bf16_kernel<DS, AS>), grid, dim3(kBwdWaves * kWave), bwd_lds_bytes<DS>(), stream, d)
+  hipLaunchKernelGGL((bwd_bf16_kernel<DS, AS>), grid, dim3((bwd_waves<DS, AS>() * kWave)), (bwd_lds_bytes<DS, AS>()), stream, d)
   if (act_set == 1 << GDPA_ACT_SOFTMAX) {
     if (dim_set == kDim128) GDPA_LAUNCH(kDim128, 1 << GDPA_ACT_SOFTMAX);
     else GDPA_LAUNCH(kDimAll, 1 << GDPA_ACT_SOFTMAX);

@@ -26,9 +26,12 @@ hipError_t launch_bwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t 
 
 // Keys of one (sequence, head) whose K and V^T fit in the forward kernel's LDS at once.
 inline constexpr int fwd_kv_capacity(int d) { return 16384 / d; }
-// Backward: 4 waves per workgroup; each wave owns 64 keys (two blocks of 32; 32 keys at d = 128)
-// for the whole sweep over query tiles of 64 rows.
+// Backward: a workgroup holds 256 keys (128 at d = 128) for the whole sweep over query tiles of
+// 64 rows: 4 waves owning 64 keys each (32 at d = 128), or, in launches with neither d = 128 nor
+// the softmax form, 8 waves (two per SIMD) owning 32 keys each.
 constexpr int kBwdWaves = 4;
+template <int DSET, int ASET>
+constexpr int bwd_waves() { return ((DSET & kDim128) || (ASET & (1 << GDPA_ACT_SOFTMAX))) ? 4 : 8; }
 constexpr int kBwdKeyBlock = 32;
 constexpr int kBwdQueryTile = 64;
 inline constexpr int bwd_keys_per_wave(int d) { return d == 128 ? 32 : 64; }
