@@ -502,8 +502,40 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     }
   };
 
+  // Eight waves, element-wise forms over resident keys: the waves with a dQ tile compute the
+  // previous tile's dQ right after their main pass, in the time the other wave of their SIMD still
+  // needs for its own main pass, instead of after the barrier; dS^T alternates between the two
+  // exchange areas (the second is free without softmax).
+  constexpr bool FQ = G::NW == 8 && !softmax && !WINDOWED && CHUNK == 0 && G::QH == 1;
+  constexpr int NK = 2 * NS;                       // 16-key steps of one dQ tile
+  const int drow = dtile * 32 + out_perm(lc);      // K^T row carried by this lane's A-operand row
+  auto dq_tile = [&](int sxoff) {
+    f32x16 a2[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_KT + drow * G::KTROW + (k * 16 + g * 8) * 2));
+      a2[k & 1] = mfma32(ka, sx_operand<G::SXROW>(lds, sxoff, k * 16, qh_first), a2[k & 1]);
+    }
+    return a2[0] + a2[1];
+  };
+  auto dq_store = [&](const f32x16& acc, int rbase) {
+    const int row = rbase + qh_first * 32 + lc;
+    if (row < L) {
+      u32x4 u0, u1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u0[e] = pack_bf16x2(acc[2 * e] * gd.scale, acc[2 * e + 1] * gd.scale);
+        u1[e] = pack_bf16x2(acc[8 + 2 * e] * gd.scale, acc[8 + 2 * e + 1] * gd.scale);
+      }
+      bf16* dst = it.dqseq + row * rs + dtile * 32 + g * 16;
+      *reinterpret_cast<u32x4*>(dst) = u0;
+      *reinterpret_cast<u32x4*>(dst + 8) = u1;
+    }
+  };
+
   for (int j = t0; j < t1; ++j) {
     const int r0 = j * G::QT;
+    f32x16 fq;  // FQ: the previous tile's dQ tile
     // ---- 1. take the blocks entering the window (all LDS readers of the previous tile are done)
     int blk[KACT];
     bool act[KACT];
@@ -615,6 +647,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     // MFMA pipe runs while the VALU works.
     if constexpr (CHUNK != 2) {
       constexpr int NIT = 2 * KACT;
+      const int sx_cur = (FQ && (j & 1)) ? G::OFF_SXL : G::OFF_SX;  // this tile's dS^T area
       f32x16 sacc[2], dpacc[2];
       bf16x8 qa[G::KK], da[G::KK];
       bf16x8 dota[G::DT][2], qta[G::DT][2];
@@ -745,7 +778,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         for (int a = 0; a < 4; ++a) {
           const int qo = (qs * 32 + a * 8 + g * 4) * 2;
           const int t = a >> 1, hlf = (a & 1) * 2;
-          *reinterpret_cast<u32x2*>(lds + G::OFF_SX + spos + qo) = u32x2{du[t][hlf], du[t][hlf + 1]};
+          *reinterpret_cast<u32x2*>(lds + sx_cur + spos + qo) = u32x2{du[t][hlf], du[t][hlf + 1]};
           if constexpr (softmax)
             *reinterpret_cast<u32x2*>(lds + G::OFF_SXL + spos + qo) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
         }
@@ -771,6 +804,8 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           }
       }
     }
+    if constexpr (FQ)
+      if (j > t0 && dq_role) fq = dq_tile((j & 1) ? G::OFF_SX : G::OFF_SXL);  // previous tile's area
     __syncthreads();  // dS^T tile complete; this tile's Q / dO / lse no longer read
     if (j + 1 < t1) {
       // next tile into LDS (while dQ runs), then the loads of the one after it: issued before this
@@ -801,14 +836,15 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
 
     // ---- 4. dQ^T = K^T dS^T over the ring slots in use (a slot outside the tile holds zero dS);
     // register r of lane (query, g) is d = dtile*32 + g*16 + r (out_perm order of the K^T rows)
-    if (CHUNK != 2 && dq_role) {
-      const int drow = dtile * 32 + out_perm(lc);  // K^T row carried by this lane's A-operand row
+    if constexpr (FQ) {
+      if (j > t0 && dq_role) dq_store(fq, r0 - G::QT);
+    }
+    if (CHUNK != 2 && !FQ && dq_role) {
 #pragma unroll
       for (int qi = 0; qi < G::QH; ++qi) {
         const int qh = qh_first + qi;
         // 16-key steps over the slots in use; the operands of step k+1 are read while step k
         // multiplies, and two accumulators keep consecutive MFMAs independent
-        constexpr int NK = 2 * NS;
         bf16x8 ka[2], sb[2], sl[2];
         auto load_step = [&](int k, int buf) {
           const int kbase = k * 16;
@@ -871,6 +907,10 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       }
     }
     if (j + 1 < t1) __syncthreads();  // next tile staged; dS^T and K^T staging free
+  }
+  if constexpr (FQ) {
+    // the last tile's dQ (its dS^T is complete since the barrier after its main pass)
+    if (t1 > t0 && dq_role) dq_store(dq_tile(((t1 - 1) & 1) ? G::OFF_SXL : G::OFF_SX), (t1 - 1) * G::QT);
   }
   if constexpr (CHUNK != 2)
 #pragma unroll
