@@ -13,8 +13,28 @@ hipError_t launch_bwd_bf16_agpr(const LaunchDesc& d, int dim_set, int act_set, h
 // One instantiation per head-dim set and activation present: a launch with one element-wise
 // activation runs a kernel without the softmax paths (and their registers); several head dims
 // share the kernel that holds all three.
-hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream) {
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, hipStream_t stream) {
   if (d.n_items == 0) return hipSuccess;
+  constexpr int kGelu_ = 1 << GDPA_ACT_GELU, kSilu_ = 1 << GDPA_ACT_SILU;
+  if (small) {
+    // every sequence has at most 32 keys (element-wise forms, no window): one wave per item
+    const dim3 sgrid((d.n_items + 3) / 4);
+#define GDPA_SMALL(DS, AS) \
+  hipLaunchKernelGGL((bwd_small_kernel<DS, AS>), sgrid, dim3(4 * kWave), (bwd_small_lds_bytes<DS>()), stream, d)
+#define GDPA_SMALL_ACTS(DS)                                                      \
+  if (act_set == kGelu_) GDPA_SMALL(DS, kGelu_);                                  \
+  else if (act_set == kSilu_) GDPA_SMALL(DS, kSilu_);                             \
+  else GDPA_SMALL(DS, kGelu_ | kSilu_);
+    switch (dim_set) {
+      case kDim32: GDPA_SMALL_ACTS(kDim32); break;
+      case kDim64: GDPA_SMALL_ACTS(kDim64); break;
+      case kDim128: GDPA_SMALL_ACTS(kDim128); break;
+      default: GDPA_SMALL_ACTS(kDim32 | kDim64 | kDim128); break;
+    }
+#undef GDPA_SMALL_ACTS
+#undef GDPA_SMALL
+    return hipGetLastError();
+  }
   const dim3 grid(d.n_items);
   constexpr int kDimAll = kDim32 | kDim64 | kDim128;
   constexpr int kGelu = 1 << GDPA_ACT_GELU, kSilu = 1 << GDPA_ACT_SILU, kSoftmax = 1 << GDPA_ACT_SOFTMAX;

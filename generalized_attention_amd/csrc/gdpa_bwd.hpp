@@ -1063,4 +1063,248 @@ __global__ void __launch_bounds__((bwd_waves<DSET, ASET>() * kWave), 1) bwd_bf16
     if (gd.head_dim == 128) { bwd_dispatch_act<128, NW, ASET>(lds, gd, b, h); return; }
 }
 
+// ---- Short key blocks: one wave per (sequence, head) item -------------------------------------
+//
+// When every sequence has at most 32 keys (element-wise forms, no window), a whole item fits one
+// wave: the wave keeps the block's K and V rows and its dK^T, dV^T accumulators in registers and
+// sweeps the item's query rows 32 at a time, with Q and dO rows staged in a private LDS area for
+// the transposing reads and dS^T in a private exchange tile for dQ. The four waves of a workgroup
+// work on four items with no barrier between them (a workgroup-wide sweep would leave three of
+// its four waves without keys).
+template <int D>
+struct SmallGeo {
+  static constexpr int KK = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int NROW = D * 2 + 16;          // row-major Q / dO tile row (bytes)
+  static constexpr int KTROW = 32 * 2 + 16;        // K^T row: 32 keys
+  static constexpr int SXROW = 32 * 2 + 16;        // dS^T row (one key): 32 queries
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_DO = OFF_Q + 32 * NROW;
+  static constexpr int OFF_KT = OFF_DO + 32 * NROW;
+  static constexpr int OFF_SX = OFF_KT + D * KTROW;
+  static constexpr int BYTES = OFF_SX + 32 * SXROW;  // per wave
+  static_assert(4 * BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int DSET>
+constexpr int bwd_small_lds_bytes() {
+  return 4 * max3((DSET & kDim32) ? SmallGeo<32>::BYTES : 0, (DSET & kDim64) ? SmallGeo<64>::BYTES : 0,
+                  (DSET & kDim128) ? SmallGeo<128>::BYTES : 0);
+}
+
+// The wave's LDS stores are complete and visible to all its lanes before its later LDS reads (and
+// the compiler keeps them in that order).
+__device__ inline void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int ACT, bool GATED>
+__device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, int b, int h) {
+  using G = SmallGeo<D>;
+  const int lane = lane_id(), lc = lane & 31, g = lane >> 5;
+  const int q0 = gd.q_off[b], k0 = gd.kv_off[b];
+  const int L = gd.q_off[b + 1] - q0, n = gd.kv_off[b + 1] - k0;
+  const int H = gd.num_heads;
+  const size_t rs = (size_t)H * D;
+  const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
+  const bf16* doseq = reinterpret_cast<const bf16*>(gd.dout) + ((size_t)q0 * H + h) * D;
+  bf16* dqseq = reinterpret_cast<bf16*>(gd.dq) + ((size_t)q0 * H + h) * D;
+  const bf16* kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
+  const bf16* vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;
+  const float* gseq = gd.g ? gd.g + (size_t)k0 * H + h : nullptr;
+  bf16* dkseq = reinterpret_cast<bf16*>(gd.dk) + ((size_t)k0 * H + h) * D;
+  bf16* dvseq = reinterpret_cast<bf16*>(gd.dv) + ((size_t)k0 * H + h) * D;
+  float* dgseq = gd.dg ? gd.dg + (size_t)k0 * H + h : nullptr;
+  constexpr int CPR = D / 8;
+  if (n <= 0) {  // no keys: dQ = 0
+    for (int idx = lane; idx < L * CPR; idx += kWave)
+      *reinterpret_cast<u32x4*>(dqseq + (idx / CPR) * rs + (idx % CPR) * 8) = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  if (L <= 0) {  // no queries: dK = dV = dG = 0
+    for (int idx = lane; idx < n * CPR; idx += kWave) {
+      *reinterpret_cast<u32x4*>(dkseq + (idx / CPR) * rs + (idx % CPR) * 8) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dvseq + (idx / CPR) * rs + (idx % CPR) * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (dgseq)
+      for (int r = lane; r < n; r += kWave) dgseq[(size_t)r * H] = 0.0f;
+    return;
+  }
+
+  // the block: this lane's key lc (rows past n are zero), K^T into the private staging tile
+  const bool kok = lc < n;
+  bf16x8 kreg[G::KK], vreg[G::KK];
+#pragma unroll
+  for (int kk = 0; kk < G::KK; ++kk) {
+    u32x4 ku = {0u, 0u, 0u, 0u}, vu = {0u, 0u, 0u, 0u};
+    if (kok) {
+      ku = *reinterpret_cast<const u32x4*>(kseq + lc * rs + g * (D / 2) + kk * 8);
+      vu = *reinterpret_cast<const u32x4*>(vseq + lc * rs + g * (D / 2) + kk * 8);
+    }
+    kreg[kk] = as_bf16x8(ku);
+    vreg[kk] = as_bf16x8(vu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d0 = g * (D / 2) + kk * 8 + 2 * e;
+      *reinterpret_cast<uint16_t*>(wl + G::OFF_KT + d0 * G::KTROW + lc * 2) = (uint16_t)(ku[e] & 0xFFFF);
+      *reinterpret_cast<uint16_t*>(wl + G::OFF_KT + (d0 + 1) * G::KTROW + lc * 2) = (uint16_t)(ku[e] >> 16);
+    }
+  }
+  float gate = 0.0f, graw = 0.0f;
+  if (GATED && kok) {
+    graw = gseq[(size_t)lc * H];
+    gate = log_sigmoid_f(graw);
+  }
+  f32x16 dk[G::DT], dv[G::DT];
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt) dk[dt] = dv[dt] = f32x16{};
+  float dgs = 0.0f;
+  const float sc = gd.scale;
+  float c1 = 0.0f, c3 = 0.0f;
+  PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
+  const float dv_scale = GATED ? 1.0f : gd.scale;
+
+  for (int r0 = 0; r0 < L; r0 += 32) {
+    // Q and dO rows r0 .. r0+31: lane (row lc, half g) loads the 16-byte pieces it needs as the A
+    // operand of S = Q K^T and dP = dO V^T, and stores them row-major for the transposing reads
+    const int row = r0 + lc;
+    bf16x8 qa[G::KK], da[G::KK];
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) {
+      u32x4 qu = {0u, 0u, 0u, 0u}, du = {0u, 0u, 0u, 0u};
+      if (row < L) {
+        qu = *reinterpret_cast<const u32x4*>(qseq + row * rs + g * (D / 2) + kk * 8);
+        du = *reinterpret_cast<const u32x4*>(doseq + row * rs + g * (D / 2) + kk * 8);
+      }
+      qa[kk] = as_bf16x8(qu);
+      da[kk] = as_bf16x8(du);
+      *reinterpret_cast<u32x4*>(wl + G::OFF_Q + lc * G::NROW + g * D + kk * 16) = qu;
+      *reinterpret_cast<u32x4*>(wl + G::OFF_DO + lc * G::NROW + g * D + kk * 16) = du;
+    }
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) {
+      sacc = mfma32(qa[kk], kreg[kk], sacc);
+      dpacc = mfma32(da[kk], vreg[kk], dpacc);
+    }
+    // register r of lane (key lc, g) is row r0 + c_row(r, g); keys and rows past the ends meet
+    // zero operands (phi(0) = 0, and their dO / Q rows are zero), so no mask is needed
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float dphi;
+      if constexpr (GATED) PointAct<ACT>::value_grad(__builtin_fmaf(sacc[r], sc, gate), 1.0f, c1, c3, p[r], dphi);
+      else PointAct<ACT>::value_grad(sacc[r], sc, c1, c3, p[r], dphi);
+      ds[r] = dpacc[r] * dphi;
+    }
+    if constexpr (GATED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dgs += ds[r];
+    }
+    u32x4 pu[2], du[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pu[t][e] = pack_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
+        du[t][e] = pack_bf16x2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1]);
+      }
+    // dS^T to the private exchange tile: registers 4a..4a+3 are 4 consecutive rows
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int t = a >> 1, hlf = (a & 1) * 2;
+      *reinterpret_cast<u32x2*>(wl + G::OFF_SX + lc * G::SXROW + (a * 8 + g * 4) * 2) = u32x2{du[t][hlf], du[t][hlf + 1]};
+    }
+    lds_wave_sync();  // the wave's Q / dO / dS^T stores are in LDS
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        dv[dt] = mfma32(tr_operand<G::NROW>(wl, G::OFF_DO, 0, t, dt), as_bf16x8(pu[t]), dv[dt]);
+        dk[dt] = mfma32(tr_operand<G::NROW>(wl, G::OFF_Q, 0, t, dt), as_bf16x8(du[t]), dk[dt]);
+      }
+    // dQ^T = K^T dS^T: register r of lane (row lc, g) is d = dt*32 + g*16 + r
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt) {
+      const int drow = dt * 32 + out_perm(lc);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(wl + G::OFF_KT + drow * G::KTROW + (k * 16 + g * 8) * 2));
+        acc = mfma32(ka, sx_operand<G::SXROW>(wl, G::OFF_SX, k * 16, 0), acc);
+      }
+      if (row < L) {
+        u32x4 u0, u1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u0[e] = pack_bf16x2(acc[2 * e] * gd.scale, acc[2 * e + 1] * gd.scale);
+          u1[e] = pack_bf16x2(acc[8 + 2 * e] * gd.scale, acc[8 + 2 * e + 1] * gd.scale);
+        }
+        bf16* dst = dqseq + row * rs + dt * 32 + g * 16;
+        *reinterpret_cast<u32x4*>(dst) = u0;
+        *reinterpret_cast<u32x4*>(dst + 8) = u1;
+      }
+    }
+    lds_wave_sync();  // every read of this tile's LDS areas is done before the next tile's stores
+  }
+  // dK, dV (and dG) of the block: register r of lane (key, g) in d-tile dt is d = dt*32 + c_row(r, g)
+  const float dgsum = dgs + __shfl_xor(dgs, 32);
+  if (kok) {
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = dt * 32 + a * 8 + g * 4;
+        u32x2 uk, uv;
+        uk[0] = pack_bf16x2(dk[dt][4 * a] * gd.scale, dk[dt][4 * a + 1] * gd.scale);
+        uk[1] = pack_bf16x2(dk[dt][4 * a + 2] * gd.scale, dk[dt][4 * a + 3] * gd.scale);
+        uv[0] = pack_bf16x2(dv[dt][4 * a] * dv_scale, dv[dt][4 * a + 1] * dv_scale);
+        uv[1] = pack_bf16x2(dv[dt][4 * a + 2] * dv_scale, dv[dt][4 * a + 3] * dv_scale);
+        *reinterpret_cast<u32x2*>(dkseq + lc * rs + d) = uk;
+        *reinterpret_cast<u32x2*>(dvseq + lc * rs + d) = uv;
+      }
+    if (dgseq != nullptr && g == 0) dgseq[(size_t)lc * H] = (1.0f / (1.0f + __expf(graw))) * dgsum;
+  }
+}
+
+template <int D, int ASET>
+__device__ __forceinline__ void bwd_small_dispatch(char* wl, const GroupDesc& gd, int b, int h) {
+  if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
+    if (gd.act == GDPA_ACT_GELU) {
+      if (gd.g != nullptr) bwd_small_item<D, GDPA_ACT_GELU, true>(wl, gd, b, h);
+      else bwd_small_item<D, GDPA_ACT_GELU, false>(wl, gd, b, h);
+      return;
+    }
+  if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
+    if (gd.act == GDPA_ACT_SILU) {
+      if (gd.g != nullptr) bwd_small_item<D, GDPA_ACT_SILU, true>(wl, gd, b, h);
+      else bwd_small_item<D, GDPA_ACT_SILU, false>(wl, gd, b, h);
+    }
+}
+
+// Workgroup x, wave w: work item 4x + w. The items are in longest-first order, so the four waves
+// of a workgroup get items of similar length.
+template <int DSET, int ASET>
+__global__ void __launch_bounds__(4 * kWave, 1) bwd_small_kernel(LaunchDesc d) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int w = wave_id();
+  const int item = (int)blockIdx.x * 4 + w;
+  if (item >= d.n_items) return;
+  int g, h, b;
+  unpack_item(d.items[item], g, h, b);
+  if (g >= d.n_groups) return;
+  GroupDesc gd = select_group(d, g);
+  if (b >= gd.num_seqs || h >= gd.num_heads) return;
+  constexpr int WB = bwd_small_lds_bytes<DSET>() / 4;
+  char* wl = lds + w * WB;
+  if constexpr ((DSET & kDim32) != 0)
+    if (gd.head_dim == 32) { bwd_small_dispatch<32, ASET>(wl, gd, b, h); return; }
+  if constexpr ((DSET & kDim64) != 0)
+    if (gd.head_dim == 64) { bwd_small_dispatch<64, ASET>(wl, gd, b, h); return; }
+  if constexpr ((DSET & kDim128) != 0)
+    if (gd.head_dim == 128) { bwd_small_dispatch<128, ASET>(wl, gd, b, h); return; }
+}
+
 }  // namespace gdpa

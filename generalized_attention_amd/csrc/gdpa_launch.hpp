@@ -13,7 +13,9 @@ enum DimSet { kDim32 = 1, kDim64 = 2, kDim128 = 4 };
 hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream);
 // act_set: bit (1 << act) for every activation present in the launch.
 hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
-hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
+// small: every problem has at most 32 keys per sequence, an element-wise activation and no window
+// (one wave per work item).
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, hipStream_t stream);
 // fp32 kernels are flat over (row, head) / (key, head); prefix tables over groups.
 struct Fp32Aux {
   int64_t row_pre[GDPA_MAX_GROUPS + 1];   // prefix of total_q * H

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from gdpa_workloads import make_workload
-from gpu_harness import check, device_group, rows_of, to64
+from gpu_harness import check, device_group, half_ulp_bf16, rows_of, to64
 
 import generalized_attention_amd as ga
 
@@ -281,6 +281,42 @@ def test_long_keys_pffn(keys, act):
 @pytest.mark.parametrize("window", [(-1, 0), (300, 0), (-1, -1), (200, 200), (64, 64), (0, 100)])
 def test_long_keys_self_attention(window, act):
     w = make_workload("causal_gated", 11, lengths=[1, 300, 700, 257, 0, 520], act=act, window=window)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+# ------------------------------------------------------------------------------------------------
+# Short key blocks (at most 32 keys per sequence: one wave per work item in the backward)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("keys,act", [(32, "silu"), (17, "gelu"), (8, "silu")])
+def test_short_keys_pffn(keys, act):
+    w = make_workload("pffn_train", 12, num_seqs=7, len_range=(1, 300), keys=keys, act=act, scale=0.125)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+def test_single_key_pffn():
+    """n = 1: every output row of O and dQ is one product of a bf16-rounded operand (P or dS) with
+    a key row, so its error is relative: rounding P / dS to bf16 (unit roundoff 2^-8) plus the
+    storage rounding. dK and dV still sum over all rows and keep the standard rule."""
+    w = make_workload("pffn_train", 12, num_seqs=7, len_range=(1, 300), keys=1, act="silu", scale=0.125)
+    g = w.groups[0]
+    dev = device_group(g)
+    o, lse = ga.gdpa_fwd(dev)
+    r = ga.gdpa_bwd(dev, g.dout.to("cuda:0"), o=o, lse=lse)
+    torch.cuda.synchronize()
+    ref_f = oracle.group_fwd(g)
+    ref_b = oracle.group_bwd(g)
+    for name, gpu, ref in (("O", to64(o), ref_f["o"]), ("dQ", to64(r["dq"]), ref_b["dq"])):
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        bound = 2.0 ** -8 * np.abs(ref) + half_ulp_bf16(np.maximum(np.abs(ref), np.abs(gpu))) + 1e-6 * rms
+        err = np.abs(gpu - ref)
+        assert np.all(err <= bound), f"{name}: {int((err > bound).sum())} elements above the single-product bound"
+    check("bf16", to64(r["dk"]), ref_b["dk"], "dK")
+    check("bf16", to64(r["dv"]), ref_b["dv"], "dV")
+
+
+def test_short_keys_gated_self_attention():
+    w = make_workload("causal_gated", 13, lengths=[0, 1, 5, 31, 32, 17, 32], act="gelu", window=(-1, -1))
     compare_workload(w, ("fwd", "bwd"))
 
 
