@@ -217,7 +217,8 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = load_traffic(args.workload, dominant)
-    roof["kernel"] = f"gdpa_{dominant} main kernel ({dominant}_bf16_kernel)"
+    roof["kernel"] = (f"gdpa_{dominant} main kernel ("
+                      + ("bwd_small_kernel / bwd_bf16_kernel" if dominant == "bwd" else "fwd_bf16_kernel") + ")")
     roof["kernel_ms"] = kms
     roof["algorithmic_bytes"] = kbytes
     roof["algorithmic_flops"] = kflops
