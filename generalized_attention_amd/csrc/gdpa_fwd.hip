@@ -27,14 +27,25 @@
 
 namespace gdpa {
 
-// Waves per workgroup. Two workgroups share a CU (LDS bound), so six waves give three waves per
-// SIMD when the register footprint allows it (launches without d = 128 problems); else four.
-template <int DSET>
-constexpr int fwd_waves() { return (DSET & kDim128) ? 4 : 4; }
+// Launch modes, by the problems in the launch:
+//   kFwdAny       any key length: resident keys, ring window or key chunks; 4 waves per workgroup,
+//                 2 workgroups/CU (2 waves per SIMD);
+//   kFwdResident  d <= 64 and every key range fits in LDS (at most 16384 / d keys): only the
+//                 resident path is built, whose smaller register footprint allows 8 waves per
+//                 workgroup, 2 workgroups/CU (4 waves per SIMD).
+enum FwdMode { kFwdAny = 0, kFwdResident = 1 };
+template <int MODE>
+constexpr int fwd_waves() { return MODE == kFwdResident ? 8 : 4; }
+// minimum waves per SIMD (the second launch bound)
+template <int MODE>
+constexpr int fwd_waves_per_simd() { return MODE == kFwdResident ? 4 : 2; }
+// Keys staged in LDS at once.
+template <int D, int MODE>
+constexpr int fwd_nkv() { return 16384 / D; }
 
-template <int D>
+template <int D, int KEYS>
 struct FwdGeo {
-  static constexpr int NKV = 16384 / D;        // keys that fit in LDS
+  static constexpr int NKV = KEYS;             // keys that fit in LDS
   static constexpr int KROW = D * 2 + 16;      // bytes per staged K row (16 B pad: no bank conflicts)
   static constexpr int VROW = NKV * 2 + 16;    // bytes per staged V^T row
   static constexpr int KK = D / 16;            // MFMA k-steps over d
@@ -44,9 +55,12 @@ struct FwdGeo {
   static constexpr int BYTES = OFF_G + NKV * 4;
 };
 
-constexpr int kFwdLdsBytes = FwdGeo<32>::BYTES > FwdGeo<64>::BYTES
-                                 ? (FwdGeo<32>::BYTES > FwdGeo<128>::BYTES ? FwdGeo<32>::BYTES : FwdGeo<128>::BYTES)
-                                 : (FwdGeo<64>::BYTES > FwdGeo<128>::BYTES ? FwdGeo<64>::BYTES : FwdGeo<128>::BYTES);
+constexpr int fwd_max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+template <int MODE>
+constexpr int fwd_lds_bytes() {
+  return fwd_max3(FwdGeo<32, fwd_nkv<32, MODE>()>::BYTES, FwdGeo<64, fwd_nkv<64, MODE>()>::BYTES,
+                  FwdGeo<128, fwd_nkv<128, MODE>()>::BYTES);
+}
 
 // Position of local key kl inside the staged V^T row: blocks of 32 keys, halves of 16, and the
 // slot order of the B operand inside each half.
@@ -59,10 +73,10 @@ __device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
 // write.
 // The keys land at LDS key positions dst + (0 .. span_pad-1) (dst a multiple of 32).
 // SERIAL: keep the rounds in order (the caller holds accumulators in registers across the staging).
-template <int D, int NT, bool SERIAL = false>
+template <int D, int NKV, int NT, bool SERIAL = false>
 __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
                          int span, int span_pad, bool softmax, int dst = 0) {
-  using G = FwdGeo<D>;
+  using G = FwdGeo<D, NKV>;
   constexpr int CPR = D / 8;                                  // 16-byte chunks per row
   constexpr int KI = (G::NKV * CPR + NT - 1) / NT;           // K chunks per thread (at most)
   constexpr int VI = (G::NKV / 4 * CPR + NT - 1) / NT;       // V units per thread (at most)
@@ -170,9 +184,9 @@ __device__ inline void load_q(QFrags<D, QS>& q, const bf16* qseq, size_t rs, int
 }
 
 // S^T block kb (32 keys x QS*32 rows) = K_kb Q^T on MFMA, K rows from LDS.
-template <int D, int QS>
+template <int D, int NKV, int QS>
 __device__ inline void scores_block(const char* lds, const QFrags<D, QS>& q, int kb, f32x16 (&s)[QS]) {
-  using G = FwdGeo<D>;
+  using G = FwdGeo<D, NKV>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) s[qs] = f32x16{};
@@ -208,11 +222,11 @@ __device__ __forceinline__ void acc_init(FwdAcc<D, QS>& a) {
 // (keys from kend on are invalid) and sits in LDS block slot b, or b mod NKV / 32 (RING).
 // GATED: the problem has a gate. MASKED: entries may need an explicit mask (the softmax form, or
 // a window); without it, keys past the end meet zero K and V rows in LDS and phi(0) = 0.
-template <int D, int ACT, int QS, bool GATED, bool MASKED, bool RING = false>
+template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool RING = false>
 __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf,
                                                FwdAcc<D, QS>& acc, int row0, int kbase, int kend, int kb0,
                                                int kb1) {
-  using G = FwdGeo<D>;
+  using G = FwdGeo<D, NKV>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
   constexpr bool softmax = ACT == GDPA_ACT_SOFTMAX;
   const float* gl = reinterpret_cast<const float*>(lds + G::OFF_G);
@@ -310,15 +324,15 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
   // while the vector units evaluate the activation; the loop body has no branches.
   f32x16 sa[QS], sb[QS];
   int kb = kb0;
-  if (kb < kb1) scores_block<D, QS>(lds, qf, kb & smask, sa);
+  if (kb < kb1) scores_block<D, NKV, QS>(lds, qf, kb & smask, sa);
   for (; kb + 2 < kb1; kb += 2) {
-    scores_block<D, QS>(lds, qf, (kb + 1) & smask, sb);
+    scores_block<D, NKV, QS>(lds, qf, (kb + 1) & smask, sb);
     process(kb, sa);
-    scores_block<D, QS>(lds, qf, (kb + 2) & smask, sa);
+    scores_block<D, NKV, QS>(lds, qf, (kb + 2) & smask, sa);
     process(kb + 1, sb);
   }
   if (kb + 1 < kb1) {
-    scores_block<D, QS>(lds, qf, (kb + 1) & smask, sb);
+    scores_block<D, NKV, QS>(lds, qf, (kb + 1) & smask, sb);
     process(kb, sa);
     process(kb + 1, sb);
   } else if (kb < kb1) {
@@ -329,10 +343,10 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
 
 // Epilogue of one wave tile: softmax normalisation and lse, or the deferred score scale of the
 // element-wise forms; each lane stores 16 consecutive d of one row.
-template <int D, int ACT, int QS, bool GATED>
+template <int D, int NKV, int ACT, int QS, bool GATED>
 __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, QS>& acc, bf16* oseq, float* lseq,
                                            int L, int row0) {
-  using G = FwdGeo<D>;
+  using G = FwdGeo<D, NKV>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
   const int H = gd.num_heads;
   const size_t rs = (size_t)H * D;
@@ -366,27 +380,28 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
 }
 
 // One wave tile against staged key blocks [kb0, kb1), then its epilogue.
-template <int D, int ACT, int QS, bool GATED, bool MASKED>
+template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED>
 __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
                                          float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   FwdAcc<D, QS> acc;
   acc_init(acc);
-  fwd_accumulate<D, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, klo, klo + span, kb0, kb1);
-  fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
+  fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, klo, klo + span, kb0, kb1);
+  fwd_finish<D, NKV, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
 }
 
 // Whether a bounded window's key range for a group of NW * 32 rows fits in the ring of LDS blocks.
-template <int D>
+template <int D, int NKV>
 __device__ __forceinline__ bool fwd_ring_fits(int wl, int wr, int group_rows) {
   if (wl < 0 || wr < 0) return false;
-  return (group_rows - 1 + wr) / 32 + (wl + 31) / 32 + 1 <= FwdGeo<D>::NKV / 32;
+  return (group_rows - 1 + wr) / 32 + (wl + 31) / 32 + 1 <= FwdGeo<D, NKV>::NKV / 32;
 }
 
 // One work item: all query rows of one (sequence, head). QS: 32-row tiles per wave while the keys
 // are resident or pass through the ring; QL: the same in the key-chunked sweep.
-template <int D, int NW, int ACT, int QS, int QL, bool GATED, bool MASKED>
+// LONG: the launch may hold key ranges longer than NKV (else only the resident path is built).
+template <int D, int NKV, int NW, int ACT, int QS, int QL, bool GATED, bool MASKED, bool LONG>
 __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, int h) {
-  using G = FwdGeo<D>;
+  using G = FwdGeo<D, NKV>;
   const int q0 = gd.q_off[b], L = gd.q_off[b + 1] - q0;
   const int k0 = gd.kv_off[b], N = gd.kv_off[b + 1] - k0;
   if (L <= 0) return;
@@ -409,10 +424,10 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
     const int span_pad = (N + 31) & ~31;
     // d <= 64: the first Q tile is in flight during the staging and each next tile's Q during
     // the current tile (d = 128: the registers do not allow it; Q is loaded per tile)
-    constexpr bool kPrefetchQ = D < 128;
+    constexpr bool kPrefetchQ = D < 128 && NW == 4;  // (with 8 waves the other waves hide the load)
     QFrags<D, QS> qcur, qnext;
     if (kPrefetchQ && w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
-    stage_kv<D, NW * kWave>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
+    stage_kv<D, NKV, NW * kWave>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
     __syncthreads();
     for (int row0 = w * RW; row0 < L; row0 += NW * RW) {
       // next tile's Q is loaded while this tile computes
@@ -422,10 +437,10 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
-      fwd_tile<D, ACT, QS, GATED, MASKED>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
+      fwd_tile<D, NKV, ACT, QS, GATED, MASKED>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       if (kPrefetchQ) qcur = qnext;
     }
-  } else if (D < 128 && fwd_ring_fits<D>(gd.wl, gd.wr, NW * RW)) {
+  } else if (LONG && D < 128 && fwd_ring_fits<D, NKV>(gd.wl, gd.wr, NW * RW)) {
     // bounded window over a long sequence: the keys pass through a ring of NKV / 32 LDS blocks
     // (block b in slot b mod NKV / 32); each group of NW * RW rows stages only the blocks that
     // enter its key range [r0 - left, r0 + NW * RW + right), so every key is read once
@@ -448,7 +463,7 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
           const int nblk = blast - bnext + 1 < NSLOT - slot ? blast - bnext + 1 : NSLOT - slot;
           const int k0 = bnext * 32;
           const int span = N - k0 < nblk * 32 ? N - k0 : nblk * 32;
-          stage_kv<D, NW * kWave>(lds, kseq + (size_t)k0 * H * D, vseq + (size_t)k0 * H * D,
+          stage_kv<D, NKV, NW * kWave>(lds, kseq + (size_t)k0 * H * D, vseq + (size_t)k0 * H * D,
                                            gseq ? gseq + (size_t)k0 * H : nullptr, H, span, nblk * 32, softmax,
                                            slot * 32);
           bnext += nblk;
@@ -463,11 +478,11 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
         FwdAcc<D, QS> acc;
         acc_init(acc);
         if (hi >= lo)
-          fwd_accumulate<D, ACT, QS, GATED, MASKED, true>(lds, gd, qf, acc, row0, 0, N, lo / 32, hi / 32 + 1);
-        fwd_finish<D, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
+          fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, true>(lds, gd, qf, acc, row0, 0, N, lo / 32, hi / 32 + 1);
+        fwd_finish<D, NKV, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
       }
     }
-  } else {
+  } else if (LONG) {
     // long key range: row groups of NW * QL * 32 rows; for each, the group's key range (all keys,
     // or [r0 - left, r0 + rows + right) under a window) is staged in chunks of NKV keys and every
     // wave carries its tile's O and softmax state across the chunks.
@@ -492,49 +507,49 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       for (int kc = glo; kc < ghi; kc += G::NKV) {
         const int span = ghi - kc < G::NKV ? ghi - kc : G::NKV;
         __syncthreads();  // previous chunk done with LDS
-        stage_kv<D, NW * kWave, true>(lds, kseq + (size_t)kc * H * D, vseq + (size_t)kc * H * D,
+        stage_kv<D, NKV, NW * kWave, true>(lds, kseq + (size_t)kc * H * D, vseq + (size_t)kc * H * D,
                     gseq ? gseq + (size_t)kc * H : nullptr, H, span, (span + 31) & ~31, softmax);
         __syncthreads();
         const int clo = lo > kc ? lo : kc;
         const int chi = hi < kc + span - 1 ? hi : kc + span - 1;
         if (active && chi >= clo) {
           if (!kHoldQ) load_q<D, QL>(qf, qseq, rs, row0, L);
-          fwd_accumulate<D, ACT, QL, GATED, MASKED>(lds, gd, qf, acc, row0, kc, kc + span, (clo - kc) / 32,
+          fwd_accumulate<D, NKV, ACT, QL, GATED, MASKED>(lds, gd, qf, acc, row0, kc, kc + span, (clo - kc) / 32,
                                                     (chi - kc) / 32 + 1);
         }
       }
-      if (active) fwd_finish<D, ACT, QL, GATED>(gd, acc, oseq, lseq, L, row0);
+      if (active) fwd_finish<D, NKV, ACT, QL, GATED>(gd, acc, oseq, lseq, L, row0);
     }
   }
 }
 
 // Gate and mask variants of one activation: a window and the softmax form are masked; a problem
 // without window or softmax runs the mask-free body.
-template <int D, int NW, int ACT, int QS>
+template <int D, int NKV, int NW, int ACT, int QS, bool LONG>
 __device__ __forceinline__ void fwd_dispatch_variant(char* lds, const GroupDesc& gd, int b, int h) {
   constexpr int QL = 1;  // (two tiles per wave in the key-chunked sweep spill registers)
   const bool masked = ACT == GDPA_ACT_SOFTMAX || gd.wl >= 0 || gd.wr >= 0;
   if (gd.g != nullptr) {
-    if (masked) fwd_item<D, NW, ACT, QS, QL, true, true>(lds, gd, b, h);
-    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, QL, true, false>(lds, gd, b, h);
+    if (masked) fwd_item<D, NKV, NW, ACT, QS, QL, true, true, LONG>(lds, gd, b, h);
+    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NKV, NW, ACT, QS, QL, true, false, LONG>(lds, gd, b, h);
   } else {
-    if (masked) fwd_item<D, NW, ACT, QS, QL, false, true>(lds, gd, b, h);
-    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NW, ACT, QS, QL, false, false>(lds, gd, b, h);
+    if (masked) fwd_item<D, NKV, NW, ACT, QS, QL, false, true, LONG>(lds, gd, b, h);
+    else if constexpr (ACT != GDPA_ACT_SOFTMAX) fwd_item<D, NKV, NW, ACT, QS, QL, false, false, LONG>(lds, gd, b, h);
   }
 }
 
-template <int D, int NW, int ASET>
+template <int D, int NKV, int NW, int ASET, bool LONG>
 __device__ __forceinline__ void fwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
   if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
-    if (gd.act == GDPA_ACT_GELU) { fwd_dispatch_variant<D, NW, GDPA_ACT_GELU, 1>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_GELU) { fwd_dispatch_variant<D, NKV, NW, GDPA_ACT_GELU, 1, LONG>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
-    if (gd.act == GDPA_ACT_SILU) { fwd_dispatch_variant<D, NW, GDPA_ACT_SILU, 1>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_SILU) { fwd_dispatch_variant<D, NKV, NW, GDPA_ACT_SILU, 1, LONG>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
-    if (gd.act == GDPA_ACT_SOFTMAX) fwd_dispatch_variant<D, NW, GDPA_ACT_SOFTMAX, 1>(lds, gd, b, h);
+    if (gd.act == GDPA_ACT_SOFTMAX) fwd_dispatch_variant<D, NKV, NW, GDPA_ACT_SOFTMAX, 1, LONG>(lds, gd, b, h);
 }
 
-template <int DSET, int ASET>
-__global__ void __launch_bounds__(fwd_waves<DSET>() * kWave, 2) fwd_bf16_kernel(LaunchDesc d) {
+template <int DSET, int ASET, int MODE>
+__global__ void __launch_bounds__(fwd_waves<MODE>() * kWave, fwd_waves_per_simd<MODE>()) fwd_bf16_kernel(LaunchDesc d) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if ((int)blockIdx.x >= d.n_items) return;
   int g, h, b;
@@ -543,20 +558,23 @@ __global__ void __launch_bounds__(fwd_waves<DSET>() * kWave, 2) fwd_bf16_kernel(
   GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
   if (gd.head_acts != nullptr) gd.act = gd.head_acts[h];  // activation of this item's head
+  constexpr int NW = fwd_waves<MODE>();
+  constexpr bool LONG = MODE == kFwdAny;
   if constexpr ((DSET & kDim32) != 0)
-    if (gd.head_dim == 32) { fwd_dispatch_act<32, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 32) { fwd_dispatch_act<32, fwd_nkv<32, MODE>(), NW, ASET, LONG>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim64) != 0)
-    if (gd.head_dim == 64) { fwd_dispatch_act<64, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 64) { fwd_dispatch_act<64, fwd_nkv<64, MODE>(), NW, ASET, LONG>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim128) != 0)
-    if (gd.head_dim == 128) { fwd_dispatch_act<128, fwd_waves<DSET>(), ASET>(lds, gd, b, h); return; }
+    if (gd.head_dim == 128) { fwd_dispatch_act<128, fwd_nkv<128, MODE>(), NW, ASET, LONG>(lds, gd, b, h); return; }
 }
 
-hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream) {
-  if (d.n_items == 0) return hipSuccess;
+template <int MODE>
+hipError_t launch_fwd_bf16_t(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream) {
   const dim3 grid(d.n_items);
   constexpr int kAll = (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX);
 #define GDPA_LAUNCH(DS, AS) \
-  hipLaunchKernelGGL((fwd_bf16_kernel<DS, AS>), grid, dim3(fwd_waves<DS>() * kWave), kFwdLdsBytes, stream, d)
+  hipLaunchKernelGGL((fwd_bf16_kernel<DS, AS, MODE>), grid, dim3(fwd_waves<MODE>() * kWave), \
+                     (fwd_lds_bytes<MODE>()), stream, d)
 #define GDPA_LAUNCH_ACTS(DS)                                          \
   switch (act_set) {                                                  \
     case 1 << GDPA_ACT_GELU: GDPA_LAUNCH(DS, 1 << GDPA_ACT_GELU); break;  \
@@ -564,15 +582,29 @@ hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStr
     case 1 << GDPA_ACT_SOFTMAX: GDPA_LAUNCH(DS, 1 << GDPA_ACT_SOFTMAX); break; \
     default: GDPA_LAUNCH(DS, kAll); break;                            \
   }
-  switch (dim_set) {
-    case kDim32: GDPA_LAUNCH_ACTS(kDim32); break;
-    case kDim64: GDPA_LAUNCH_ACTS(kDim64); break;
-    case kDim128: GDPA_LAUNCH_ACTS(kDim128); break;
-    default: GDPA_LAUNCH_ACTS(kDim32 | kDim64 | kDim128); break;  // several head dims
+  if constexpr (MODE == kFwdResident) {  // d <= 64 only (d = 128 does not fit 128 registers)
+    switch (dim_set) {
+      case kDim32: GDPA_LAUNCH_ACTS(kDim32); break;
+      case kDim64: GDPA_LAUNCH_ACTS(kDim64); break;
+      default: GDPA_LAUNCH_ACTS(kDim32 | kDim64); break;
+    }
+  } else {
+    switch (dim_set) {
+      case kDim32: GDPA_LAUNCH_ACTS(kDim32); break;
+      case kDim64: GDPA_LAUNCH_ACTS(kDim64); break;
+      case kDim128: GDPA_LAUNCH_ACTS(kDim128); break;
+      default: GDPA_LAUNCH_ACTS(kDim32 | kDim64 | kDim128); break;  // several head dims
+    }
   }
 #undef GDPA_LAUNCH_ACTS
 #undef GDPA_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, int key_mode, hipStream_t stream) {
+  if (d.n_items == 0) return hipSuccess;
+  return key_mode == kFwdResident ? launch_fwd_bf16_t<kFwdResident>(d, dim_set, act_set, stream)
+                                   : launch_fwd_bf16_t<kFwdAny>(d, dim_set, act_set, stream);
 }
 
 }  // namespace gdpa

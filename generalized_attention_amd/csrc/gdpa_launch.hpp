@@ -12,7 +12,8 @@ enum DimSet { kDim32 = 1, kDim64 = 2, kDim128 = 4 };
 
 hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream);
 // act_set: bit (1 << act) for every activation present in the launch.
-hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
+// key_mode: 1 = d <= 64 and every key range fits the forward's LDS (16384 / d keys); 0 = any.
+hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, int key_mode, hipStream_t stream);
 // small: every problem has at most 32 keys per sequence, an element-wise activation and no window
 // (one wave per work item).
 hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, hipStream_t stream);
