@@ -62,7 +62,11 @@ struct BwdGeo {
   static constexpr int OFF_ROW = OFF_SXL + CAP * SXROW;     // lse2[QT] (log2 units)
   static constexpr int OFF_DPART = OFF_ROW + QT * 4;        // softmax: partial D_i per wave [NW][QT]
   static constexpr int OFF_GATE = OFF_DPART + NW * QT * 4;  // gate term per ring position [CAP]
-  static constexpr int BYTES = OFF_GATE + CAP * 4;
+  // 8 waves: a second Q / dO tile buffer (the next tile is stored during the current one)
+  static constexpr int QBUFS = NW == 8 ? 2 : 1;
+  static constexpr int OFF_QN1 = OFF_GATE + CAP * 4;
+  static constexpr int OFF_DON1 = OFF_QN1 + QT * NROW;
+  static constexpr int BYTES = QBUFS == 2 ? OFF_DON1 + QT * NROW : OFF_GATE + CAP * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
   static_assert(CAP == bwd_capacity(D), "resident keys per workgroup");
   static_assert(NW == 4 || D <= 64, "8 waves only for d <= 64");
@@ -299,16 +303,18 @@ __device__ void prefetch_qtile(QTileRegs<D, NW>& pf, const bf16* qseq, const bf1
   }
 }
 
+// buf: which Q / dO tile buffer (the second exists with 8 waves)
 template <int D, int NW, bool SOFTMAX, bool DSUM = false>
-__device__ void store_qtile(char* lds, const QTileRegs<D, NW>& pf) {
+__device__ void store_qtile(char* lds, const QTileRegs<D, NW>& pf, int buf = 0) {
   using G = BwdGeo<D, NW>;
+  const int qoff = buf ? G::OFF_QN1 : G::OFF_QN, doff = buf ? G::OFF_DON1 : G::OFF_DON;
 #pragma unroll
   for (int i = 0; i < G::NPF; ++i) {
     const int idx = threadIdx.x + i * G::THREADS;
     if (idx < G::QT * G::CPR) {
       const int r = idx / G::CPR, c = idx % G::CPR;
-      *reinterpret_cast<u32x4*>(lds + G::OFF_QN + r * G::NROW + c * 16) = pf.q[i];
-      *reinterpret_cast<u32x4*>(lds + G::OFF_DON + r * G::NROW + c * 16) = pf.d[i];
+      *reinterpret_cast<u32x4*>(lds + qoff + r * G::NROW + c * 16) = pf.q[i];
+      *reinterpret_cast<u32x4*>(lds + doff + r * G::NROW + c * 16) = pf.d[i];
     }
   }
   if constexpr (SOFTMAX)
@@ -648,6 +654,8 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     if constexpr (CHUNK != 2) {
       constexpr int NIT = 2 * KACT;
       const int sx_cur = (FQ && (j & 1)) ? G::OFF_SXL : G::OFF_SX;  // this tile's dS^T area
+      const int q_cur = (FQ && (j & 1)) ? G::OFF_QN1 : G::OFF_QN;    // this tile's Q / dO buffer
+      const int do_cur = (FQ && (j & 1)) ? G::OFF_DON1 : G::OFF_DON;
       f32x16 sacc[2], dpacc[2];
       bf16x8 qa[G::KK], da[G::KK];
       bf16x8 dota[G::DT][2], qta[G::DT][2];
@@ -655,8 +663,8 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       auto load_a = [&](int qs) {
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
-          qa[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_QN + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
-          da[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_DON + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+          qa[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + q_cur + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+          da[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + do_cur + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
         }
       };
       auto issue_sdp = [&](int kb, int slot) {
@@ -787,8 +795,8 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              dota[dt][t] = tr_operand<G::NROW>(lds, G::OFF_DON, qs, t, dt);
-              qta[dt][t] = tr_operand<G::NROW>(lds, G::OFF_QN, qs, t, dt);
+              dota[dt][t] = tr_operand<G::NROW>(lds, do_cur, qs, t, dt);
+              qta[dt][t] = tr_operand<G::NROW>(lds, q_cur, qs, t, dt);
             }
         }
 #pragma unroll
@@ -804,8 +812,19 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           }
       }
     }
-    if constexpr (FQ)
+    if constexpr (FQ) {
+      // one barrier per tile: the next tile goes into the other Q / dO buffer (last read by the
+      // previous tile's main pass) before the barrier, then the previous tile's dQ
+      if (j + 1 < t1) {
+        store_qtile<D, NW, softmax, DSUM>(lds, pf, (j + 1) & 1);
+        if (j + 2 < t1)
+          prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
+      }
       if (j > t0 && dq_role) fq = dq_tile((j & 1) ? G::OFF_SX : G::OFF_SXL);  // previous tile's area
+      __syncthreads();  // this tile's dS^T and the next tile's Q / dO complete
+      if (j > t0 && dq_role) dq_store(fq, r0 - G::QT);
+      continue;
+    }
     __syncthreads();  // dS^T tile complete; this tile's Q / dO / lse no longer read
     if (j + 1 < t1) {
       // next tile into LDS (while dQ runs), then the loads of the one after it: issued before this
@@ -836,9 +855,6 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
 
     // ---- 4. dQ^T = K^T dS^T over the ring slots in use (a slot outside the tile holds zero dS);
     // register r of lane (query, g) is d = dtile*32 + g*16 + r (out_perm order of the K^T rows)
-    if constexpr (FQ) {
-      if (j > t0 && dq_role) dq_store(fq, r0 - G::QT);
-    }
     if (CHUNK != 2 && !FQ && dq_role) {
 #pragma unroll
       for (int qi = 0; qi < G::QH; ++qi) {
