@@ -125,6 +125,7 @@ def test_workspace_size_key_chunks(lib):
 INVALID_PROBLEMS = [
     ("negative seqs", dict(num_seqs=-1), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("zero heads", dict(num_heads=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("257 heads", dict(num_heads=257), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("head dim 48", dict(head_dim=48), _lib.GDPA_ERR_UNSUPPORTED),
     ("bad dtype", dict(dtype=7), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("bad act", dict(act=3), _lib.GDPA_ERR_INVALID_ARGUMENT),

@@ -339,6 +339,23 @@ def test_seed_pool_full_size():
     compare_workload(make_workload("seed_pool", 0), ("fwd", "bwd"))
 
 
+def test_maximum_head_count():
+    """256 heads (the largest the work-item encoding takes), several head dims and a ragged mix of
+    short sequences, forward and backward."""
+    import dataclasses
+    for d, act in ((32, "gelu"), (64, "softmax")):
+        w = make_workload("pffn_train", 14, num_seqs=3, len_range=(1, 70), keys=40, act=act, scale=0.125)
+        g = w.groups[0]
+        rng = np.random.default_rng(15)
+        t, n = g.total_q, g.total_kv
+        g.spec = dataclasses.replace(g.spec, num_heads=256, head_dim=d)
+        g.q = torch.from_numpy(rng.standard_normal((t, 256, d))).to(torch.bfloat16)
+        g.k = torch.from_numpy(rng.standard_normal((n, 256, d))).to(torch.bfloat16)
+        g.v = torch.from_numpy(rng.standard_normal((n, 256, d))).to(torch.bfloat16)
+        g.dout = torch.from_numpy(rng.standard_normal((t, 256, d))).to(torch.bfloat16)
+        compare_workload(w, ("fwd", "bwd"))
+
+
 def test_per_head_activation_fp32():
     w = make_workload("tiny_fp32", 3, act=("softmax", "gelu"))
     compare_workload(w, ("fwd", "bwd"))
