@@ -321,6 +321,21 @@ def test_short_keys_gated_self_attention():
 
 
 # ------------------------------------------------------------------------------------------------
+# Saturated activations: scaled scores of several hundred, where sigmoid(x) is 0 or 1 in fp32 and
+# 2^(-x log2 e) overflows to +inf for x below about -88
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,keys,act", [("pffn_train", None, "silu"), ("pffn_train", None, "gelu"),
+                                           ("pffn_train", 16, "silu"), ("causal_gated", None, "gelu"),
+                                           ("causal_gated", None, "softmax")])
+def test_saturated_scores(name, keys, act):
+    kw = dict(num_seqs=5, len_range=(1, 300), act=act, scale=30.0)
+    if keys is not None:
+        kw["keys"] = keys
+    compare_workload(make_workload(name, 21, **kw), ("fwd", "bwd"))
+
+
+# ------------------------------------------------------------------------------------------------
 # Shared seed queries (PMA / hierarchical seed pooling form)
 # ------------------------------------------------------------------------------------------------
 
