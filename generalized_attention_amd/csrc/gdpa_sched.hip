@@ -13,12 +13,17 @@ namespace gdpa {
 
 // Launched with exactly kNumBuckets threads (one per bucket in the scan).
 __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc d) {
+  static_assert(kNumBuckets % 64 == 0 && kNumBuckets / 64 <= 64, "bucket scan layout");
   __shared__ int32_t hist[kNumBuckets];
   __shared__ int32_t cursor[kNumBuckets];
+  __shared__ int32_t wave_total[kNumBuckets / 64];
   const int tid = threadIdx.x;
   for (int i = tid; i < kNumBuckets; i += blockDim.x) hist[i] = 0;
   __syncthreads();
 
+  // pass 1: bucket key of every sequence (the thread's first sequence stays in registers, later
+  // ones go through the scratch array) and the bucket histogram in work items
+  int key0 = 0, g0 = 0, b0 = 0;
   for (int s = tid; s < d.n_seqs_total; s += blockDim.x) {
     int g = 0;
     while (g + 1 < d.n_groups && s >= d.grp[g + 1].seq_base) ++g;
@@ -30,36 +35,52 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
     const int64_t work = (L + 32) * (N + 32) * gd.head_dim;  // +32: fixed per-tile costs
     int64_t key = work >> d.work_shift;
     if (key > kNumBuckets - 1) key = kNumBuckets - 1;
-    d.scratch[s] = (int32_t)key;
+    if (s == tid) {
+      key0 = (int)key;
+      g0 = g;
+      b0 = b;
+    } else {
+      d.scratch[s] = (int32_t)key;
+    }
     atomicAdd(&hist[key], gd.num_heads);
   }
   __syncthreads();
   // exclusive prefix sum in descending bucket order (longest work first): thread t owns bucket
-  // kNumBuckets-1-t; Hillis-Steele scan over the 1024 buckets in LDS.
+  // kNumBuckets-1-t. Each wave scans its 64 buckets with lane shuffles; the wave totals are then
+  // added in wave order.
   {
     const int k = kNumBuckets - 1 - tid;
-    int32_t v = hist[k];
-    cursor[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kNumBuckets; off <<= 1) {
-      const int32_t add = tid >= off ? cursor[tid - off] : 0;
-      __syncthreads();
-      cursor[tid] += add;
-      __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int32_t v = hist[k];
+    int32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t up = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += up;
     }
-    const int32_t excl = cursor[tid] - v;
+    if (lane == 63) wave_total[wave] = incl;
     __syncthreads();
-    hist[k] = excl;  // hist now holds the start position of each bucket
-    __syncthreads();
-    cursor[k] = excl;
+    int32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += wave_total[w];
+    cursor[k] = base + incl - v;
   }
   __syncthreads();
+  // pass 2: each sequence takes num_heads consecutive slots of its bucket (the order inside a
+  // bucket is free: items of one bucket have about the same work)
   for (int s = tid; s < d.n_seqs_total; s += blockDim.x) {
-    int g = 0;
-    while (g + 1 < d.n_groups && s >= d.grp[g + 1].seq_base) ++g;
+    int g, b;
+    int32_t key;
+    if (s == tid) {
+      g = g0;
+      b = b0;
+      key = key0;
+    } else {
+      g = 0;
+      while (g + 1 < d.n_groups && s >= d.grp[g + 1].seq_base) ++g;
+      b = s - d.grp[g].seq_base;
+      key = d.scratch[s];
+    }
     const GroupDesc& gd = d.grp[g];
-    const int b = s - gd.seq_base;
-    const int32_t key = d.scratch[s];
     const int32_t pos = atomicAdd(&cursor[key], gd.num_heads);
     for (int h = 0; h < gd.num_heads; ++h) d.items[pos + h] = pack_item(g, h, b);
   }

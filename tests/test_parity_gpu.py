@@ -320,6 +320,14 @@ def test_short_keys_gated_self_attention():
     compare_workload(w, ("fwd", "bwd"))
 
 
+@pytest.mark.parametrize("num_seqs,keys", [(1500, 16), (1100, 64)])
+def test_more_sequences_than_scheduler_threads(num_seqs, keys):
+    """More sequences than the work-list builder has threads (1024): its loops over sequences
+    take several rounds."""
+    w = make_workload("pffn_train", 31, num_seqs=num_seqs, len_range=(1, 40), keys=keys, scale=0.125)
+    compare_workload(w, ("fwd", "bwd"))
+
+
 # ------------------------------------------------------------------------------------------------
 # Saturated activations: scaled scores of several hundred, where sigmoid(x) is 0 or 1 in fp32 and
 # 2^(-x log2 e) overflows to +inf for x below about -88
