@@ -28,6 +28,7 @@ GDPA_ACT_SOFTMAX = 2
 GDPA_MAX_GROUPS = 16
 GDPA_FLAG_PLANNED = 1
 GDPA_FLAG_SHARED_Q = 2
+GDPA_FLAG_FP32_OUT = 4
 
 EXPORTED = ("gdpa_workspace_size", "gdpa_plan", "gdpa_fwd", "gdpa_bwd", "gdpa_fwd_grouped",
             "gdpa_bwd_grouped", "gdpa_strerror", "gdpa_version")

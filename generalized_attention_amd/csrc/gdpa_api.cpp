@@ -35,7 +35,7 @@ int check_problem(const gdpa_problem& p) {
   if (p.act < GDPA_ACT_GELU || p.act > GDPA_ACT_SOFTMAX) return GDPA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p.scale)) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.window_left < -1 || p.window_right < -1) return GDPA_ERR_INVALID_ARGUMENT;
-  if ((p.flags & ~(GDPA_FLAG_PLANNED | GDPA_FLAG_SHARED_Q)) != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((p.flags & ~(GDPA_FLAG_PLANNED | GDPA_FLAG_SHARED_Q | GDPA_FLAG_FP32_OUT)) != 0) return GDPA_ERR_INVALID_ARGUMENT;
   if (shared_q(p) && p.self_attention) return GDPA_ERR_INVALID_ARGUMENT;
   if (shared_q(p) && p.dtype != GDPA_DTYPE_BF16) return GDPA_ERR_UNSUPPORTED;
   if (p.self_attention != 0 && p.self_attention != 1) return GDPA_ERR_INVALID_ARGUMENT;
@@ -140,6 +140,7 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
     gd.delta = reinterpret_cast<float*>(base + L.delta) + L.delta_base[g];
     gd.dq32 = reinterpret_cast<float*>(base + L.dq32) + L.dq32_base[g];
     gd.shared_q = shared_q(p) ? p.max_seqlen_q : 0;
+    gd.out_f32 = p.dtype == GDPA_DTYPE_BF16 && (p.flags & GDPA_FLAG_FP32_OUT) ? 1 : 0;
     gd.q_off = p.q_offsets;
     gd.kv_off = p.kv_offsets;
     gd.num_seqs = p.num_seqs;

@@ -101,10 +101,7 @@ __global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd) {
   const f32x4* part = reinterpret_cast<const f32x4*>(gd.dq32);
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int b0 = 0; b0 < gd.num_seqs; b0 += kSeqsPerSlot) acc += part[(int64_t)b0 * cols + col];
-  u32x2 u;
-  u[0] = pack_bf16x2(acc[0] * gd.scale, acc[1] * gd.scale);
-  u[1] = pack_bf16x2(acc[2] * gd.scale, acc[3] * gd.scale);
-  reinterpret_cast<u32x2*>(gd.dq)[col] = u;
+  out_store4(out_ptr(gd.dq, gd.out_f32, (size_t)col * 4), acc * gd.scale);
 }
 
 hipError_t launch_reduce_shared_dq(const GroupDesc& gd, hipStream_t stream) {

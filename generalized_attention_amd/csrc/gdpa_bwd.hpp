@@ -210,62 +210,30 @@ __device__ __forceinline__ void take_block(BwdWave<D, NW>& st, int kb, char* lds
   take_commit<D, NW, ACT>(st, kb, lds, tr, gseq != nullptr, s);
 }
 
-// dK, dV (and dG) of an owned slot, packed to their output types, between the slot's last
-// accumulation and the stores. Accumulator register r of lane (key, g) in d-tile dt is
+// Write dK, dV (and dG) of owned slot kb. Accumulator register r of lane (key, g) in d-tile dt is
 // d = dt*32 + c_row(r, g): four runs of 4 consecutive d per lane.
 template <int D, int NW>
-struct FlushRegs {
-  u32x2 k[BwdGeo<D, NW>::DT][4];
-  u32x2 v[BwdGeo<D, NW>::DT][4];
-  float dg;
-  int key;  // sequence-local key of this lane (>= n: nothing to write)
-};
-
-template <int D, int NW>
-__device__ __forceinline__ void flush_pack(FlushRegs<D, NW>& fr, const BwdWave<D, NW>& st, int kb, float scale,
-                                           float dv_scale) {
+__device__ __forceinline__ void flush_block(BwdWave<D, NW>& st, int kb, const GroupDesc& gd, OutPtr dkseq, OutPtr dvseq,
+                                            float* dgseq, int n, float dv_scale) {
   using G = BwdGeo<D, NW>;
-  const int lane = lane_id(), kc = lane & 31;
-  fr.key = st.cur[kb] * kBwdKeyBlock + kc;
+  const int lane = lane_id(), kc = lane & 31, g = lane >> 5;
+  const int key = st.cur[kb] * kBwdKeyBlock + kc;  // sequence-local key of this lane
   const float dgsum = st.dgs[kb] + __shfl_xor(st.dgs[kb], 32);
-  fr.dg = (1.0f / (1.0f + __expf(st.graw[kb]))) * dgsum;  // sigmoid(-G) * sum_i ds_ij
-#pragma unroll
-  for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      fr.k[dt][a][0] = pack_bf16x2(st.dk[kb][dt][4 * a] * scale, st.dk[kb][dt][4 * a + 1] * scale);
-      fr.k[dt][a][1] = pack_bf16x2(st.dk[kb][dt][4 * a + 2] * scale, st.dk[kb][dt][4 * a + 3] * scale);
-      fr.v[dt][a][0] = pack_bf16x2(st.dv[kb][dt][4 * a] * dv_scale, st.dv[kb][dt][4 * a + 1] * dv_scale);
-      fr.v[dt][a][1] = pack_bf16x2(st.dv[kb][dt][4 * a + 2] * dv_scale, st.dv[kb][dt][4 * a + 3] * dv_scale);
-    }
-}
-
-template <int D, int NW>
-__device__ __forceinline__ void flush_store(const FlushRegs<D, NW>& fr, const GroupDesc& gd, bf16* dkseq, bf16* dvseq,
-                                            float* dgseq, int n) {
-  using G = BwdGeo<D, NW>;
-  const int g = lane_id() >> 5;
   const size_t rs = (size_t)gd.num_heads * D;
-  if (fr.key < n) {
+  if (key < n) {
 #pragma unroll
     for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int d = dt * 32 + a * 8 + g * 4;
-        *reinterpret_cast<u32x2*>(dkseq + fr.key * rs + d) = fr.k[dt][a];
-        *reinterpret_cast<u32x2*>(dvseq + fr.key * rs + d) = fr.v[dt][a];
+        const size_t e = key * rs + dt * 32 + a * 8 + g * 4;
+        const f32x16& k = st.dk[kb][dt];
+        const f32x16& v = st.dv[kb][dt];
+        out_store4(dkseq + e, f32x4{k[4 * a], k[4 * a + 1], k[4 * a + 2], k[4 * a + 3]} * gd.scale);
+        out_store4(dvseq + e, f32x4{v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]} * dv_scale);
       }
-    if (dgseq != nullptr && g == 0) dgseq[(size_t)fr.key * gd.num_heads] = fr.dg;
+    // sigmoid(-G) * sum_i ds_ij
+    if (dgseq != nullptr && g == 0) dgseq[(size_t)key * gd.num_heads] = (1.0f / (1.0f + __expf(st.graw[kb]))) * dgsum;
   }
-}
-
-// Write dK, dV (and dG) of owned slot kb.
-template <int D, int NW>
-__device__ __forceinline__ void flush_block(BwdWave<D, NW>& st, int kb, const GroupDesc& gd, bf16* dkseq, bf16* dvseq, float* dgseq,
-                            int n, float dv_scale) {
-  FlushRegs<D, NW> fr;
-  flush_pack<D, NW>(fr, st, kb, gd.scale, dv_scale);
-  flush_store<D, NW>(fr, gd, dkseq, dvseq, dgseq, n);
 }
 
 // Registers holding the next query tile of Q and dO (and its lse) between the global load and
@@ -374,12 +342,12 @@ struct BwdItem {
   const bf16* qseq;
   const bf16* doseq;
   const float* lseseq;
-  bf16* dqseq;
+  OutPtr dqseq;
   const bf16* kseq;
   const bf16* vseq;
   const float* gseq;
-  bf16* dkseq;
-  bf16* dvseq;
+  OutPtr dkseq;
+  OutPtr dvseq;
   float* dgseq;
   float* dq32seq;      // key chunks: fp32 dQ rows of this item (row stride rs)
   float* dsumseq;      // key chunks, softmax: D_i of this item's rows (row stride H)
@@ -526,17 +494,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   };
   auto dq_store = [&](const f32x16& acc, int rbase) {
     const int row = rbase + qh_first * 32 + lc;
-    if (row < L) {
-      u32x4 u0, u1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u0[e] = pack_bf16x2(acc[2 * e] * gd.scale, acc[2 * e + 1] * gd.scale);
-        u1[e] = pack_bf16x2(acc[8 + 2 * e] * gd.scale, acc[8 + 2 * e + 1] * gd.scale);
-      }
-      bf16* dst = it.dqseq + row * rs + dtile * 32 + g * 16;
-      *reinterpret_cast<u32x4*>(dst) = u0;
-      *reinterpret_cast<u32x4*>(dst + 8) = u1;
-    }
+    if (row < L) out_store16(it.dqseq + (row * rs + dtile * 32 + g * 16), acc, gd.scale);
   };
 
   for (int j = t0; j < t1; ++j) {
@@ -893,32 +851,16 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
               if (c != cf) v[e] += *reinterpret_cast<const f32x4*>(p32 + 4 * e);
             }
             if (c == cl && !it.shared_q) {
-              u32x4 u0, u1;
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                u0[2 * e] = pack_bf16x2(v[e][0] * gd.scale, v[e][1] * gd.scale);
-                u0[2 * e + 1] = pack_bf16x2(v[e][2] * gd.scale, v[e][3] * gd.scale);
-                u1[2 * e] = pack_bf16x2(v[2 + e][0] * gd.scale, v[2 + e][1] * gd.scale);
-                u1[2 * e + 1] = pack_bf16x2(v[2 + e][2] * gd.scale, v[2 + e][3] * gd.scale);
-              }
-              bf16* dst = it.dqseq + row * rs + dtile * 32 + g * 16;
-              *reinterpret_cast<u32x4*>(dst) = u0;
-              *reinterpret_cast<u32x4*>(dst + 8) = u1;
+              const OutPtr dst = it.dqseq + (row * rs + dtile * 32 + g * 16);
+              out_store8(dst, v[0] * gd.scale, v[1] * gd.scale);
+              out_store8(dst + 8, v[2] * gd.scale, v[3] * gd.scale);
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e) *reinterpret_cast<f32x4*>(p32 + 4 * e) = v[e];
             }
           }
         } else if (row < L) {
-          u32x4 u0, u1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            u0[e] = pack_bf16x2(acc[2 * e] * gd.scale, acc[2 * e + 1] * gd.scale);
-            u1[e] = pack_bf16x2(acc[8 + 2 * e] * gd.scale, acc[8 + 2 * e + 1] * gd.scale);
-          }
-          bf16* dst = it.dqseq + row * rs + dtile * 32 + g * 16;
-          *reinterpret_cast<u32x4*>(dst) = u0;
-          *reinterpret_cast<u32x4*>(dst + 8) = u1;
+          out_store16(it.dqseq + (row * rs + dtile * 32 + g * 16), acc, gd.scale);
         }
       }
     }
@@ -954,14 +896,14 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   it.qseq = reinterpret_cast<const bf16*>(gd.q) + (qrow * H + h) * D;
   it.doseq = reinterpret_cast<const bf16*>(gd.dout) + ((size_t)q0 * H + h) * D;
   it.lseseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
-  it.dqseq = reinterpret_cast<bf16*>(gd.dq) + ((size_t)q0 * H + h) * D;
+  it.dqseq = out_ptr(gd.dq, gd.out_f32, ((size_t)q0 * H + h) * D);
   it.dq32seq = gd.dq32 ? gd.dq32 + (dqrow * H + h) * D : nullptr;
   it.dsumseq = gd.delta ? gd.delta + (size_t)q0 * H + h : nullptr;
   it.kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
   it.vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;
   it.gseq = gd.g ? gd.g + (size_t)k0 * H + h : nullptr;
-  it.dkseq = reinterpret_cast<bf16*>(gd.dk) + ((size_t)k0 * H + h) * D;
-  it.dvseq = reinterpret_cast<bf16*>(gd.dv) + ((size_t)k0 * H + h) * D;
+  it.dkseq = out_ptr(gd.dk, gd.out_f32, ((size_t)k0 * H + h) * D);
+  it.dvseq = out_ptr(gd.dv, gd.out_f32, ((size_t)k0 * H + h) * D);
   it.dgseq = gd.dg ? gd.dg + (size_t)k0 * H + h : nullptr;
   it.kofs = 0;
   it.ntot = it.n;
@@ -979,7 +921,7 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
     } else {
       for (int idx = threadIdx.x; idx < L * G::CPR; idx += G::THREADS) {
         const int r = idx / G::CPR, c = idx % G::CPR;
-        *reinterpret_cast<u32x4*>(it.dqseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+        out_zero8(it.dqseq + (r * rs + c * 8));
       }
     }
     return;
@@ -987,8 +929,8 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   if (L <= 0) {  // no queries: dK = dV = dG = 0
     for (int idx = threadIdx.x; idx < n * G::CPR; idx += G::THREADS) {
       const int r = idx / G::CPR, c = idx % G::CPR;
-      *reinterpret_cast<u32x4*>(it.dkseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(it.dvseq + r * rs + c * 8) = u32x4{0u, 0u, 0u, 0u};
+      out_zero8(it.dkseq + (r * rs + c * 8));
+      out_zero8(it.dvseq + (r * rs + c * 8));
     }
     if (it.dgseq)
       for (int r = threadIdx.x; r < n; r += G::THREADS) it.dgseq[(size_t)r * H] = 0.0f;
@@ -1126,23 +1068,23 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
   const size_t rs = (size_t)H * D;
   const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + ((size_t)q0 * H + h) * D;
   const bf16* doseq = reinterpret_cast<const bf16*>(gd.dout) + ((size_t)q0 * H + h) * D;
-  bf16* dqseq = reinterpret_cast<bf16*>(gd.dq) + ((size_t)q0 * H + h) * D;
+  const OutPtr dqseq = out_ptr(gd.dq, gd.out_f32, ((size_t)q0 * H + h) * D);
   const bf16* kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
   const bf16* vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;
   const float* gseq = gd.g ? gd.g + (size_t)k0 * H + h : nullptr;
-  bf16* dkseq = reinterpret_cast<bf16*>(gd.dk) + ((size_t)k0 * H + h) * D;
-  bf16* dvseq = reinterpret_cast<bf16*>(gd.dv) + ((size_t)k0 * H + h) * D;
+  const OutPtr dkseq = out_ptr(gd.dk, gd.out_f32, ((size_t)k0 * H + h) * D);
+  const OutPtr dvseq = out_ptr(gd.dv, gd.out_f32, ((size_t)k0 * H + h) * D);
   float* dgseq = gd.dg ? gd.dg + (size_t)k0 * H + h : nullptr;
   constexpr int CPR = D / 8;
   if (n <= 0) {  // no keys: dQ = 0
     for (int idx = lane; idx < L * CPR; idx += kWave)
-      *reinterpret_cast<u32x4*>(dqseq + (idx / CPR) * rs + (idx % CPR) * 8) = u32x4{0u, 0u, 0u, 0u};
+      out_zero8(dqseq + ((idx / CPR) * rs + (idx % CPR) * 8));
     return;
   }
   if (L <= 0) {  // no queries: dK = dV = dG = 0
     for (int idx = lane; idx < n * CPR; idx += kWave) {
-      *reinterpret_cast<u32x4*>(dkseq + (idx / CPR) * rs + (idx % CPR) * 8) = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(dvseq + (idx / CPR) * rs + (idx % CPR) * 8) = u32x4{0u, 0u, 0u, 0u};
+      out_zero8(dkseq + ((idx / CPR) * rs + (idx % CPR) * 8));
+      out_zero8(dvseq + ((idx / CPR) * rs + (idx % CPR) * 8));
     }
     if (dgseq)
       for (int r = lane; r < n; r += kWave) dgseq[(size_t)r * H] = 0.0f;
@@ -1251,17 +1193,7 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(wl + G::OFF_KT + drow * G::KTROW + (k * 16 + g * 8) * 2));
         acc = mfma32(ka, sx_operand<G::SXROW>(wl, G::OFF_SX, k * 16, 0), acc);
       }
-      if (row < L) {
-        u32x4 u0, u1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u0[e] = pack_bf16x2(acc[2 * e] * gd.scale, acc[2 * e + 1] * gd.scale);
-          u1[e] = pack_bf16x2(acc[8 + 2 * e] * gd.scale, acc[8 + 2 * e + 1] * gd.scale);
-        }
-        bf16* dst = dqseq + row * rs + dt * 32 + g * 16;
-        *reinterpret_cast<u32x4*>(dst) = u0;
-        *reinterpret_cast<u32x4*>(dst + 8) = u1;
-      }
+      if (row < L) out_store16(dqseq + (row * rs + dt * 32 + g * 16), acc, gd.scale);
     }
     lds_wave_sync();  // every read of this tile's LDS areas is done before the next tile's stores
   }
@@ -1272,14 +1204,9 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
     for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int d = dt * 32 + a * 8 + g * 4;
-        u32x2 uk, uv;
-        uk[0] = pack_bf16x2(dk[dt][4 * a] * gd.scale, dk[dt][4 * a + 1] * gd.scale);
-        uk[1] = pack_bf16x2(dk[dt][4 * a + 2] * gd.scale, dk[dt][4 * a + 3] * gd.scale);
-        uv[0] = pack_bf16x2(dv[dt][4 * a] * dv_scale, dv[dt][4 * a + 1] * dv_scale);
-        uv[1] = pack_bf16x2(dv[dt][4 * a + 2] * dv_scale, dv[dt][4 * a + 3] * dv_scale);
-        *reinterpret_cast<u32x2*>(dkseq + lc * rs + d) = uk;
-        *reinterpret_cast<u32x2*>(dvseq + lc * rs + d) = uv;
+        const size_t e = lc * rs + dt * 32 + a * 8 + g * 4;
+        out_store4(dkseq + e, f32x4{dk[dt][4 * a], dk[dt][4 * a + 1], dk[dt][4 * a + 2], dk[dt][4 * a + 3]} * gd.scale);
+        out_store4(dvseq + e, f32x4{dv[dt][4 * a], dv[dt][4 * a + 1], dv[dt][4 * a + 2], dv[dt][4 * a + 3]} * dv_scale);
       }
     if (dgseq != nullptr && g == 0) dgseq[(size_t)lc * H] = (1.0f / (1.0f + __expf(graw))) * dgsum;
   }

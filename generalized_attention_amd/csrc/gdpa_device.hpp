@@ -50,6 +50,7 @@ struct GroupDesc {
   int32_t wr;
   int32_t seq_base;   // index of this group's first sequence in the global sequence numbering
   int32_t shared_q;   // rows of a query matrix shared by every sequence (0: per-sequence queries)
+  int32_t out_f32;    // bf16 problem whose outputs o, dq, dk, dv are float32
 };
 
 struct LaunchDesc {
@@ -144,6 +145,39 @@ __device__ inline float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u
 __device__ inline float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
 __device__ inline bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// An output tensor of a bf16 problem: bf16 elements, or float32 ones when the caller asked for
+// float32 outputs. Offsets count elements; stores take fp32 values and round them only for bf16.
+struct OutPtr {
+  char* p;
+  int32_t f32;
+  __device__ inline OutPtr operator+(size_t e) const { return OutPtr{p + (e << (f32 ? 2 : 1)), f32}; }
+};
+__device__ inline OutPtr out_ptr(void* base, int32_t f32, size_t e) { return OutPtr{static_cast<char*>(base), f32} + e; }
+// 8 consecutive elements a[0..3], b[0..3] (16-byte aligned for bf16, 32-byte for float32)
+__device__ inline void out_store8(OutPtr o, const f32x4& a, const f32x4& b) {
+  if (o.f32) {
+    reinterpret_cast<f32x4*>(o.p)[0] = a;
+    reinterpret_cast<f32x4*>(o.p)[1] = b;
+  } else {
+    *reinterpret_cast<u32x4*>(o.p) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                           pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+  }
+}
+// 4 consecutive elements
+__device__ inline void out_store4(OutPtr o, const f32x4& a) {
+  if (o.f32) *reinterpret_cast<f32x4*>(o.p) = a;
+  else *reinterpret_cast<u32x2*>(o.p) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+}
+// 16 consecutive elements: a C tile's registers 0..15 of one lane, times s
+__device__ inline void out_store16(OutPtr o, const f32x16& c, float s) {
+  out_store8(o, f32x4{c[0], c[1], c[2], c[3]} * s, f32x4{c[4], c[5], c[6], c[7]} * s);
+  out_store8(o + 8, f32x4{c[8], c[9], c[10], c[11]} * s, f32x4{c[12], c[13], c[14], c[15]} * s);
+}
+__device__ inline void out_zero8(OutPtr o) {
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  out_store8(o, z, z);
+}
 
 // ----------------------------------------------------------------------------------------------
 // Activations in fp32 registers.

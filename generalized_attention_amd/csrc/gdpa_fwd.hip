@@ -344,7 +344,7 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
 // Epilogue of one wave tile: softmax normalisation and lse, or the deferred score scale of the
 // element-wise forms; each lane stores 16 consecutive d of one row.
 template <int D, int NKV, int ACT, int QS, bool GATED>
-__device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, QS>& acc, bf16* oseq, float* lseq,
+__device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, QS>& acc, OutPtr oseq, float* lseq,
                                            int L, int row0) {
   using G = FwdGeo<D, NKV>;
   const int lane = lane_id(), qc = lane & 31, g = lane >> 5;
@@ -364,15 +364,10 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
     if (row < L) {
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt) {
-        u32x4 u0, u1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u0[e] = pack_bf16x2(acc.o[qs][dt][2 * e] * inv, acc.o[qs][dt][2 * e + 1] * inv);
-          u1[e] = pack_bf16x2(acc.o[qs][dt][8 + 2 * e] * inv, acc.o[qs][dt][8 + 2 * e + 1] * inv);
-        }
-        bf16* dst = oseq + row * rs + dt * 32 + g * 16;
-        *reinterpret_cast<u32x4*>(dst) = u0;
-        *reinterpret_cast<u32x4*>(dst + 8) = u1;
+        const f32x16& o = acc.o[qs][dt];
+        const OutPtr dst = oseq + (row * rs + dt * 32 + g * 16);
+        out_store8(dst, f32x4{o[0], o[1], o[2], o[3]} * inv, f32x4{o[4], o[5], o[6], o[7]} * inv);
+        out_store8(dst + 8, f32x4{o[8], o[9], o[10], o[11]} * inv, f32x4{o[12], o[13], o[14], o[15]} * inv);
       }
       if (softmax && g == 0) lseq[(size_t)row * H] = lse;
     }
@@ -381,7 +376,7 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
 
 // One wave tile against staged key blocks [kb0, kb1), then its epilogue.
 template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED>
-__device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, bf16* oseq,
+__device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, OutPtr oseq,
                                          float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   FwdAcc<D, QS> acc;
   acc_init(acc);
@@ -410,7 +405,7 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
   // a shared query matrix (seed queries): every sequence reads its query rows from row 0
   const size_t qrow = gd.shared_q ? 0 : (size_t)q0;
   const bf16* qseq = reinterpret_cast<const bf16*>(gd.q) + (qrow * H + h) * D;
-  bf16* oseq = reinterpret_cast<bf16*>(gd.o) + ((size_t)q0 * H + h) * D;
+  const OutPtr oseq = out_ptr(gd.o, gd.out_f32, ((size_t)q0 * H + h) * D);
   float* lseq = gd.lse ? gd.lse + (size_t)q0 * H + h : nullptr;
   const bf16* kseq = reinterpret_cast<const bf16*>(gd.k) + ((size_t)k0 * H + h) * D;
   const bf16* vseq = reinterpret_cast<const bf16*>(gd.v) + ((size_t)k0 * H + h) * D;

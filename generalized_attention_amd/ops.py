@@ -37,6 +37,11 @@ class GroupArgs:
     head_acts: Optional[torch.Tensor] = None  # int32 [H] on the device: activation per head
     shared_q: bool = False  # q is one query matrix shared by every sequence (rows of o: total_q)
     total_q: Optional[int] = None  # rows of o / lse / dout (default: rows of q)
+    fp32_out: bool = False  # bf16 problem with float32 o, dq, dk, dv
+
+    @property
+    def out_dtype(self) -> torch.dtype:
+        return torch.float32 if self.fp32_out else self.q.dtype
 
     @property
     def rows(self) -> int:
@@ -60,7 +65,8 @@ class GroupArgs:
         p.max_seqlen_q = int(self.max_seqlen_q)
         p.max_seqlen_kv = int(self.max_seqlen_kv)
         p.self_attention = 1 if self.self_attention else 0
-        p.flags = (_lib.GDPA_FLAG_PLANNED if self.planned else 0) | (_lib.GDPA_FLAG_SHARED_Q if self.shared_q else 0)
+        p.flags = ((_lib.GDPA_FLAG_PLANNED if self.planned else 0) | (_lib.GDPA_FLAG_SHARED_Q if self.shared_q else 0)
+                   | (_lib.GDPA_FLAG_FP32_OUT if self.fp32_out else 0))
         p.q_offsets = self.q_offsets.data_ptr()
         p.kv_offsets = self.kv_offsets.data_ptr()
         p.head_acts = 0 if self.head_acts is None else self.head_acts.data_ptr()
@@ -69,11 +75,12 @@ class GroupArgs:
 
 def make_group(q, k, v, q_offsets, kv_offsets, *, act, scale: float, window=(-1, -1), g=None,
                self_attention: Optional[bool] = None, lengths_q=None, lengths_kv=None,
-               shared_q: bool = False) -> GroupArgs:
+               shared_q: bool = False, fp32_out: bool = False) -> GroupArgs:
     """Build GroupArgs from device tensors. Offsets may be given on the host (int64 numpy/torch)
     or the device; the max lengths come from host lengths when given (no device sync).
     act: an activation name, or a sequence with one name per head. shared_q: q is one [S, H, d]
-    query matrix whose row i is query row i of every sequence (each sequence has <= S rows)."""
+    query matrix whose row i is query row i of every sequence (each sequence has <= S rows).
+    fp32_out: a bf16 problem writes o, dq, dk, dv in float32."""
     dev = q.device
     head_acts = None
     if not isinstance(act, str):
@@ -100,7 +107,8 @@ def make_group(q, k, v, q_offsets, kv_offsets, *, act, scale: float, window=(-1,
     return GroupArgs(q=q, k=k, v=v, q_offsets=qo, kv_offsets=ko, act=act, scale=scale,
                      max_seqlen_q=max_q, max_seqlen_kv=int(max(lengths_kv, default=0)),
                      window=tuple(window), g=g, self_attention=bool(self_attention), head_acts=head_acts,
-                     shared_q=bool(shared_q), total_q=int(sum(lengths_q)) if shared_q else None)
+                     shared_q=bool(shared_q), total_q=int(sum(lengths_q)) if shared_q else None,
+                     fp32_out=bool(fp32_out))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> int:
@@ -133,7 +141,7 @@ def _fwd_tensors(grp: GroupArgs, o, lse) -> _lib.gdpa_tensors:
 
 
 def _alloc_fwd(grp: GroupArgs):
-    o = torch.empty((grp.rows,) + tuple(grp.q.shape[1:]), dtype=grp.q.dtype, device=grp.q.device)
+    o = torch.empty((grp.rows,) + tuple(grp.q.shape[1:]), dtype=grp.out_dtype, device=grp.q.device)
     lse = None
     if grp.may_softmax:
         lse = torch.empty(grp.rows, grp.q.shape[1], dtype=torch.float32, device=grp.q.device)
@@ -161,7 +169,9 @@ def _bwd_tensors(grp: GroupArgs, dout, o, lse, dq, dk, dv, dg) -> _lib.gdpa_tens
 
 
 def _alloc_bwd(grp: GroupArgs, want_dg: bool):
-    dq, dk, dv = torch.empty_like(grp.q), torch.empty_like(grp.k), torch.empty_like(grp.v)
+    dt = grp.out_dtype
+    dq, dk, dv = (torch.empty_like(grp.q, dtype=dt), torch.empty_like(grp.k, dtype=dt),
+                  torch.empty_like(grp.v, dtype=dt))
     dg = torch.empty_like(grp.g) if (want_dg and grp.g is not None) else None
     return dq, dk, dv, dg
 

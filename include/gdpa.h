@@ -60,6 +60,14 @@ extern "C" {
  * at most max_seqlen_q. bf16 only; not with self_attention (hence no window). */
 #define GDPA_FLAG_SHARED_Q 2
 
+/* gdpa_problem.flags: float32 outputs for a bf16 problem. o (forward) and dq, dk, dv (backward)
+ * are float32 arrays of the same shapes; q, k, v and dout stay bf16. The arithmetic is unchanged
+ * (bf16 MFMA operands, P and dS rounded once to bf16, fp32 accumulation); only the final rounding
+ * of the results to bf16 is left out, which removes the largest term of their error against the
+ * exact result. Groups of one call may differ in it. No effect on a float32 problem, whose
+ * outputs are float32 already. */
+#define GDPA_FLAG_FP32_OUT 4
+
 typedef enum gdpa_status {
   GDPA_OK = 0,
   GDPA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, inconsistent window, ... */
@@ -112,7 +120,8 @@ typedef struct gdpa_tensors {
   void* o;           /* forward output [total_q, H, d] */
   float* lse;        /* forward output [total_q, H] natural-log row log-sum-exp; softmax only */
   const void* dout;  /* backward input: dL/dO [total_q, H, d] */
-  void* dq;          /* backward outputs, same layout and dtype as q, k, v */
+  void* dq;          /* backward outputs, same layout as q, k, v; their dtype, or float32 with
+                        GDPA_FLAG_FP32_OUT (o too) */
   void* dk;
   void* dv;
   float* dg;         /* gate gradient [total_kv, H] float32; NULL if not wanted */

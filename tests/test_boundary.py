@@ -122,6 +122,14 @@ def test_workspace_size_key_chunks(lib):
     assert _lib.gdpa_workspace_size([wide], 1) - base >= 1200 * 4 * 64 * 4
 
 
+def test_fp32_output_flag():
+    """float32 outputs change no workspace, in either pass, and are accepted (a no-op) in fp32."""
+    for pass_ in (0, 1):
+        base = _lib.gdpa_workspace_size([good_problem()], pass_)
+        assert _lib.gdpa_workspace_size([good_problem(flags=_lib.GDPA_FLAG_FP32_OUT)], pass_) == base
+    assert _lib.gdpa_workspace_size([good_problem(flags=_lib.GDPA_FLAG_FP32_OUT, dtype=_lib.GDPA_DTYPE_FP32)], 0) > 0
+
+
 INVALID_PROBLEMS = [
     ("negative seqs", dict(num_seqs=-1), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("zero heads", dict(num_heads=0), _lib.GDPA_ERR_INVALID_ARGUMENT),
@@ -132,7 +140,7 @@ INVALID_PROBLEMS = [
     ("nan scale", dict(scale=float("nan")), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window below -1", dict(window_left=-2), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window on cross-attention", dict(window_left=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
-    ("unknown flag", dict(flags=4), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("unknown flag", dict(flags=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("shared queries in self-attention", dict(flags=_lib.GDPA_FLAG_SHARED_Q, self_attention=1, total_kv=100,
                                               max_seqlen_kv=60), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("shared queries in fp32", dict(flags=_lib.GDPA_FLAG_SHARED_Q, dtype=_lib.GDPA_DTYPE_FP32), _lib.GDPA_ERR_UNSUPPORTED),

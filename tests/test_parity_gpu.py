@@ -38,14 +38,15 @@ def run_bwd(groups_dev, douts, fwd_outs, want_dg):
     return ga.gdpa_bwd_grouped(groups_dev, douts, fwd_outs=fwd_outs, want_dg=want_dg)
 
 
-def compare_workload(w, passes, sample=None, want_dg=True, scale=None):
-    """Run the workload on the GPU; compare all (or the sampled) sequences with the oracle."""
+def compare_workload(w, passes, sample=None, want_dg=True, scale=None, fp32_out=False):
+    """Run the workload on the GPU; compare all (or the sampled) sequences with the oracle.
+    fp32_out: the bf16 groups write float32 outputs (checked by the literal rule)."""
     groups = w.groups
     if scale is not None:
         import dataclasses
         for g in groups:
             g.spec = dataclasses.replace(g.spec, scale=scale)
-    dev = [device_group(g) for g in groups]
+    dev = [device_group(g, fp32_out=fp32_out) for g in groups]
     print(f"[gpu] {w.name} seed={w.seed} groups={len(groups)} T={[g.total_q for g in groups][:3]} "
           f"passes={passes}", flush=True)
     fwd_outs = run_fwd(dev)
@@ -71,6 +72,9 @@ def compare_workload(w, passes, sample=None, want_dg=True, scale=None):
         qr = rows_of(g.q_offsets, seqs)
         kr = rows_of(g.kv_offsets, seqs)
         dt = g.spec.dtype
+        if fp32_out and dt == "bf16":
+            dt = "bf16/f32"
+            assert fwd_outs[gi][0].dtype == torch.float32
         ref = oracle.group_fwd(sub)
         o, lse = fwd_outs[gi]
         report[f"g{gi}.o"] = chk(dt, to64(o)[qr], ref["o"], f"{w.name} g{gi} O")
@@ -326,6 +330,24 @@ def test_more_sequences_than_scheduler_threads(num_seqs, keys):
     take several rounds."""
     w = make_workload("pffn_train", 31, num_seqs=num_seqs, len_range=(1, 40), keys=keys, scale=0.125)
     compare_workload(w, ("fwd", "bwd"))
+
+
+# ------------------------------------------------------------------------------------------------
+# float32 outputs of bf16 problems: every store path (forward epilogue, dQ per tile, dQ from fp32
+# key-chunk rows, the shared-query sum, dK / dV flushes, the short-key kernel, empty items)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,kw", [
+    ("pffn_train", dict(num_seqs=9, len_range=(1, 400), scale=0.125)),
+    ("pffn_train", dict(num_seqs=7, len_range=(1, 300), keys=24, act="gelu", scale=0.125)),
+    ("pffn_train", dict(num_seqs=4, len_range=(1, 300), keys=600, scale=0.125)),
+    ("causal_gated", dict(num_seqs=5, len_range=(1, 400))),
+    ("causal_gated", dict(lengths=[0, 1, 33, 0, 64, 129], act="silu")),
+    ("seed_pool", dict(num_seqs=5, len_range=(1, 600))),
+    ("grouped10", dict(num_seqs=3, len_range=(1, 70))),
+])
+def test_fp32_outputs(name, kw):
+    compare_workload(make_workload(name, 17, **kw), ("fwd", "bwd"), fp32_out=True)
 
 
 # ------------------------------------------------------------------------------------------------
