@@ -8,6 +8,11 @@ sequences with lengths uniform in [100, 1000], H=4, d=64, n=256 context-generate
 sample, SiLU, scale 1/1000 (seed 0 of the input recipe; synthetic data).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pffn_train] [--no-cpu-baseline]
+
+Besides the contract fields the line carries kernel_ms (mean per-kernel times), timing (p10 / p50
+/ p90 of the step, the forward and the backward, and of a cold step that follows a 512 MiB write
+flushing the Infinity Cache), roofline (the dominant kernel against its bound), mfma_reference (a
+measured large bf16 library GEMM rate and the active core clock) and cpu_baseline (the oracle).
 """
 
 from __future__ import annotations
@@ -68,6 +73,64 @@ def load_traffic(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
+def percentiles(xs):
+    """p10 / p50 / p90 of a list of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)), "p90": float(np.percentile(a, 90))}
+
+
+def observed_sclk_mhz():
+    """The GPU core clock level marked active in sysfs (first card that reports one), or None."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def measured_gemm_tflops(torch):
+    """A reachable dense bf16 MFMA rate on this GPU: a large library GEMM (8192^3, hipBLASLt via
+    torch.matmul), best of 10 runs, and the core clock read while GEMMs keep the GPU busy. A
+    reference point for the kernels, not part of the path. Returns (TFLOP/s, MHz or None)."""
+    n = 8192
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    for _ in range(40):  # ~40 ms of queued work; the clock is sampled while it runs
+        torch.matmul(a, b)
+    time.sleep(0.01)
+    sclk = observed_sclk_mhz()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 / (best * 1e-3) / 1e12, sclk
+
+
+def cpu_model_name():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(workload, passes, seqs: int):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -91,6 +154,7 @@ def cpu_baseline(workload, passes, seqs: int):
         elapsed += time.perf_counter() - t0
         flops += wk["fwd_flops"] + (wk["bwd_flops"] if "bwd" in passes else 0.0)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model_name(),
             "sample": f"{picked} sequences drawn from the same workload (seeded), fwd{'+bwd' if 'bwd' in passes else ''}, "
                       f"{elapsed:.1f} s, {flops / 1e9:.2f} GFLOP of model work"}
 
@@ -198,6 +262,22 @@ def main():
         k_ms["plan"] += e[0].elapsed_time(e[1]) / args.steps
         k_ms["fwd"] += e[1].elapsed_time(e[2]) / args.steps
         k_ms["bwd"] += e[2].elapsed_time(e[3]) / args.steps
+    timing = {"step_ms": percentiles([e[0].elapsed_time(e[3]) for e in evs]),
+              "fwd_ms": percentiles([e[1].elapsed_time(e[2]) for e in evs])}
+    if "bwd" in passes:
+        timing["bwd_ms"] = percentiles([e[2].elapsed_time(e[3]) for e in evs])
+    # cold: a 512 MiB write (twice the 256 MB Infinity Cache) between steps, outside the events
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = min(args.steps, 50)
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
+    for i in range(n_cold):
+        flush.zero_()
+        cold[i][0].record()
+        step()
+        cold[i][1].record()
+    torch.cuda.synchronize()
+    timing["cold_step_ms"] = percentiles([c[0].elapsed_time(c[1]) for c in cold])
+    del flush
     for o in fwd_outs + [tuple(b[:3]) for b in bwd_outs]:
         for t in o:
             if t is not None and not torch.isfinite(t).all():
@@ -245,8 +325,12 @@ def main():
         "pct_of_mfma_peak": 100.0 * tflops / MFMA_PEAK_BF16_TFLOPS,
         "hbm_gbps_step": (work["fwd_bytes"] + (work["bwd_bytes"] if "bwd" in passes else 0.0)) / (ms_per_step * 1e-3) / 1e9,
         "kernel_ms": k_ms,
+        "timing": timing,
         "roofline": roof,
     }
+    gemm, sclk = measured_gemm_tflops(torch)
+    out["mfma_reference"] = {"measured_gemm_tflops": gemm, "step_frac_of_measured": tflops / gemm,
+                             "sclk_mhz_under_gemm": sclk}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, passes, args.cpu_seqs)
     else:
