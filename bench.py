@@ -172,7 +172,7 @@ def main():
                     help="run only a plain 512 MiB device-to-device copy (scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the GDPA path has no "
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); the GDPA path has no "
               f"cross-GPU step and is run per GPU on its share of the batch.", file=sys.stderr)
         sys.exit(2)
 

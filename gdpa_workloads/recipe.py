@@ -125,9 +125,9 @@ def _lengths(rng, b: int, lo_hi: Tuple[int, int]) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
-# Workload registry. Shapes follow the pages' workload descriptions; where the pages leave a value
-# open (dtype, score scale) the recipe takes one reading: bf16 for the training shapes, scale
-# 1/L_max for the pointwise forms, 1/sqrt(d) for the softmax form.
+# Workload registry. Shapes follow the workload descriptions of the Kunlun review and README;
+# where they leave a value open (dtype, score scale) the recipe takes one reading: bf16 for the
+# training shapes, scale 1/L_max for the pointwise forms, 1/sqrt(d) for the softmax form.
 # ----------------------------------------------------------------------------------------------
 CONFIGS: Dict[str, str] = {
     "tiny_fp32": "tiny PFFN-form GDPA fp32: B=4, L in [1,64], H=2, d=32, n=64, GELU, fwd",

@@ -1,8 +1,8 @@
 // Jagged work decomposition: one workgroup builds the longest-first list of
 // (group, head, sequence) work items from the device offsets.
 //
-// The pages name tile scheduling over jagged, large-batch inputs as one of the GDPA kernel's
-// levers (Kunlun review, section 2.3). Here a work item is one whole (sequence, head) pair; the
+// The Kunlun review (section 2.3) names tile scheduling over jagged, large-batch inputs as one of
+// the GDPA kernel's levers. Here a work item is one whole (sequence, head) pair; the
 // main kernels take items in list order, one workgroup per item, and the hardware dispatcher
 // hands the next item to whichever compute unit frees up first, so a longest-first order gives
 // the classic LPT balance without a persistent kernel or atomics in the main kernels.

@@ -9,13 +9,14 @@ What they compare against (none of it re-types the oracle's formulas):
   * torch library routines in float64: ``torch.nn.functional.gelu`` (exact erf form),
     ``silu``, ``logsigmoid``, ``scaled_dot_product_attention`` and autograd;
   * closed-form worked examples (``tests/golden/worked_examples.json``);
-  * identities the pages state: the element-wise form equals the back-to-back product
+  * identities the sources state: the element-wise form equals the back-to-back product
     act(X W1) W2 (Kunlun review, section 2.3 / Figure 2; substack breakdown, "Core
     Architecture"), softmax rows sum to one, a gate of +inf reduces the gated form to plain
     scaled dot-product attention (reproduction README, "Core equations"), a window at least as
     long as the sequence equals full attention (review, section 2.5);
   * central finite differences of the oracle's own forward for its backward;
-  * invariants: sample independence, zero upstream gradient, zero-sum key gradients of softmax.
+  * invariants: sample independence, permutation equivariance over sequences, zero upstream
+    gradient, zero-sum key gradients of softmax.
 """
 
 from __future__ import annotations
@@ -297,6 +298,26 @@ def check_invariants(orc):
     pert = orc.fwd(pb["q"], k2, pb["v"], pb["qo"], pb["ko"], act="gelu", scale=0.6)["o"]
     assert np.array_equal(base[:4], pert[:4])
     assert not np.array_equal(base[4:], pert[4:])
+    # permutation equivariance: the sequences in reverse order give the same per-sequence results
+    lq, lk = [3, 0, 5, 2], [4, 2, 3, 1]
+    pb = rand_problem(10, lq, lk, gate=True)
+    fw = orc.fwd(pb["q"], pb["k"], pb["v"], pb["qo"], pb["ko"], act="silu", scale=0.7, g=pb["g"])
+    bw = orc.bwd(pb["q"], pb["k"], pb["v"], pb["do"], pb["qo"], pb["ko"], act="silu", scale=0.7, g=pb["g"],
+                 want_dg=True)
+    order = [3, 2, 1, 0]
+
+    def rows(off, b):
+        return np.arange(off[b], off[b + 1])
+
+    qi = np.concatenate([rows(pb["qo"], b) for b in order])
+    ki = np.concatenate([rows(pb["ko"], b) for b in order])
+    qo2, ko2 = offsets([lq[b] for b in order]), offsets([lk[b] for b in order])
+    fw2 = orc.fwd(pb["q"][qi], pb["k"][ki], pb["v"][ki], qo2, ko2, act="silu", scale=0.7, g=pb["g"][ki])
+    bw2 = orc.bwd(pb["q"][qi], pb["k"][ki], pb["v"][ki], pb["do"][qi], qo2, ko2, act="silu", scale=0.7,
+                  g=pb["g"][ki], want_dg=True)
+    assert np.array_equal(fw["o"][qi], fw2["o"]) and np.array_equal(bw["dq"][qi], bw2["dq"])
+    for n in ("dk", "dv", "dg"):
+        assert np.array_equal(bw[n][ki], bw2[n]), n
 
 
 def check_activation_closed_forms(lib):
