@@ -8,11 +8,12 @@ sequences with lengths uniform in [100, 1000], H=4, d=64, n=256 context-generate
 sample, SiLU, scale 1/1000 (seed 0 of the input recipe; synthetic data).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pffn_train] [--no-cpu-baseline]
+                      [--no-cold]
 
 Besides the contract fields the line carries kernel_ms (mean per-kernel times), timing (p10 / p50
 / p90 of the step, the forward and the backward, and of a cold step that follows a 512 MiB write
 flushing the Infinity Cache), roofline (the dominant kernel against its bound), mfma_reference (a
-measured large bf16 library GEMM rate and the active core clock) and cpu_baseline (the oracle).
+measured large bf16 library GEMM rate) and cpu_baseline (the oracle).
 """
 
 from __future__ import annotations
@@ -80,24 +81,9 @@ def percentiles(xs):
     return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)), "p90": float(np.percentile(a, 90))}
 
 
-def observed_sclk_mhz():
-    """The GPU core clock level marked active in sysfs (first card that reports one), or None."""
-    import glob
-    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            with open(f) as fh:
-                for line in fh:
-                    if line.rstrip().endswith("*"):
-                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
-        except (OSError, ValueError, IndexError):
-            continue
-    return None
-
-
 def measured_gemm_tflops(torch):
     """A reachable dense bf16 MFMA rate on this GPU: a large library GEMM (8192^3, hipBLASLt via
-    torch.matmul), best of 10 runs, and the core clock read while GEMMs keep the GPU busy. A
-    reference point for the kernels, not part of the path. Returns (TFLOP/s, MHz or None)."""
+    torch.matmul), best of 10 runs. A reference point for the kernels, not part of the path."""
     n = 8192
     a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
     b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
@@ -112,12 +98,7 @@ def measured_gemm_tflops(torch):
         e1.record()
         torch.cuda.synchronize()
         best = min(best, e0.elapsed_time(e1))
-    for _ in range(40):  # ~40 ms of queued work; the clock is sampled while it runs
-        torch.matmul(a, b)
-    time.sleep(0.01)
-    sclk = observed_sclk_mhz()
-    torch.cuda.synchronize()
-    return 2.0 * n ** 3 / (best * 1e-3) / 1e12, sclk
+    return 2.0 * n ** 3 / (best * 1e-3) / 1e12
 
 
 def cpu_model_name():
@@ -168,6 +149,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps (keeps a profiler's per-kernel averages to the warm steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (scales HBM byte counters)")
     args = ap.parse_args()
@@ -266,18 +249,19 @@ def main():
               "fwd_ms": percentiles([e[1].elapsed_time(e[2]) for e in evs])}
     if "bwd" in passes:
         timing["bwd_ms"] = percentiles([e[2].elapsed_time(e[3]) for e in evs])
-    # cold: a 512 MiB write (twice the 256 MB Infinity Cache) between steps, outside the events
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    n_cold = min(args.steps, 50)
-    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
-    for i in range(n_cold):
-        flush.zero_()
-        cold[i][0].record()
-        step()
-        cold[i][1].record()
-    torch.cuda.synchronize()
-    timing["cold_step_ms"] = percentiles([c[0].elapsed_time(c[1]) for c in cold])
-    del flush
+    if not args.no_cold:
+        # cold: a 512 MiB write (twice the 256 MB Infinity Cache) between steps, outside the events
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        n_cold = min(args.steps, 50)
+        cold = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
+        for i in range(n_cold):
+            flush.zero_()
+            cold[i][0].record()
+            step()
+            cold[i][1].record()
+        torch.cuda.synchronize()
+        timing["cold_step_ms"] = percentiles([c[0].elapsed_time(c[1]) for c in cold])
+        del flush
     for o in fwd_outs + [tuple(b[:3]) for b in bwd_outs]:
         for t in o:
             if t is not None and not torch.isfinite(t).all():
@@ -328,9 +312,8 @@ def main():
         "timing": timing,
         "roofline": roof,
     }
-    gemm, sclk = measured_gemm_tflops(torch)
-    out["mfma_reference"] = {"measured_gemm_tflops": gemm, "step_frac_of_measured": tflops / gemm,
-                             "sclk_mhz_under_gemm": sclk}
+    gemm = measured_gemm_tflops(torch)
+    out["mfma_reference"] = {"measured_gemm_tflops": gemm, "step_frac_of_measured": tflops / gemm}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, passes, args.cpu_seqs)
     else:
