@@ -222,7 +222,7 @@ __device__ __forceinline__ void acc_init(FwdAcc<D, QS>& a) {
 // (keys from kend on are invalid) and sits in LDS block slot b, or b mod NKV / 32 (RING).
 // GATED: the problem has a gate. MASKED: entries may need an explicit mask (the softmax form, or
 // a window); without it, keys past the end meet zero K and V rows in LDS and phi(0) = 0.
-template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool RING = false>
+template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool RING = false, bool PIPE = true>
 __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf,
                                                FwdAcc<D, QS>& acc, int row0, int kbase, int kend, int kb0,
                                                int kb1) {
@@ -319,6 +319,16 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
       }
   };
 
+  if constexpr (!PIPE) {
+    // one score buffer: with four waves per SIMD the other waves' element-wise work covers each
+    // wave's MFMA chain, and the 16 registers of a second buffer are worth more as headroom
+    f32x16 sa[QS];
+    for (int kb = kb0; kb < kb1; ++kb) {
+      scores_block<D, NKV, QS>(lds, qf, kb & smask, sa);
+      process(kb, sa);
+    }
+    return;
+  }
   // Software pipeline over pairs of blocks with two score buffers: the score MFMAs of the next
   // block are issued before the element-wise work of the current one, so the matrix cores run
   // while the vector units evaluate the activation; the loop body has no branches.
@@ -375,12 +385,12 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
 }
 
 // One wave tile against staged key blocks [kb0, kb1), then its epilogue.
-template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED>
+template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool PIPE>
 __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, OutPtr oseq,
                                          float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   FwdAcc<D, QS> acc;
   acc_init(acc);
-  fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED>(lds, gd, qf, acc, row0, klo, klo + span, kb0, kb1);
+  fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, false, PIPE>(lds, gd, qf, acc, row0, klo, klo + span, kb0, kb1);
   fwd_finish<D, NKV, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
 }
 
@@ -432,7 +442,8 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
-      fwd_tile<D, NKV, ACT, QS, GATED, MASKED>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
+      // (8 waves: four per SIMD, no software pipeline inside a wave; 4 waves: two per SIMD, with it)
+      fwd_tile<D, NKV, ACT, QS, GATED, MASKED, NW == 4>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       if (kPrefetchQ) qcur = qnext;
     }
   } else if (LONG && D < 128 && fwd_ring_fits<D, NKV>(gd.wl, gd.wr, NW * RW)) {
