@@ -427,6 +427,46 @@ def test_maximum_head_count():
         compare_workload(w, ("fwd", "bwd"))
 
 
+def with_head_dim(w, heads, d, seed):
+    """The workload's sequences and options with fresh N(0,1) inputs of another head count / dim."""
+    import dataclasses
+    g = w.groups[0]
+    rng = np.random.default_rng(seed)
+    g.spec = dataclasses.replace(g.spec, num_heads=heads, head_dim=d, scale=1.0 / math.sqrt(d))
+    t, n = g.total_q, g.total_kv
+
+    def draw(rows):
+        return torch.from_numpy(rng.standard_normal((rows, heads, d))).to(torch.bfloat16)
+
+    g.q, g.k, g.v, g.dout = draw(t), draw(n), draw(n), draw(t)
+    if g.g is not None:
+        g.g = torch.from_numpy(rng.standard_normal((n, heads))).to(torch.float32)
+    return w
+
+
+HEAD_DIM_CASES = [
+    # (head dim, workload, overrides): d = 128 holds 128 keys per workgroup in the backward and
+    # stages 128 keys at a time in the forward; d = 32 holds 256 and 512
+    (128, "pffn_train", dict(keys=100, act="gelu")),
+    (128, "pffn_train", dict(keys=300, act="silu")),
+    (128, "causal_gated", dict(act="softmax")),
+    (128, "causal_gated", dict(act="silu", window=(-1, -1))),
+    (32, "pffn_train", dict(keys=300, act="silu")),
+    (32, "pffn_train", dict(keys=600, act="gelu")),
+    (32, "causal_gated", dict(act="softmax")),
+    (32, "causal_gated", dict(act="gelu", window=(40, 40))),
+]
+
+
+@pytest.mark.parametrize("d,name,kw", HEAD_DIM_CASES,
+                         ids=[f"d{d}-{n}-{'-'.join(f'{k}{v}' for k, v in kw.items())}" for d, n, kw in HEAD_DIM_CASES])
+def test_head_dims(d, name, kw):
+    """Head dims 32 and 128 through the single-problem launches (resident keys, key chunks, ring
+    windows, both backward forms), with ragged lengths over several tiles."""
+    w = make_workload(name, 23, num_seqs=4, len_range=(1, 450), **kw)
+    compare_workload(with_head_dim(w, 2, d, 29), ("fwd", "bwd"))
+
+
 def test_per_head_activation_fp32():
     w = make_workload("tiny_fp32", 3, act=("softmax", "gelu"))
     compare_workload(w, ("fwd", "bwd"))
