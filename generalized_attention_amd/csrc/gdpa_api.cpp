@@ -206,16 +206,20 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
       for (int g = 0; g < n_groups; ++g)
         acts |= ps[g].head_acts ? (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX)
                                 : 1 << ps[g].act;
-      // forward mode 1: d <= 64 and every key range resident in LDS; backward with one wave per
-      // item: at most 32 keys, element-wise, no window
-      int key_mode = 1;
+      // forward mode 1: d <= 64 and every key range resident in LDS; 2: d <= 64, a longer key
+      // range and no window (windows keep the 4-wave ring); 0 otherwise. Backward with one wave
+      // per item: at most 32 keys, element-wise, no window
+      bool any_long = false, any_window = false, any_d128 = false;
       bool small = true;
       for (int g = 0; g < n_groups; ++g) {
         const int kv = ps[g].max_seqlen_kv;
-        if (kv > fwd_kv_capacity(ps[g].head_dim) || ps[g].head_dim == 128) key_mode = 0;
+        any_long |= kv > fwd_kv_capacity(ps[g].head_dim);
+        any_window |= ps[g].window_left >= 0 || ps[g].window_right >= 0;
+        any_d128 |= ps[g].head_dim == 128;
         small = small && kv <= 32 && ps[g].act != GDPA_ACT_SOFTMAX && !ps[g].head_acts &&
                 ps[g].window_left < 0 && ps[g].window_right < 0 && !shared_q(ps[g]);
       }
+      const int key_mode = any_d128 ? 0 : !any_long ? 1 : any_window ? 0 : 2;
       e = pass == 0 ? launch_fwd_bf16(d, dims, acts, key_mode, s) : launch_bwd_bf16(d, dims, acts, small, s);
     }
     for (int g = 0; g < n_groups && e == hipSuccess; ++g)

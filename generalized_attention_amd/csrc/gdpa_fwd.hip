@@ -32,13 +32,16 @@ namespace gdpa {
 //                 2 workgroups/CU (2 waves per SIMD);
 //   kFwdResident  d <= 64 and every key range fits in LDS (at most 16384 / d keys): only the
 //                 resident path is built, whose smaller register footprint allows 8 waves per
-//                 workgroup, 2 workgroups/CU (4 waves per SIMD).
-enum FwdMode { kFwdAny = 0, kFwdResident = 1 };
+//                 workgroup, 2 workgroups/CU (4 waves per SIMD);
+//   kFwdLong8     d <= 64, some key range longer than that and no window: 8 waves as above with
+//                 the key-chunk path, whose row groups of 256 rows stage each key range half as
+//                 often as groups of 128.
+enum FwdMode { kFwdAny = 0, kFwdResident = 1, kFwdLong8 = 2 };
 template <int MODE>
-constexpr int fwd_waves() { return MODE == kFwdResident ? 8 : 4; }
+constexpr int fwd_waves() { return MODE == kFwdAny ? 4 : 8; }
 // minimum waves per SIMD (the second launch bound)
 template <int MODE>
-constexpr int fwd_waves_per_simd() { return MODE == kFwdResident ? 4 : 2; }
+constexpr int fwd_waves_per_simd() { return MODE == kFwdAny ? 2 : 4; }
 // Keys staged in LDS at once.
 template <int D, int MODE>
 constexpr int fwd_nkv() { return 16384 / D; }
@@ -484,7 +487,8 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
         FwdAcc<D, QS> acc;
         acc_init(acc);
         if (hi >= lo)
-          fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, true>(lds, gd, qf, acc, row0, 0, N, lo / 32, hi / 32 + 1);
+          fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, true, NW == 4>(lds, gd, qf, acc, row0, 0, N, lo / 32,
+                                                                      hi / 32 + 1);
         fwd_finish<D, NKV, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
       }
     }
@@ -520,8 +524,8 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
         const int chi = hi < kc + span - 1 ? hi : kc + span - 1;
         if (active && chi >= clo) {
           if (!kHoldQ) load_q<D, QL>(qf, qseq, rs, row0, L);
-          fwd_accumulate<D, NKV, ACT, QL, GATED, MASKED>(lds, gd, qf, acc, row0, kc, kc + span, (clo - kc) / 32,
-                                                    (chi - kc) / 32 + 1);
+          fwd_accumulate<D, NKV, ACT, QL, GATED, MASKED, false, NW == 4>(lds, gd, qf, acc, row0, kc, kc + span,
+                                                                     (clo - kc) / 32, (chi - kc) / 32 + 1);
         }
       }
       if (active) fwd_finish<D, NKV, ACT, QL, GATED>(gd, acc, oseq, lseq, L, row0);
@@ -565,7 +569,7 @@ __global__ void __launch_bounds__(fwd_waves<MODE>() * kWave, fwd_waves_per_simd<
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
   if (gd.head_acts != nullptr) gd.act = gd.head_acts[h];  // activation of this item's head
   constexpr int NW = fwd_waves<MODE>();
-  constexpr bool LONG = MODE == kFwdAny;
+  constexpr bool LONG = MODE != kFwdResident;
   if constexpr ((DSET & kDim32) != 0)
     if (gd.head_dim == 32) { fwd_dispatch_act<32, fwd_nkv<32, MODE>(), NW, ASET, LONG>(lds, gd, b, h); return; }
   if constexpr ((DSET & kDim64) != 0)
@@ -588,7 +592,7 @@ hipError_t launch_fwd_bf16_t(const LaunchDesc& d, int dim_set, int act_set, hipS
     case 1 << GDPA_ACT_SOFTMAX: GDPA_LAUNCH(DS, 1 << GDPA_ACT_SOFTMAX); break; \
     default: GDPA_LAUNCH(DS, kAll); break;                            \
   }
-  if constexpr (MODE == kFwdResident) {  // d <= 64 only (d = 128 does not fit 128 registers)
+  if constexpr (MODE != kFwdAny) {  // d <= 64 only (d = 128 does not fit 128 registers)
     switch (dim_set) {
       case kDim32: GDPA_LAUNCH_ACTS(kDim32); break;
       case kDim64: GDPA_LAUNCH_ACTS(kDim64); break;
@@ -609,8 +613,9 @@ hipError_t launch_fwd_bf16_t(const LaunchDesc& d, int dim_set, int act_set, hipS
 
 hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, int key_mode, hipStream_t stream) {
   if (d.n_items == 0) return hipSuccess;
-  return key_mode == kFwdResident ? launch_fwd_bf16_t<kFwdResident>(d, dim_set, act_set, stream)
-                                   : launch_fwd_bf16_t<kFwdAny>(d, dim_set, act_set, stream);
+  if (key_mode == kFwdResident) return launch_fwd_bf16_t<kFwdResident>(d, dim_set, act_set, stream);
+  if (key_mode == kFwdLong8) return launch_fwd_bf16_t<kFwdLong8>(d, dim_set, act_set, stream);
+  return launch_fwd_bf16_t<kFwdAny>(d, dim_set, act_set, stream);
 }
 
 }  // namespace gdpa

@@ -12,7 +12,8 @@ enum DimSet { kDim32 = 1, kDim64 = 2, kDim128 = 4 };
 
 hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream);
 // act_set: bit (1 << act) for every activation present in the launch.
-// key_mode: 1 = d <= 64 and every key range fits the forward's LDS (16384 / d keys); 0 = any.
+// key_mode: 1 = d <= 64 and every key range fits the forward's LDS (16384 / d keys); 2 = d <= 64,
+// no window and some key range longer than that; 0 = any.
 hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, int key_mode, hipStream_t stream);
 // small: every problem has at most 32 keys per sequence, an element-wise activation and no window
 // (one wave per work item).
