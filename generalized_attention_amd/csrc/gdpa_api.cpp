@@ -220,7 +220,8 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
                 ps[g].window_left < 0 && ps[g].window_right < 0 && !shared_q(ps[g]);
       }
       const int key_mode = any_d128 ? 0 : !any_long ? 1 : any_window ? 0 : 2;
-      e = pass == 0 ? launch_fwd_bf16(d, dims, acts, key_mode, s) : launch_bwd_bf16(d, dims, acts, small, s);
+      e = pass == 0 ? launch_fwd_bf16(d, dims, acts, key_mode, s)
+                    : launch_bwd_bf16(d, dims, acts, small, !any_window, s);
     }
     for (int g = 0; g < n_groups && e == hipSuccess; ++g)
       if (pass == 1 && shared_q(ps[g])) e = launch_reduce_shared_dq(d.grp[g], s);

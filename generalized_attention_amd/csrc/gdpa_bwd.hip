@@ -13,7 +13,9 @@ hipError_t launch_bwd_bf16_agpr(const LaunchDesc& d, int dim_set, int act_set, h
 // One instantiation per head-dim set and activation present: a launch with one element-wise
 // activation runs a kernel without the softmax paths (and their registers); several head dims
 // share the kernel that holds all three.
-hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, hipStream_t stream) {
+// wide_softmax: no window in the launch; the softmax-only launches at d <= 64 then run 8 waves.
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, bool wide_softmax,
+                           hipStream_t stream) {
   if (d.n_items == 0) return hipSuccess;
   constexpr int kGelu_ = 1 << GDPA_ACT_GELU, kSilu_ = 1 << GDPA_ACT_SILU;
   if (small) {
@@ -52,9 +54,17 @@ hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool s
   } else if (act_set == kSilu) {
     GDPA_LAUNCH_DIMS(kSilu);
   } else if (act_set == kSoftmax && dim_set == kDim32) {
-    GDPA_LAUNCH(kDim32, kSoftmax);
+    if (wide_softmax) {
+      GDPA_LAUNCH(kDim32, (kSoftmax | kBwdWideSoftmax));
+    } else {
+      GDPA_LAUNCH(kDim32, kSoftmax);
+    }
   } else if (act_set == kSoftmax && dim_set == kDim64) {
-    GDPA_LAUNCH(kDim64, kSoftmax);
+    if (wide_softmax) {
+      GDPA_LAUNCH(kDim64, (kSoftmax | kBwdWideSoftmax));
+    } else {
+      GDPA_LAUNCH(kDim64, kSoftmax);
+    }
   } else {
     return launch_bwd_bf16_agpr(d, dim_set, act_set, stream);
   }

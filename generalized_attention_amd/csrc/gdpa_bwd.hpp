@@ -637,8 +637,9 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       // the products of iteration it+1 are issued before the element-wise work of it (the dO^T / Q^T
       // operands of dV / dK are read only after it, which keeps their registers free meanwhile).
       // Key-chunk passes, whose fp32 dQ rows already hold registers, run without it (measured
-      // faster there: shared seed queries 540 -> 523 us).
-      constexpr bool PIPE = CHUNK == 0;
+      // faster there: shared seed queries 540 -> 523 us), and so does the softmax form with 8
+      // waves (no registers to spare).
+      constexpr bool PIPE = CHUNK == 0 && !(softmax && NW == 8);
       if constexpr (PIPE) {
         load_a(0);
         issue_sdp(0, 0);

@@ -17,7 +17,8 @@ hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream);
 hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, int key_mode, hipStream_t stream);
 // small: every problem has at most 32 keys per sequence, an element-wise activation and no window
 // (one wave per work item).
-hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, hipStream_t stream);
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, bool wide_softmax,
+                           hipStream_t stream);
 // fp32 kernels are flat over (row, head) / (key, head); prefix tables over groups.
 struct Fp32Aux {
   int64_t row_pre[GDPA_MAX_GROUPS + 1];   // prefix of total_q * H
@@ -31,11 +32,15 @@ hipError_t launch_bwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t 
 // Keys of one (sequence, head) whose K and V^T fit in the forward kernel's LDS at once.
 inline constexpr int fwd_kv_capacity(int d) { return 16384 / d; }
 // Backward: a workgroup holds 256 keys (128 at d = 128) for the whole sweep over query tiles of
-// 64 rows: 4 waves owning 64 keys each (32 at d = 128), or, in launches with neither d = 128 nor
-// the softmax form, 8 waves (two per SIMD) owning 32 keys each.
+// 64 rows: 4 waves owning 64 keys each (32 at d = 128), or, in launches without d = 128 and
+// without the softmax form (or with it but no window: kBwdWideSoftmax in the activation set),
+// 8 waves (two per SIMD) owning 32 keys each.
 constexpr int kBwdWaves = 4;
+constexpr int kBwdWideSoftmax = 1 << 3;  // activation-set flag: softmax launch with 8 waves
 template <int DSET, int ASET>
-constexpr int bwd_waves() { return ((DSET & kDim128) || (ASET & (1 << GDPA_ACT_SOFTMAX))) ? 4 : 8; }
+constexpr int bwd_waves() {
+  return ((DSET & kDim128) || ((ASET & (1 << GDPA_ACT_SOFTMAX)) && !(ASET & kBwdWideSoftmax))) ? 4 : 8;
+}
 constexpr int kBwdKeyBlock = 32;
 constexpr int kBwdQueryTile = 64;
 inline constexpr int bwd_keys_per_wave(int d) { return d == 128 ? 32 : 64; }
