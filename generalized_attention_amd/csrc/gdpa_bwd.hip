@@ -110,7 +110,16 @@ __global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd) {
   if (col >= cols) return;
   const f32x4* part = reinterpret_cast<const f32x4*>(gd.dq32);
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int b0 = 0; b0 < gd.num_seqs; b0 += kSeqsPerSlot) acc += part[(int64_t)b0 * cols + col];
+  // the same sequence order as one slot at a time, with four slots' loads in flight together
+  int b0 = 0;
+  for (; b0 + 4 * kSeqsPerSlot <= gd.num_seqs; b0 += 4 * kSeqsPerSlot) {
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = part[(int64_t)(b0 + i * kSeqsPerSlot) * cols + col];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += v[i];
+  }
+  for (; b0 < gd.num_seqs; b0 += kSeqsPerSlot) acc += part[(int64_t)b0 * cols + col];
   out_store4(out_ptr(gd.dq, gd.out_f32, (size_t)col * 4), acc * gd.scale);
 }
 
