@@ -13,7 +13,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pffn_trai
 Besides the contract fields the line carries kernel_ms (mean per-kernel times), timing (p10 / p50
 / p90 of the step, the forward and the backward, and of a cold step that follows a 512 MiB write
 flushing the Infinity Cache), roofline (the dominant kernel against its bound), mfma_reference (a
-measured large bf16 library GEMM rate) and cpu_baseline (the oracle).
+measured large bf16 library GEMM rate), hbm_reference (a measured 1 GiB copy rate) and
+cpu_baseline (the oracle).
 """
 
 from __future__ import annotations
@@ -99,6 +100,31 @@ def measured_gemm_tflops(torch):
         torch.cuda.synchronize()
         best = min(best, e0.elapsed_time(e1))
     return 2.0 * n ** 3 / (best * 1e-3) / 1e12
+
+
+def measured_hbm_gbps(torch):
+    """A reachable HBM rate on this GPU for traffic that both reads and writes: a 1 GiB
+    device-to-device copy, best of 5 (bytes read + written). A reference point, not part of the
+    path: the GDPA kernels also both read and write."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = min(t, e0.elapsed_time(e1))
+        return t
+
+    copy_ms = best(lambda: b.copy_(a))
+    return {"copy_gbps": 2.0 * n / (copy_ms * 1e-3) / 1e9}
 
 
 def cpu_model_name():
@@ -317,6 +343,12 @@ def main():
         out["mfma_reference"] = {"measured_gemm_tflops": gemm, "step_frac_of_measured": tflops / gemm}
     except RuntimeError as exc:  # a reference only: the line is printed without it
         out["mfma_reference"] = {"error": str(exc)[:200]}
+    try:
+        hbm = measured_hbm_gbps(torch)
+        hbm["dominant_kernel_frac_of_copy"] = roof["achieved"] / hbm["copy_gbps"] if roof["unit"] == "GB/s" else None
+        out["hbm_reference"] = hbm
+    except RuntimeError as exc:
+        out["hbm_reference"] = {"error": str(exc)[:200]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, passes, args.cpu_seqs)
     else:
