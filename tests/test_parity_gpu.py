@@ -255,6 +255,49 @@ def test_sample_independence():
     assert not torch.equal(o1[r1], o2[r1])
 
 
+def _run_planned(groups, plan_groups, douts):
+    """Forward and backward of `groups` with GDPA_FLAG_PLANNED, on a work list that gdpa_plan built
+    from `plan_groups` (same group count, sequence and head counts)."""
+    import dataclasses
+    ws = ga.workspace(groups, 1)
+    ga.gdpa_plan(plan_groups, ws)
+    planned = [dataclasses.replace(g, planned=True) for g in groups]
+    if len(planned) == 1:
+        o, lse = ga.gdpa_fwd(planned[0], ws=ws)
+        return [(o, lse)], [ga.gdpa_bwd(planned[0], douts[0], o=o, lse=lse, ws=ws)]
+    fo = ga.gdpa_fwd_grouped(planned, ws=ws)
+    return fo, ga.gdpa_bwd_grouped(planned, douts, fwd_outs=fo, ws=ws)
+
+
+@pytest.mark.parametrize("name,kw", [("pffn_train", dict(num_seqs=9, len_range=(1, 400))),
+                                     ("causal_gated", dict(num_seqs=5, len_range=(1, 700))),
+                                     ("grouped10", dict(num_seqs=3, len_range=(1, 200)))])
+def test_planned_calls(name, kw):
+    """A work list built once by gdpa_plan serves both passes (bit-identical to unplanned calls),
+    also when it was built from other offsets of the same shape (it is a permutation of the
+    same items; only its order is stale)."""
+    w = make_workload(name, 41, **kw)
+    other = make_workload(name, 42, **kw)  # other lengths, same sequence and head counts
+    dev = [device_group(g) for g in w.groups]
+    dev_other = [device_group(g) for g in other.groups]
+    douts = [g.dout.to("cuda:0") for g in w.groups]
+    if len(dev) == 1:
+        o, lse = ga.gdpa_fwd(dev[0])
+        ref_f, ref_b = [(o, lse)], [ga.gdpa_bwd(dev[0], douts[0], o=o, lse=lse)]
+    else:
+        ref_f = ga.gdpa_fwd_grouped(dev)
+        ref_b = ga.gdpa_bwd_grouped(dev, douts, fwd_outs=ref_f)
+    for plan_from in (dev, dev_other):
+        f, b = _run_planned(dev, plan_from, douts)
+        torch.cuda.synchronize()
+        for (o1, l1), (o2, l2) in zip(ref_f, f):
+            assert torch.equal(o1, o2)
+            assert (l1 is None and l2 is None) or torch.equal(l1, l2)
+        for r1, r2 in zip(ref_b, b):
+            for k in r1:
+                assert torch.equal(r1[k], r2[k]), k
+
+
 def test_permutation_equivariance():
     """The sequences in reverse order give bit-identical per-sequence outputs and gradients (each
     work item's arithmetic is independent of where the schedule puts it)."""
