@@ -298,6 +298,37 @@ def test_planned_calls(name, kw):
                 assert torch.equal(r1[k], r2[k]), k
 
 
+def test_streams():
+    """Calls run on the caller's current stream: two problems enqueued on two side streams at
+    once (own workspaces and outputs) give the results of the same calls on the default stream."""
+    w1 = make_workload("pffn_train", 51, num_seqs=6, len_range=(1, 400))
+    w2 = make_workload("causal_gated", 52, num_seqs=4, len_range=(1, 500))
+    jobs = []
+    for w in (w1, w2):
+        g = w.groups[0]
+        jobs.append((device_group(g), g.dout.to("cuda:0")))
+
+    def run(dev, dout):
+        o, lse = ga.gdpa_fwd(dev)
+        r = ga.gdpa_bwd(dev, dout, o=o, lse=lse)
+        return o, r
+
+    ref = [run(d, do) for d, do in jobs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    out = []
+    for (d, do), st in zip(jobs, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            out.append(run(d, do))
+    for st in streams:
+        st.synchronize()
+    for (o1, r1), (o2, r2) in zip(ref, out):
+        assert torch.equal(o1, o2)
+        for k in r1:
+            assert torch.equal(r1[k], r2[k]), k
+
+
 def test_permutation_equivariance():
     """The sequences in reverse order give bit-identical per-sequence outputs and gradients (each
     work item's arithmetic is independent of where the schedule puts it)."""
