@@ -62,6 +62,8 @@ struct LaunchDesc {
   int32_t* items;      // [n_items] packed (group, head, seq) in longest-first order
   int32_t* scratch;    // builder scratch: [n_seqs_total] bucket keys + [2*kNumBuckets] counters
 };
+// passed by value as the kernels' argument (the argument block holds at most 4 KB)
+static_assert(sizeof(LaunchDesc) <= 4096, "kernel argument size");
 
 // Copy of group g's descriptor (g is uniform across the workgroup). A chain of uniform selects
 // instead of a dynamic index into the kernel-argument table keeps the table out of scratch.
