@@ -282,6 +282,6 @@ const char* gdpa_strerror(int status) {
   }
 }
 
-int gdpa_version(void) { return 100; }
+int gdpa_version(void) { return 200; }  // 0.2.0: float32 outputs (GDPA_FLAG_FP32_OUT)
 
 }  // extern "C"
