@@ -223,3 +223,22 @@ def test_product_path_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_binding_fp32_outputs_marshalling():
+    """The binding sets GDPA_FLAG_FP32_OUT and allocates float32 outputs for it (host tensors:
+    marshalling only, nothing is launched)."""
+    import torch
+    import generalized_attention_amd as ga
+
+    q = torch.zeros(10, 2, 32, dtype=torch.bfloat16)
+    k = torch.zeros(6, 2, 32, dtype=torch.bfloat16)
+    for fp32_out in (False, True):
+        grp = ga.make_group(q, k, k, [0, 4, 10], [0, 3, 6], act="silu", scale=0.5, fp32_out=fp32_out)
+        flags = grp.problem().flags
+        assert bool(flags & _lib.GDPA_FLAG_FP32_OUT) == fp32_out
+        o, lse = ga.ops._alloc_fwd(grp)
+        dq, dk, dv, dg = ga.ops._alloc_bwd(grp, want_dg=False)
+        want = torch.float32 if fp32_out else torch.bfloat16
+        assert o.dtype == dq.dtype == dk.dtype == dv.dtype == want and lse is None and dg is None
+        assert o.shape == q.shape and dk.shape == k.shape
