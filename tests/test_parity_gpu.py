@@ -127,6 +127,31 @@ def test_tiny_fp32_backward():
     compare_workload(make_workload("tiny_fp32", 0), ("fwd", "bwd"))
 
 
+def as_fp32(w, shrink=0.25):
+    """The workload's sequences and options in float32 (inputs cast exactly, then scaled by
+    `shrink` so that outputs stay O(1) and the absolute fp32 rule measures the kernel)."""
+    import dataclasses
+    for g in w.groups:
+        g.spec = dataclasses.replace(g.spec, dtype="fp32")
+        g.q, g.k, g.v, g.dout = (t.to(torch.float32) * shrink for t in (g.q, g.k, g.v, g.dout))
+    return w
+
+
+FP32_CASES = [
+    ("causal_gated", dict(lengths=[0, 1, 5, 33, 64, 97], act="softmax")),
+    ("causal_gated", dict(lengths=[1, 17, 64, 90], act="gelu", window=(8, 8))),
+    ("causal_gated", dict(lengths=[3, 40, 100], act="silu", window=(-1, -1))),
+    ("pffn_train", dict(num_seqs=4, len_range=(1, 60), keys=300, act="silu", scale=0.125)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FP32_CASES, ids=[f"{n}-{kw.get('act')}-{kw.get('window', '')}" for n, kw in FP32_CASES])
+def test_fp32_forms(name, kw):
+    """The float32 kernels beyond the tiny workload: gated softmax with its gate gradient, windows,
+    full self-attention, and a key range longer than any staging unit."""
+    compare_workload(as_fp32(make_workload(name, 61, **kw)), ("fwd", "bwd"))
+
+
 @pytest.mark.parametrize("seed,scale", [(0, None), (1, None), (2, 1.0 / 8)])
 def test_pffn_train_reduced(seed, scale):
     w = make_workload("pffn_train", seed, num_seqs=10, len_range=(1, 700))
