@@ -354,6 +354,48 @@ def test_streams():
             assert torch.equal(r1[k], r2[k]), k
 
 
+def test_graph_capture():
+    """The library allocates, frees and synchronizes nothing, so a whole training step (plan,
+    forward, backward) can be captured in a graph: every replay, with eager work between them,
+    reproduces the eager results bit for bit."""
+    import dataclasses
+    w = make_workload("pffn_train", 71, num_seqs=8, len_range=(1, 400))
+    g = w.groups[0]
+    dev = device_group(g)
+    dout = g.dout.to("cuda:0")
+    ws = ga.workspace([dev], 1)
+    planned = dataclasses.replace(dev, planned=True)
+    o, lse = ga.ops._alloc_fwd(dev)
+    outs = ga.ops._alloc_bwd(dev, want_dg=False)
+
+    def step():
+        ga.gdpa_plan([dev], ws)
+        ga.gdpa_fwd(planned, o=o, lse=lse, ws=ws)
+        ga.gdpa_bwd(planned, dout, o=o, lse=lse, out=outs, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    results = (o,) + tuple(outs[:3])
+    ref = [t.clone() for t in results]
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for t in results:
+            t.fill_(float("nan"))  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(results, ref):
+            assert torch.equal(t, r)
+
+
 def test_permutation_equivariance():
     """The sequences in reverse order give bit-identical per-sequence outputs and gradients (each
     work item's arithmetic is independent of where the schedule puts it)."""
