@@ -170,7 +170,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)  # ~50 ms: the timed steps start at steady clocks
     ap.add_argument("--workload", default="pffn_train", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=256)
