@@ -111,7 +111,10 @@ typedef struct gdpa_problem {
   const int32_t* head_acts;
 } gdpa_problem;
 
-/* Device tensors of one problem. Unused entries may be NULL. */
+/* Device tensors of one problem. Unused entries may be NULL, and so may every tensor with no rows
+   (total_q == 0: o, lse, dout, and q, dq unless the queries are shared, whose rows number
+   max_seqlen_q; total_kv == 0: k, v, g, dk, dv, dg). A problem with
+   num_seqs == 0 (then total_q == total_kv == 0) returns GDPA_OK and enqueues nothing. */
 typedef struct gdpa_tensors {
   const void* q;     /* [total_q, H, d] */
   const void* k;     /* [total_kv, H, d] */

@@ -206,6 +206,23 @@ def test_any_key_length_accepted(lib):
     assert _lib.gdpa_workspace_size([cross], 1) > 0
 
 
+def test_empty_problem_accepted(lib):
+    """No sequences (and then no rows and no keys): every tensor pointer may be null, and the
+    calls return GDPA_OK with nothing enqueued, so no HIP call is made here."""
+    for act in (_lib.GDPA_ACT_SILU, _lib.GDPA_ACT_SOFTMAX):
+        p = good_problem(num_seqs=0, total_q=0, total_kv=0, max_seqlen_q=0, max_seqlen_kv=0, act=act,
+                         q_offsets=0, kv_offsets=0)
+        none = good_tensors(q=0, k=0, v=0, o=0, dout=0, dq=0, dk=0, dv=0)
+        for pass_ in (0, 1):
+            assert _lib.gdpa_workspace_size([p], pass_) > 0
+        assert _lib.gdpa_plan([p], FAKE * 16, 1 << 20, 0) == _lib.GDPA_OK
+        assert _lib.gdpa_fwd(p, none, FAKE * 16, 1 << 20, 0) == _lib.GDPA_OK
+        assert _lib.gdpa_bwd(p, none, FAKE * 16, 1 << 20, 0) == _lib.GDPA_OK
+        assert _lib.gdpa_fwd_grouped([p, p], [none, none], FAKE * 16, 1 << 20, 0) == _lib.GDPA_OK
+    # rows without sequences are inconsistent
+    assert _lib.gdpa_workspace_size([good_problem(num_seqs=0)], 0) == 0
+
+
 def test_grouped_requires_same_dtype(lib):
     a = good_problem()
     b = good_problem(dtype=_lib.GDPA_DTYPE_FP32)

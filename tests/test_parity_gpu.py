@@ -491,6 +491,30 @@ def test_short_keys_gated_self_attention():
     compare_workload(w, ("fwd", "bwd"))
 
 
+@pytest.mark.parametrize("name,lengths", [("pffn_train", [0, 0, 0]), ("causal_gated", [0, 0]),
+                                          ("pffn_train", [])])
+def test_empty_batches(name, lengths):
+    """Every sequence empty, or no sequences: the calls succeed and return outputs without rows;
+    the PFFN form still has keys, and with no query rows their dK and dV are exactly zero (the
+    sums over queries are empty). The gradients start as NaN, so every key row must be written."""
+    w = make_workload(name, 5, lengths=lengths)
+    g = w.groups[0]
+    print(f"[gpu] empty batch {name} lengths={lengths}", flush=True)
+    dev = device_group(g)
+    want_dg = g.g is not None
+    o, lse = ga.gdpa_fwd(dev)
+    out = ga.ops._alloc_bwd(dev, want_dg=want_dg)
+    for t in out:
+        if t is not None:
+            t.fill_(float("nan"))
+    grads = ga.gdpa_bwd(dev, g.dout.to("cuda:0"), o=o, lse=lse, out=out, want_dg=want_dg)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and grads["dq"].shape[0] == 0
+    assert grads["dk"].shape[0] == g.total_kv and grads["dv"].shape[0] == g.total_kv
+    for key in ("dk", "dv") + (("dg",) if want_dg else ()):
+        assert bool(torch.all(grads[key] == 0)), key
+
+
 @pytest.mark.parametrize("num_seqs,keys", [(1500, 16), (1100, 64)])
 def test_more_sequences_than_scheduler_threads(num_seqs, keys):
     """More sequences than the work-list builder has threads (1024): its loops over sequences
