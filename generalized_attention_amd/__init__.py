@@ -9,6 +9,7 @@ device memory and the current stream; it computes nothing of the operator).
 from . import _lib  # noqa: F401
 from .ops import (  # noqa: F401
     GroupArgs,
+    device_error,
     gdpa_bwd,
     gdpa_bwd_grouped,
     gdpa_fwd,

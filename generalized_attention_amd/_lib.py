@@ -29,9 +29,16 @@ GDPA_MAX_GROUPS = 16
 GDPA_FLAG_PLANNED = 1
 GDPA_FLAG_SHARED_Q = 2
 GDPA_FLAG_FP32_OUT = 4
+GDPA_FLAG_VALIDATE = 8
+GDPA_FLAG_SPLIT_OPERANDS = 16
+
+GDPA_WS_ERROR_OFFSET = 0
+GDPA_DEVICE_ERR_OFFSETS = 1
+GDPA_DEVICE_ERR_LENGTH = 2
+GDPA_DEVICE_ERR_SELF = 4
 
 EXPORTED = ("gdpa_workspace_size", "gdpa_plan", "gdpa_fwd", "gdpa_bwd", "gdpa_fwd_grouped",
-            "gdpa_bwd_grouped", "gdpa_strerror", "gdpa_version")
+            "gdpa_bwd_grouped", "gdpa_validate_offsets", "gdpa_strerror", "gdpa_version")
 
 
 class gdpa_problem(ctypes.Structure):
@@ -103,6 +110,8 @@ def load(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     lib.gdpa_plan.argtypes = [P(gdpa_problem), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.gdpa_plan.restype = ctypes.c_int
+    lib.gdpa_validate_offsets.argtypes = [P(gdpa_problem), ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdpa_validate_offsets.restype = ctypes.c_int
     lib.gdpa_strerror.argtypes = [ctypes.c_int]
     lib.gdpa_strerror.restype = ctypes.c_char_p
     lib.gdpa_version.argtypes = []
@@ -131,6 +140,13 @@ def gdpa_plan(problems, ws, ws_bytes, stream) -> int:
     n = len(problems)
     pa = (gdpa_problem * n)(*problems)
     return load().gdpa_plan(pa, n, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
+
+
+def gdpa_validate_offsets(problem, q_offsets_host, kv_offsets_host) -> int:
+    """The offsets rules on host int32 arrays (numpy, contiguous): GDPA_DEVICE_ERR_* bits or a
+    negative status."""
+    return load().gdpa_validate_offsets(ctypes.byref(problem), q_offsets_host.ctypes.data_as(ctypes.c_void_p),
+                                        kv_offsets_host.ctypes.data_as(ctypes.c_void_p))
 
 
 def gdpa_fwd(problem, tensors, ws, ws_bytes, stream) -> int:

@@ -17,11 +17,15 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgdpa.so")
 
-SOURCES = ["gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_bwd_agpr.hip", "gdpa_fp32.hip"]
-# Per-source options. The backward kernels keep MFMA results in the VGPR form (no register-class
-# copies between the score accumulators and the element-wise code); one kernel variant that this
-# compiler cannot build that way lives in its own source.
-EXTRA = {"gdpa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# (the kernel families sit in separate units so that they compile in parallel; largest first)
+SOURCES = ["gdpa_bwd_pw.hip", "gdpa_fwd_any.hip", "gdpa_bwd_mix_all.hip", "gdpa_bwd_mix_d128.hip",
+           "gdpa_bwd_mix_d64.hip", "gdpa_bwd_mix_d32.hip", "gdpa_bwd_agpr.hip", "gdpa_bwd_sm.hip", "gdpa_fwd.hip",
+           "gdpa_bwd.hip", "gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fp32.hip"]
+# Per-source options. Most backward kernels keep MFMA results in the VGPR form (no register-class
+# copies between the score accumulators and the element-wise code); the kernel families that this
+# compiler cannot build that way live in sources of their own.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"gdpa_bwd.hip": _VGPR_FORM, "gdpa_bwd_pw.hip": _VGPR_FORM, "gdpa_bwd_sm.hip": _VGPR_FORM}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -47,7 +51,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1, 16)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -5,9 +5,11 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "gdpa.h"
+#include "gdpa_check.hpp"
 #include "gdpa_launch.hpp"
 
 namespace gdpa {
@@ -16,11 +18,15 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Workspace: a 256-byte header (the device error word at GDPA_WS_ERROR_OFFSET), the work list,
+// the builder's per-sequence keys, the softmax row terms and the fp32 dQ rows.
 struct WsLayout {
   size_t items = 0, keys = 0, delta = 0, dq32 = 0, total = 0;
   int64_t n_items = 0, n_seqs = 0, delta_rows = 0, dq32_floats = 0;
   int64_t delta_base[GDPA_MAX_GROUPS] = {};
   int64_t dq32_base[GDPA_MAX_GROUPS] = {};
+  bool has_delta[GDPA_MAX_GROUPS] = {};  // the group reserved row terms / fp32 dQ rows
+  bool has_dq32[GDPA_MAX_GROUPS] = {};
 };
 
 bool shared_q(const gdpa_problem& p) { return (p.flags & GDPA_FLAG_SHARED_Q) != 0; }
@@ -35,7 +41,9 @@ int check_problem(const gdpa_problem& p) {
   if (p.act < GDPA_ACT_GELU || p.act > GDPA_ACT_SOFTMAX) return GDPA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p.scale)) return GDPA_ERR_INVALID_ARGUMENT;
   if (p.window_left < -1 || p.window_right < -1) return GDPA_ERR_INVALID_ARGUMENT;
-  if ((p.flags & ~(GDPA_FLAG_PLANNED | GDPA_FLAG_SHARED_Q | GDPA_FLAG_FP32_OUT)) != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((p.flags & ~(GDPA_FLAG_PLANNED | GDPA_FLAG_SHARED_Q | GDPA_FLAG_FP32_OUT | GDPA_FLAG_VALIDATE |
+                   GDPA_FLAG_SPLIT_OPERANDS)) != 0)
+    return GDPA_ERR_INVALID_ARGUMENT;
   if (shared_q(p) && p.self_attention) return GDPA_ERR_INVALID_ARGUMENT;
   if (shared_q(p) && p.dtype != GDPA_DTYPE_BF16) return GDPA_ERR_UNSUPPORTED;
   if (p.self_attention != 0 && p.self_attention != 1) return GDPA_ERR_INVALID_ARGUMENT;
@@ -58,7 +66,8 @@ int check_problem(const gdpa_problem& p) {
 // softmax, the row term D_i live in the workspace.
 bool bwd_chunked(const gdpa_problem& p) {
   return p.dtype == GDPA_DTYPE_BF16 &&
-         (shared_q(p) || bwd_may_chunk(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv));
+         (shared_q(p) || bwd_may_chunk(p.head_dim, p.window_left, p.window_right, p.max_seqlen_kv,
+                                       (p.flags & GDPA_FLAG_SPLIT_OPERANDS) != 0));
 }
 
 // The problem may contain softmax heads (its own act, or any head when the activation is per head).
@@ -96,21 +105,23 @@ int layout(const gdpa_problem* ps, int n_groups, int pass, WsLayout* L) {
     L->n_seqs += ps[g].num_seqs;
     L->delta_base[g] = L->delta_rows;
     // softmax backward: per-row D_i (fp32: between its two kernels; bf16: across key chunks)
-    if (pass == 1 && may_softmax(ps[g]) && (ps[g].dtype == GDPA_DTYPE_FP32 || bwd_chunked(ps[g])))
+    if (pass == 1 && may_softmax(ps[g]) && (ps[g].dtype == GDPA_DTYPE_FP32 || bwd_chunked(ps[g]))) {
       L->delta_rows += ps[g].total_q * ps[g].num_heads;
+      L->has_delta[g] = true;
+    }
     L->dq32_base[g] = L->dq32_floats;
     if (pass == 1 && bwd_chunked(ps[g])) {
       const int64_t rows = shared_q(ps[g]) ? (int64_t)ps[g].num_seqs * ps[g].max_seqlen_q : ps[g].total_q;
       L->dq32_floats += rows * ps[g].num_heads * ps[g].head_dim;
+      L->has_dq32[g] = true;
     }
   }
   if (L->n_items >= ((int64_t)1 << 31) || L->n_seqs >= ((int64_t)1 << 31)) return GDPA_ERR_UNSUPPORTED;
-  L->items = 0;
-  L->keys = align_up((size_t)L->n_items * 4);
+  L->items = kAlign;  // after the header
+  L->keys = L->items + align_up((size_t)L->n_items * 4);
   L->delta = L->keys + align_up((size_t)L->n_seqs * 4);
   L->dq32 = L->delta + align_up((size_t)L->delta_rows * 4);
   L->total = L->dq32 + align_up((size_t)L->dq32_floats * 4);
-  if (L->total == 0) L->total = kAlign;
   return GDPA_OK;
 }
 
@@ -129,6 +140,8 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
   char* base = static_cast<char*>(ws);
   d->items = reinterpret_cast<int32_t*>(base + L.items);
   d->scratch = reinterpret_cast<int32_t*>(base + L.keys);
+  d->err = reinterpret_cast<int32_t*>(base + GDPA_WS_ERROR_OFFSET);
+  d->check_err = 0;
   uint64_t max_work = 1;
   int seq_base = 0;
   for (int g = 0; g < n_groups; ++g) {
@@ -137,10 +150,12 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
     GroupDesc& gd = d->grp[g];
     gd.q = t.q; gd.k = t.k; gd.v = t.v; gd.g = t.g; gd.o = t.o; gd.lse = t.lse;
     gd.dout = t.dout; gd.dq = t.dq; gd.dk = t.dk; gd.dv = t.dv; gd.dg = t.dg;
-    gd.delta = reinterpret_cast<float*>(base + L.delta) + L.delta_base[g];
-    gd.dq32 = reinterpret_cast<float*>(base + L.dq32) + L.dq32_base[g];
+    // (null where the group reserved none: the kernels refuse an item that would need them)
+    gd.delta = L.has_delta[g] ? reinterpret_cast<float*>(base + L.delta) + L.delta_base[g] : nullptr;
+    gd.dq32 = L.has_dq32[g] ? reinterpret_cast<float*>(base + L.dq32) + L.dq32_base[g] : nullptr;
     gd.shared_q = shared_q(p) ? p.max_seqlen_q : 0;
     gd.out_f32 = p.dtype == GDPA_DTYPE_BF16 && (p.flags & GDPA_FLAG_FP32_OUT) ? 1 : 0;
+    gd.split_all = (p.flags & GDPA_FLAG_SPLIT_OPERANDS) ? 1 : 0;
     gd.q_off = p.q_offsets;
     gd.kv_off = p.kv_offsets;
     gd.num_seqs = p.num_seqs;
@@ -151,6 +166,11 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
     gd.scale = p.scale;
     gd.wl = p.window_left;
     gd.wr = p.window_right;
+    gd.total_q = (int32_t)p.total_q;
+    gd.total_kv = (int32_t)p.total_kv;
+    gd.max_q = p.max_seqlen_q;
+    gd.max_kv = p.max_seqlen_kv;
+    gd.self_attn = p.self_attention;
     gd.seq_base = seq_base;
     seq_base += p.num_seqs;
     uint64_t n = (uint64_t)p.max_seqlen_kv;
@@ -171,6 +191,14 @@ int dim_set_of(const gdpa_problem* ps, int n_groups) {
   return s;
 }
 
+// GDPA_DEBUG=1 in the environment, or GDPA_FLAG_VALIDATE in any problem: validate the offsets first.
+bool validate_requested(const gdpa_problem* ps, int n_groups) {
+  for (int g = 0; g < n_groups; ++g)
+    if (ps[g].flags & GDPA_FLAG_VALIDATE) return true;
+  const char* env = std::getenv("GDPA_DEBUG");
+  return env != nullptr && env[0] == '1' && env[1] == '\0';
+}
+
 int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, size_t ws_bytes, void* stream,
         int pass) {
   WsLayout L;
@@ -186,6 +214,8 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
 
   LaunchDesc d;
   fill_desc(ps, ts, n_groups, ws, L, &d);
+  const bool validate = validate_requested(ps, n_groups);
+  d.check_err = validate ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (ps[0].dtype == GDPA_DTYPE_FP32) {
@@ -197,9 +227,12 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
       aux.row_base[g] = L.delta_base[g];
     }
     aux.ws_delta = reinterpret_cast<float*>(static_cast<char*>(ws) + L.delta);
-    e = pass == 0 ? launch_fwd_fp32(d, aux, s) : launch_bwd_fp32(d, aux, s);
+    // (no work list: the error word is cleared, or set by the validation, by a kernel of its own)
+    e = validate ? launch_validate(d, s) : launch_clear_error(d.err, s);
+    if (e == hipSuccess) e = pass == 0 ? launch_fwd_fp32(d, aux, s) : launch_bwd_fp32(d, aux, s);
   } else {
-    e = (ps[0].flags & GDPA_FLAG_PLANNED) ? hipSuccess : launch_schedule(d, s);
+    e = (ps[0].flags & GDPA_FLAG_PLANNED) ? hipSuccess : launch_schedule(d, s);  // clears the error word
+    if (e == hipSuccess && validate) e = launch_validate(d, s);
     if (e == hipSuccess) {
       const int dims = dim_set_of(ps, n_groups);
       int acts = 0;
@@ -224,7 +257,7 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
                     : launch_bwd_bf16(d, dims, acts, small, !any_window, s);
     }
     for (int g = 0; g < n_groups && e == hipSuccess; ++g)
-      if (pass == 1 && shared_q(ps[g])) e = launch_reduce_shared_dq(d.grp[g], s);
+      if (pass == 1 && shared_q(ps[g])) e = launch_reduce_shared_dq(d, d.grp[g], s);
   }
   return e == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
 }
@@ -263,12 +296,37 @@ int gdpa_plan(const gdpa_problem* problems, int32_t n_groups, void* ws, size_t w
   int rc = gdpa::layout(problems, n_groups, 0, &L);
   if (rc != GDPA_OK) return rc;
   if (!ws || ((uintptr_t)ws % gdpa::kAlign) != 0 || ws_bytes < L.total) return GDPA_ERR_WORKSPACE;
-  if (L.n_items == 0 || problems[0].dtype != GDPA_DTYPE_BF16) return GDPA_OK;  // fp32 kernels need no list
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // nothing to order: no later call launches a kernel (no items), or fp32 calls, which need no
+  // list and clear the error word themselves
+  if (L.n_items == 0 || problems[0].dtype != GDPA_DTYPE_BF16) return GDPA_OK;
   gdpa::LaunchDesc d;
   gdpa_tensors none[GDPA_MAX_GROUPS];
   std::memset(none, 0, sizeof(none));
   gdpa::fill_desc(problems, none, n_groups, ws, L, &d);
-  return gdpa::launch_schedule(d, static_cast<hipStream_t>(stream)) == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
+  return gdpa::launch_schedule(d, s) == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
+}
+
+int gdpa_validate_offsets(const gdpa_problem* problem, const int32_t* q_offsets_host,
+                          const int32_t* kv_offsets_host) {
+  if (!problem) return GDPA_ERR_INVALID_ARGUMENT;
+  gdpa_problem p = *problem;
+  // the device pointers are not read here: stand in host copies so the problem checks pass
+  p.q_offsets = q_offsets_host;
+  p.kv_offsets = kv_offsets_host;
+  int rc = gdpa::check_problem(p);
+  if (rc != GDPA_OK) return rc;
+  if (p.num_seqs > 0 && (!q_offsets_host || !kv_offsets_host)) return GDPA_ERR_INVALID_ARGUMENT;
+  gdpa::OffsetsRules r;
+  r.num_seqs = p.num_seqs;
+  r.self_attention = p.self_attention;
+  r.total_q = p.total_q;
+  r.total_kv = p.total_kv;
+  r.max_q = p.max_seqlen_q;
+  r.max_kv = p.max_seqlen_kv;
+  int32_t bits = 0;
+  for (int b = 0; b < p.num_seqs; ++b) bits |= gdpa::seq_offsets_error(r, q_offsets_host, kv_offsets_host, b);
+  return bits;
 }
 
 const char* gdpa_strerror(int status) {
@@ -282,6 +340,6 @@ const char* gdpa_strerror(int status) {
   }
 }
 
-int gdpa_version(void) { return 200; }  // 0.2.0: float32 outputs (GDPA_FLAG_FP32_OUT)
+int gdpa_version(void) { return 300; }  // 0.3.0: device error word, offsets validation
 
 }  // extern "C"

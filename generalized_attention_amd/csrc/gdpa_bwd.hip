@@ -1,14 +1,22 @@
-// Launchers of the bf16 backward kernels (the kernels themselves are in gdpa_bwd.hpp).
-//
-// This translation unit is compiled with MFMA results in the VGPR form, which keeps the score
-// accumulators next to the element-wise code (no register-class copies in the inner loop). The
-// launches with the softmax form at d = 128, or with every activation, are built in their own
-// unit without that option (gdpa_bwd_agpr.hip).
+// Launchers of the bf16 backward kernels (the kernels themselves are in gdpa_bwd.hpp): the
+// dispatch over kernel families, the short-key kernel and the shared-query dQ sum. Compiled with
+// MFMA results in the VGPR form (no register-class copies between the accumulators and the
+// element-wise code).
 #include "gdpa_bwd.hpp"
 
 namespace gdpa {
 
-hipError_t launch_bwd_bf16_agpr(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
+// Kernel families, each instantiated in a unit of its own so that the library builds in parallel:
+// element-wise forms (gdpa_bwd_pw.hip) and the softmax form at d <= 64 (gdpa_bwd_sm.hip), both
+// with MFMA results in the VGPR form; the softmax form at d = 128 or over several head dims
+// (gdpa_bwd_agpr.hip) and launches holding every activation (gdpa_bwd_mix_*.hip) without it.
+hipError_t launch_bwd_pointwise(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
+hipError_t launch_bwd_softmax(const LaunchDesc& d, int dim_set, bool wide_softmax, hipStream_t stream);
+hipError_t launch_bwd_softmax_agpr(const LaunchDesc& d, int dim_set, hipStream_t stream);
+hipError_t launch_bwd_mixed_d32(const LaunchDesc& d, hipStream_t stream);
+hipError_t launch_bwd_mixed_d64(const LaunchDesc& d, hipStream_t stream);
+hipError_t launch_bwd_mixed_d128(const LaunchDesc& d, hipStream_t stream);
+hipError_t launch_bwd_mixed_all(const LaunchDesc& d, hipStream_t stream);
 
 // One instantiation per head-dim set and activation present: a launch with one element-wise
 // activation runs a kernel without the softmax paths (and their registers); several head dims
@@ -37,40 +45,17 @@ hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool s
 #undef GDPA_SMALL
     return hipGetLastError();
   }
-  const dim3 grid(d.n_items);
-  constexpr int kDimAll = kDim32 | kDim64 | kDim128;
-  constexpr int kGelu = 1 << GDPA_ACT_GELU, kSilu = 1 << GDPA_ACT_SILU, kSoftmax = 1 << GDPA_ACT_SOFTMAX;
-#define GDPA_LAUNCH(DS, AS) \
-  hipLaunchKernelGGL((bwd_bf16_kernel<DS, AS>), grid, dim3((bwd_waves<DS, AS>() * kWave)), (bwd_lds_bytes<DS, AS>()), stream, d)
-#define GDPA_LAUNCH_DIMS(AS)                            \
-  switch (dim_set) {                                    \
-    case kDim32: GDPA_LAUNCH(kDim32, AS); break;        \
-    case kDim64: GDPA_LAUNCH(kDim64, AS); break;        \
-    case kDim128: GDPA_LAUNCH(kDim128, AS); break;      \
-    default: GDPA_LAUNCH(kDimAll, AS); break;           \
+  constexpr int kSoftmax = 1 << GDPA_ACT_SOFTMAX;
+  if (act_set == kGelu_ || act_set == kSilu_) return launch_bwd_pointwise(d, dim_set, act_set, stream);
+  if (act_set == kSoftmax && (dim_set == kDim32 || dim_set == kDim64))
+    return launch_bwd_softmax(d, dim_set, wide_softmax, stream);
+  if (act_set == kSoftmax) return launch_bwd_softmax_agpr(d, dim_set, stream);
+  switch (dim_set) {
+    case kDim32: return launch_bwd_mixed_d32(d, stream);
+    case kDim64: return launch_bwd_mixed_d64(d, stream);
+    case kDim128: return launch_bwd_mixed_d128(d, stream);
+    default: return launch_bwd_mixed_all(d, stream);
   }
-  if (act_set == kGelu) {
-    GDPA_LAUNCH_DIMS(kGelu);
-  } else if (act_set == kSilu) {
-    GDPA_LAUNCH_DIMS(kSilu);
-  } else if (act_set == kSoftmax && dim_set == kDim32) {
-    if (wide_softmax) {
-      GDPA_LAUNCH(kDim32, (kSoftmax | kBwdWideSoftmax));
-    } else {
-      GDPA_LAUNCH(kDim32, kSoftmax);
-    }
-  } else if (act_set == kSoftmax && dim_set == kDim64) {
-    if (wide_softmax) {
-      GDPA_LAUNCH(kDim64, (kSoftmax | kBwdWideSoftmax));
-    } else {
-      GDPA_LAUNCH(kDim64, kSoftmax);
-    }
-  } else {
-    return launch_bwd_bf16_agpr(d, dim_set, act_set, stream);
-  }
-#undef GDPA_LAUNCH_DIMS
-#undef GDPA_LAUNCH
-  return hipGetLastError();
 }
 
 // ---- shared query matrix: dQ = scale * sum over sequences of their fp32 partial rows ----------
@@ -81,7 +66,8 @@ hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool s
 // second sums those slots in sequence order and writes dq in bf16.
 constexpr int kSeqsPerSlot = 8;
 
-__global__ void __launch_bounds__(256) reduce_shared_dq_stage1(GroupDesc gd) {
+__global__ void __launch_bounds__(256) reduce_shared_dq_stage1(GroupDesc gd, const int32_t* err, int32_t check_err) {
+  if (check_err && *err != 0) return;  // validation refused the launch
   const int S = gd.shared_q, rowf4 = gd.num_heads * gd.head_dim / 4;
   const int64_t cols = (int64_t)S * rowf4;
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -103,7 +89,8 @@ __global__ void __launch_bounds__(256) reduce_shared_dq_stage1(GroupDesc gd) {
   }
 }
 
-__global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd) {
+__global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd, const int32_t* err, int32_t check_err) {
+  if (check_err && *err != 0) return;
   const int S = gd.shared_q, rowf4 = gd.num_heads * gd.head_dim / 4;
   const int64_t cols = (int64_t)S * rowf4;
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -123,16 +110,16 @@ __global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd) {
   out_store4(out_ptr(gd.dq, gd.out_f32, (size_t)col * 4), acc * gd.scale);
 }
 
-hipError_t launch_reduce_shared_dq(const GroupDesc& gd, hipStream_t stream) {
+hipError_t launch_reduce_shared_dq(const LaunchDesc& d, const GroupDesc& gd, hipStream_t stream) {
   const int64_t cols = (int64_t)gd.shared_q * gd.num_heads * gd.head_dim / 4;
   if (cols == 0) return hipSuccess;
   const unsigned nx = (unsigned)((cols + 255) / 256);
   if (gd.num_seqs > 0) {
     const int slots = (gd.num_seqs + kSeqsPerSlot - 1) / kSeqsPerSlot;
     const unsigned ny = (unsigned)(slots < 65535 ? slots : 65535);
-    hipLaunchKernelGGL(reduce_shared_dq_stage1, dim3(nx, ny), dim3(256), 0, stream, gd);
+    hipLaunchKernelGGL(reduce_shared_dq_stage1, dim3(nx, ny), dim3(256), 0, stream, gd, d.err, d.check_err);
   }
-  hipLaunchKernelGGL(reduce_shared_dq_stage2, dim3(nx), dim3(256), 0, stream, gd);
+  hipLaunchKernelGGL(reduce_shared_dq_stage2, dim3(nx), dim3(256), 0, stream, gd, d.err, d.check_err);
   return hipGetLastError();
 }
 

@@ -377,7 +377,12 @@ __device__ inline void row_chunks(int row, int ntot, int wl, int wr, int kchunk,
 // CHUNK: 0 = the item's keys are all resident; 1 = one chunk of CAP keys starting at it.kofs, dQ
 // accumulated over the chunks in fp32 workspace rows (softmax: D_i read from the workspace);
 // 2 = softmax row-term pass over one chunk: only D_i, accumulated into the workspace.
-template <int D, int NW, int ACT, bool GATED, int KACT, bool WINDOWED, int CHUNK = 0>
+// SPLIT: an element-wise item whose keys are all resident, with at most kSplitTerms rows or keys:
+// P and dS enter the dV, dK and dQ products as a high + low bf16 pair like the softmax form's.
+// Masks are applied, so a windowed item whose keys are all resident runs here too. (Key chunks of
+// an element-wise item with that few rows take the pair in dV and dK by a uniform branch: their
+// dQ sums run over more keys than a chunk holds.)
+template <int D, int NW, int ACT, bool GATED, int KACT, bool WINDOWED, int CHUNK = 0, bool SPLIT = false>
 __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const BwdItem& it) {
   using G = BwdGeo<D, NW>;
   constexpr int NS = G::NW * KACT;  // ring slots in use
@@ -389,7 +394,14 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   static_assert(CHUNK == 0 || (!WINDOWED && KACT == G::KB), "key chunks hold every block");
   // entries need explicit masks in the softmax form, inside a window or in a key chunk; without
   // a window every block is resident for the whole sweep (taken once, before it)
-  constexpr bool MASKED = softmax || WINDOWED || CHUNK != 0;
+  constexpr bool MASKED = softmax || WINDOWED || CHUNK != 0 || SPLIT;
+  // P and dS as a high + low bf16 pair in dV / dK, and dS in dQ (the softmax form always;
+  // element-wise items with few rows / few keys)
+  constexpr bool split = softmax || SPLIT;
+  constexpr bool split_dq = split;
+  // element-wise key chunks of an item with few rows (or split operands asked for): the pair in
+  // dV / dK only (uniform)
+  const bool chunk_rows_split = !split && CHUNK == 1 && (it.L <= kSplitTerms || gd.split_all);
   constexpr bool DSUM = CHUNK == 1 && softmax;  // D_i comes from the workspace
   // keys are chunk-local below; masks compare sequence positions kofs + key with the rows
   const int kofs = CHUNK ? it.kofs : 0;
@@ -480,7 +492,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   // previous tile's dQ right after their main pass, in the time the other wave of their SIMD still
   // needs for its own main pass, instead of after the barrier; dS^T alternates between the two
   // exchange areas (the second is free without softmax).
-  constexpr bool FQ = G::NW == 8 && !softmax && !WINDOWED && CHUNK == 0 && G::QH == 1;
+  constexpr bool FQ = G::NW == 8 && !split && !WINDOWED && CHUNK == 0 && G::QH == 1;
   constexpr int NK = 2 * NS;                       // 16-key steps of one dQ tile
   const int drow = dtile * 32 + out_perm(lc);      // K^T row carried by this lane's A-operand row
   auto dq_tile = [&](int sxoff) {
@@ -639,7 +651,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       // Key-chunk passes, whose fp32 dQ rows already hold registers, run without it (measured
       // faster there: shared seed queries 540 -> 523 us), and so does the softmax form with 8
       // waves (no registers to spare).
-      constexpr bool PIPE = CHUNK == 0 && !(softmax && NW == 8);
+      constexpr bool PIPE = CHUNK == 0 && !(split && NW == 8);
       if constexpr (PIPE) {
         load_a(0);
         issue_sdp(0, 0);
@@ -680,9 +692,9 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         const int key = kf + lc;                       // this lane's key (sequence position)
         const int spos = (s * kBwdKeyBlock + lc) * G::SXROW;
         // P and dS as bf16 B operands (k-tile t = registers 8t..8t+7); zero for a block outside
-        // the tile. The softmax form also carries the rounding remainder as a second bf16 term
-        // (x ~ hi + lo): its products mix a few large probabilities, whose bf16 rounding alone
-        // would exceed the tolerance.
+        // the tile. The softmax form (and a few-term element-wise item) also carries the rounding
+        // remainder as a second bf16 term (x ~ hi + lo): its products mix a few large terms, whose
+        // bf16 rounding alone would exceed the tolerance.
         u32x4 pu[2], du[2], plu[2], dlu[2];
         auto elementwise = [&]() {
           // register r is query row rf + c_row(r, g), key `key`
@@ -728,7 +740,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
             for (int e = 0; e < 4; ++e) {
               pu[t][e] = pack_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
               du[t][e] = pack_bf16x2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1]);
-              if constexpr (softmax) {
+              if (split || chunk_rows_split) {
                 plu[t][e] = pack_bf16x2(p[8 * t + 2 * e] - bf16_lo(pu[t][e]), p[8 * t + 2 * e + 1] - bf16_hi(pu[t][e]));
                 dlu[t][e] = pack_bf16x2(ds[8 * t + 2 * e] - bf16_lo(du[t][e]), ds[8 * t + 2 * e + 1] - bf16_hi(du[t][e]));
               }
@@ -748,7 +760,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           const int qo = (qs * 32 + a * 8 + g * 4) * 2;
           const int t = a >> 1, hlf = (a & 1) * 2;
           *reinterpret_cast<u32x2*>(lds + sx_cur + spos + qo) = u32x2{du[t][hlf], du[t][hlf + 1]};
-          if constexpr (softmax)
+          if constexpr (split_dq)
             *reinterpret_cast<u32x2*>(lds + G::OFF_SXL + spos + qo) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
         }
         if (kb == 0) {
@@ -766,7 +778,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           for (int t = 0; t < 2; ++t) {
             st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(pu[t]), st.dv[kb][dt]);
             st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(du[t]), st.dk[kb][dt]);
-            if constexpr (softmax) {
+            if (split || chunk_rows_split) {
               st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(plu[t]), st.dv[kb][dt]);
               st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(dlu[t]), st.dk[kb][dt]);
             }
@@ -827,7 +839,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           const int kbase = k * 16;
           ka[buf] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_KT + drow * G::KTROW + (kbase + g * 8) * 2));
           sb[buf] = sx_operand<G::SXROW>(lds, G::OFF_SX, kbase, qh);
-          if constexpr (softmax) sl[buf] = sx_operand<G::SXROW>(lds, G::OFF_SXL, kbase, qh);
+          if constexpr (split_dq) sl[buf] = sx_operand<G::SXROW>(lds, G::OFF_SXL, kbase, qh);
         };
         f32x16 acc2[2] = {f32x16{}, f32x16{}};
         load_step(0, 0);
@@ -835,7 +847,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         for (int k = 0; k < NK; ++k) {
           if (k + 1 < NK) load_step(k + 1, (k + 1) & 1);
           acc2[k & 1] = mfma32(ka[k & 1], sb[k & 1], acc2[k & 1]);
-          if constexpr (softmax) acc2[k & 1] = mfma32(ka[k & 1], sl[k & 1], acc2[k & 1]);
+          if constexpr (split_dq) acc2[k & 1] = mfma32(ka[k & 1], sl[k & 1], acc2[k & 1]);
         }
         const f32x16 acc = acc2[0] + acc2[1];
         const int row = r0 + qh * 32 + lc;
@@ -940,7 +952,8 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
     return;
   }
   const bool windowed = it.wl >= 0 || it.wr >= 0;
-  if (it.shared_q || (n > G::CAP && !bwd_ring_ok(D, it.wl, it.wr))) {
+  const bool split_all = ACT != GDPA_ACT_SOFTMAX && gd.split_all;
+  if (it.shared_q || bwd_needs_chunks(D, it.wl, it.wr, n, split_all)) {
     // key chunks of CAP keys, one after the other; each sweeps the query tiles whose rows see it.
     // Softmax first accumulates D_i over every chunk (a pass of its own), then the main passes.
     const int nch = (n + G::CAP - 1) / G::CAP;
@@ -976,6 +989,14 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
     }
     return;
   }
+  if constexpr (ACT != GDPA_ACT_SOFTMAX) {
+    // few rows or few keys (or split operands asked for): the hi + lo operand form, every key
+    // resident (longer ones took the chunk path above)
+    if (L <= kSplitTerms || n <= kSplitTerms || split_all) {
+      bwd_sweep<D, NW, ACT, GATED, G::KB, false, 0, true>(lds, gd, it);
+      return;
+    }
+  }
   // One owned block per wave suffices when all keys fit in NW blocks. Zero padding makes the
   // entries past the ends vanish for the element-wise forms (phi(0) = 0; dO and V rows past the
   // ends are zero), so only the softmax form and windows need explicit masks.
@@ -1008,13 +1029,27 @@ __device__ __forceinline__ void bwd_dispatch_act(char* lds, const GroupDesc& gd,
 template <int DSET, int ASET>
 __global__ void __launch_bounds__((bwd_waves<DSET, ASET>() * kWave), 1) bwd_bf16_kernel(LaunchDesc d) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  if ((int)blockIdx.x >= d.n_items) return;
+  if ((int)blockIdx.x >= d.n_items || launch_refused(d)) return;
   int g, h, b;
   unpack_item(d.items[blockIdx.x], g, h, b);
   if (g >= d.n_groups) return;
   GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
   if (gd.head_acts != nullptr) gd.act = gd.head_acts[h];  // activation of this item's head
+  {
+    const int q0 = gd.q_off[b], q1 = gd.q_off[b + 1], k0 = gd.kv_off[b], k1 = gd.kv_off[b + 1];
+    int32_t e = item_error(gd, q0, q1, k0, k1, -1);
+    // key chunks (or a shared query matrix) accumulate in workspace rows the host reserves only
+    // when the max_seqlen_kv hint (or the flag) asks for them
+    const bool chunked = gd.shared_q || bwd_needs_chunks(gd.head_dim, gd.wl, gd.wr, k1 - k0,
+                                                         gd.split_all && gd.act != GDPA_ACT_SOFTMAX);
+    if (e == 0 && chunked && (gd.dq32 == nullptr || (gd.act == GDPA_ACT_SOFTMAX && gd.delta == nullptr)))
+      e = GDPA_DEVICE_ERR_LENGTH;
+    if (e != 0) {
+      if (threadIdx.x == 0) report_error(d, e);
+      return;
+    }
+  }
   constexpr int NW = bwd_waves<DSET, ASET>();
   if constexpr ((DSET & kDim32) != 0)
     if (gd.head_dim == 32) { bwd_dispatch_act<32, NW, ASET>(lds, gd, b, h); return; }
@@ -1043,7 +1078,8 @@ struct SmallGeo {
   static constexpr int OFF_DO = OFF_Q + 32 * NROW;
   static constexpr int OFF_KT = OFF_DO + 32 * NROW;
   static constexpr int OFF_SX = OFF_KT + D * KTROW;
-  static constexpr int BYTES = OFF_SX + 32 * SXROW;  // per wave
+  static constexpr int OFF_SXL = OFF_SX + 32 * SXROW;  // rounding remainder of dS^T (few keys)
+  static constexpr int BYTES = OFF_SXL + 32 * SXROW;   // per wave
   static_assert(4 * BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -1126,6 +1162,9 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
   float c1 = 0.0f, c3 = 0.0f;
   PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
   const float dv_scale = GATED ? 1.0f : gd.scale;
+  // few rows: dK, dV sums of at most kSplitTerms products; few keys: dQ sums likewise. Their P / dS
+  // operands then carry the rounding remainder as a second bf16 term (uniform per item).
+  const bool split_rows = L <= kSplitTerms || gd.split_all, split_keys = n <= kSplitTerms || gd.split_all;
 
   for (int r0 = 0; r0 < L; r0 += 32) {
     // Q and dO rows r0 .. r0+31: lane (row lc, half g) loads the 16-byte pieces it needs as the A
@@ -1164,27 +1203,37 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) dgs += ds[r];
     }
-    u32x4 pu[2], du[2];
+    u32x4 pu[2], du[2], plu[2], dlu[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pu[t][e] = pack_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
         du[t][e] = pack_bf16x2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1]);
+        plu[t][e] = pack_bf16x2(p[8 * t + 2 * e] - bf16_lo(pu[t][e]), p[8 * t + 2 * e + 1] - bf16_hi(pu[t][e]));
+        dlu[t][e] = pack_bf16x2(ds[8 * t + 2 * e] - bf16_lo(du[t][e]), ds[8 * t + 2 * e + 1] - bf16_hi(du[t][e]));
       }
     // dS^T to the private exchange tile: registers 4a..4a+3 are 4 consecutive rows
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int t = a >> 1, hlf = (a & 1) * 2;
       *reinterpret_cast<u32x2*>(wl + G::OFF_SX + lc * G::SXROW + (a * 8 + g * 4) * 2) = u32x2{du[t][hlf], du[t][hlf + 1]};
+      if (split_keys)
+        *reinterpret_cast<u32x2*>(wl + G::OFF_SXL + lc * G::SXROW + (a * 8 + g * 4) * 2) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
     }
     lds_wave_sync();  // the wave's Q / dO / dS^T stores are in LDS
 #pragma unroll
     for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        dv[dt] = mfma32(tr_operand<G::NROW>(wl, G::OFF_DO, 0, t, dt), as_bf16x8(pu[t]), dv[dt]);
-        dk[dt] = mfma32(tr_operand<G::NROW>(wl, G::OFF_Q, 0, t, dt), as_bf16x8(du[t]), dk[dt]);
+        const bf16x8 dot = tr_operand<G::NROW>(wl, G::OFF_DO, 0, t, dt);
+        const bf16x8 qt = tr_operand<G::NROW>(wl, G::OFF_Q, 0, t, dt);
+        dv[dt] = mfma32(dot, as_bf16x8(pu[t]), dv[dt]);
+        dk[dt] = mfma32(qt, as_bf16x8(du[t]), dk[dt]);
+        if (split_rows) {
+          dv[dt] = mfma32(dot, as_bf16x8(plu[t]), dv[dt]);
+          dk[dt] = mfma32(qt, as_bf16x8(dlu[t]), dk[dt]);
+        }
       }
     // dQ^T = K^T dS^T: register r of lane (row lc, g) is d = dt*32 + g*16 + r
 #pragma unroll
@@ -1195,6 +1244,7 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
       for (int k = 0; k < 2; ++k) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(wl + G::OFF_KT + drow * G::KTROW + (k * 16 + g * 8) * 2));
         acc = mfma32(ka, sx_operand<G::SXROW>(wl, G::OFF_SX, k * 16, 0), acc);
+        if (split_keys) acc = mfma32(ka, sx_operand<G::SXROW>(wl, G::OFF_SXL, k * 16, 0), acc);
       }
       if (row < L) out_store16(dqseq + (row * rs + dt * 32 + g * 16), acc, gd.scale);
     }
@@ -1237,12 +1287,20 @@ __global__ void __launch_bounds__(4 * kWave, 1) bwd_small_kernel(LaunchDesc d) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int w = wave_id();
   const int item = (int)blockIdx.x * 4 + w;
-  if (item >= d.n_items) return;
+  if (item >= d.n_items || launch_refused(d)) return;
   int g, h, b;
   unpack_item(d.items[item], g, h, b);
   if (g >= d.n_groups) return;
   GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;
+  {
+    // one block of at most 32 keys per item
+    const int32_t e = item_error(gd, gd.q_off[b], gd.q_off[b + 1], gd.kv_off[b], gd.kv_off[b + 1], kBwdKeyBlock);
+    if (e != 0) {
+      if (lane_id() == 0) report_error(d, e);
+      return;
+    }
+  }
   constexpr int WB = bwd_small_lds_bytes<DSET>() / 4;
   char* wl = lds + w * WB;
   if constexpr ((DSET & kDim32) != 0)

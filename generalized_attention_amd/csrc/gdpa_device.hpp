@@ -51,6 +51,12 @@ struct GroupDesc {
   int32_t seq_base;   // index of this group's first sequence in the global sequence numbering
   int32_t shared_q;   // rows of a query matrix shared by every sequence (0: per-sequence queries)
   int32_t out_f32;    // bf16 problem whose outputs o, dq, dk, dv are float32
+  int32_t total_q;    // rows of o / dout (and of q unless shared)
+  int32_t total_kv;   // rows of k, v
+  int32_t max_q;      // max_seqlen_q hint
+  int32_t max_kv;     // max_seqlen_kv hint
+  int32_t self_attn;  // query and key sequences are the same rows
+  int32_t split_all;  // element-wise backward: P and dS as high + low bf16 pairs in every item
 };
 
 struct LaunchDesc {
@@ -61,9 +67,30 @@ struct LaunchDesc {
   int32_t work_shift;  // bucket = min(kNumBuckets-1, work >> work_shift)
   int32_t* items;      // [n_items] packed (group, head, seq) in longest-first order
   int32_t* scratch;    // builder scratch: [n_seqs_total] bucket keys + [2*kNumBuckets] counters
+  int32_t* err;        // device error word (GDPA_DEVICE_ERR_* bits) in the workspace
+  int32_t check_err;   // validation ran first: kernels return at once if the word is non-zero
 };
 // passed by value as the kernels' argument (the argument block holds at most 4 KB)
 static_assert(sizeof(LaunchDesc) <= 4096, "kernel argument size");
+
+// Debug validation found bad offsets: the main kernels leave every output untouched.
+__device__ inline bool launch_refused(const LaunchDesc& d) {
+  return d.check_err && *d.err != 0;
+}
+
+// The item's own offsets, checked before any tensor access: row ranges inside their tensors,
+// lengths within what the launch provisioned (kv_cap keys, or any if kv_cap < 0; a shared query
+// matrix has shared_q rows), equal lengths under a window. Returns GDPA_DEVICE_ERR_* bits.
+__device__ inline int32_t item_error(const GroupDesc& gd, int q0, int q1, int k0, int k1, int kv_cap) {
+  int32_t e = 0;
+  if (q0 < 0 || q1 < q0 || q1 > gd.total_q || k0 < 0 || k1 < k0 || k1 > gd.total_kv) return GDPA_DEVICE_ERR_OFFSETS;
+  if ((kv_cap >= 0 && k1 - k0 > kv_cap) || (gd.shared_q && q1 - q0 > gd.shared_q)) e |= GDPA_DEVICE_ERR_LENGTH;
+  if ((gd.wl >= 0 || gd.wr >= 0) && q1 - q0 != k1 - k0) e |= GDPA_DEVICE_ERR_SELF;
+  return e;
+}
+
+// Record error bits from one lane of the item (the item then writes nothing).
+__device__ inline void report_error(const LaunchDesc& d, int32_t e) { atomicOr(d.err, e); }
 
 // Copy of group g's descriptor (g is uniform across the workgroup). A chain of uniform selects
 // instead of a dynamic index into the kernel-argument table keeps the table out of scratch.

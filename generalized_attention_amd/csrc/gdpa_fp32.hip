@@ -48,10 +48,21 @@ __device__ inline void key_range(const GroupDesc& gd, int i, int n, int& lo, int
 
 }  // namespace
 
+// The row's (or key's) sequence b found by the search must own it, and b's offsets must pass the
+// item check; otherwise the thread records the error and writes nothing.
+__device__ inline bool fp32_guard(const GroupDesc& gd, int b, int64_t pos, bool is_key, int32_t* err) {
+  const int q0 = gd.q_off[b], q1 = gd.q_off[b + 1], k0 = gd.kv_off[b], k1 = gd.kv_off[b + 1];
+  int32_t e = item_error(gd, q0, q1, k0, k1, -1);
+  if (e == 0 && (is_key ? (pos < k0 || pos >= k1) : (pos < q0 || pos >= q1))) e = GDPA_DEVICE_ERR_OFFSETS;
+  if (e != 0) atomicOr(err, e);
+  return e == 0;
+}
+
 template <int D>
-__device__ void fwd_row(const GroupDesc& gd, int64_t grow, int h) {
+__device__ void fwd_row(const GroupDesc& gd, int64_t grow, int h, int32_t* err) {
   const int H = gd.num_heads;
   const int b = seq_of(gd.q_off, gd.num_seqs, grow);
+  if (!fp32_guard(gd, b, grow, false, err)) return;
   const int q0 = gd.q_off[b], k0 = gd.kv_off[b];
   const int i = (int)(grow - q0), n = gd.kv_off[b + 1] - k0;
   const float* q = reinterpret_cast<const float*>(gd.q) + (grow * H + h) * D;
@@ -92,9 +103,10 @@ __device__ void fwd_row(const GroupDesc& gd, int64_t grow, int h) {
 }
 
 template <int D>
-__device__ void bwd_row(const GroupDesc& gd, int64_t grow, int h, const float* ws_lse, float* ws_delta) {
+__device__ void bwd_row(const GroupDesc& gd, int64_t grow, int h, const float* ws_lse, float* ws_delta, int32_t* err) {
   const int H = gd.num_heads;
   const int b = seq_of(gd.q_off, gd.num_seqs, grow);
+  if (!fp32_guard(gd, b, grow, false, err)) return;
   const int q0 = gd.q_off[b], k0 = gd.kv_off[b];
   const int i = (int)(grow - q0), n = gd.kv_off[b + 1] - k0;
   const float* q = reinterpret_cast<const float*>(gd.q) + (grow * H + h) * D;
@@ -137,9 +149,11 @@ __device__ void bwd_row(const GroupDesc& gd, int64_t grow, int h, const float* w
 }
 
 template <int D>
-__device__ void bwd_key(const GroupDesc& gd, int64_t gkey, int h, const float* ws_lse, const float* ws_delta) {
+__device__ void bwd_key(const GroupDesc& gd, int64_t gkey, int h, const float* ws_lse, const float* ws_delta,
+                        int32_t* err) {
   const int H = gd.num_heads;
   const int b = seq_of(gd.kv_off, gd.num_seqs, gkey);
+  if (!fp32_guard(gd, b, gkey, true, err)) return;
   const int q0 = gd.q_off[b], k0 = gd.kv_off[b];
   const int j = (int)(gkey - k0), L = gd.q_off[b + 1] - q0, n = gd.kv_off[b + 1] - k0;
   const float* kj = reinterpret_cast<const float*>(gd.k) + (gkey * H + h) * D;
@@ -202,40 +216,42 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(LaunchDesc d, Fp32Aux aux
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int g, h;
   int64_t row;
-  if (!flat_to(aux.row_pre, d.n_groups, d, t, g, row, h)) return;
+  if (launch_refused(d) || !flat_to(aux.row_pre, d.n_groups, d, t, g, row, h)) return;
   const GroupDesc& gd = d.grp[g];
-  if (gd.head_dim == 32) fwd_row<32>(gd, row, h);
-  else if (gd.head_dim == 64) fwd_row<64>(gd, row, h);
-  else fwd_row<128>(gd, row, h);
+  if (gd.head_dim == 32) fwd_row<32>(gd, row, h, d.err);
+  else if (gd.head_dim == 64) fwd_row<64>(gd, row, h, d.err);
+  else fwd_row<128>(gd, row, h, d.err);
 }
 
 __global__ void __launch_bounds__(256) bwd_fp32_rows_kernel(LaunchDesc d, Fp32Aux aux) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int g, h;
   int64_t row;
-  if (!flat_to(aux.row_pre, d.n_groups, d, t, g, row, h)) return;
+  if (launch_refused(d) || !flat_to(aux.row_pre, d.n_groups, d, t, g, row, h)) return;
   const GroupDesc& gd = d.grp[g];
   const float* wl = gd.lse;
   float* wd = aux.ws_delta + aux.row_base[g];
-  if (gd.head_dim == 32) bwd_row<32>(gd, row, h, wl, wd);
-  else if (gd.head_dim == 64) bwd_row<64>(gd, row, h, wl, wd);
-  else bwd_row<128>(gd, row, h, wl, wd);
+  if (gd.head_dim == 32) bwd_row<32>(gd, row, h, wl, wd, d.err);
+  else if (gd.head_dim == 64) bwd_row<64>(gd, row, h, wl, wd, d.err);
+  else bwd_row<128>(gd, row, h, wl, wd, d.err);
 }
 
 __global__ void __launch_bounds__(256) bwd_fp32_keys_kernel(LaunchDesc d, Fp32Aux aux) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int g, h;
   int64_t key;
-  if (!flat_to(aux.key_pre, d.n_groups, d, t, g, key, h)) return;
+  if (launch_refused(d) || !flat_to(aux.key_pre, d.n_groups, d, t, g, key, h)) return;
   const GroupDesc& gd = d.grp[g];
   const float* wl = gd.lse;
   const float* wd = aux.ws_delta + aux.row_base[g];
-  if (gd.head_dim == 32) bwd_key<32>(gd, key, h, wl, wd);
-  else if (gd.head_dim == 64) bwd_key<64>(gd, key, h, wl, wd);
-  else bwd_key<128>(gd, key, h, wl, wd);
+  if (gd.head_dim == 32) bwd_key<32>(gd, key, h, wl, wd, d.err);
+  else if (gd.head_dim == 64) bwd_key<64>(gd, key, h, wl, wd, d.err);
+  else bwd_key<128>(gd, key, h, wl, wd, d.err);
 }
 
 static int64_t blocks_for(int64_t n) { return (n + 255) / 256; }
+// both are kernel arguments of the fp32 kernels (the argument block holds at most 4 KB)
+static_assert(sizeof(LaunchDesc) + sizeof(Fp32Aux) <= 4096, "kernel argument size");
 
 hipError_t launch_fwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t stream) {
   const int64_t n = aux.row_pre[d.n_groups];

@@ -11,6 +11,9 @@ namespace gdpa {
 enum DimSet { kDim32 = 1, kDim64 = 2, kDim128 = 4 };
 
 hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream);
+// Offsets validation into the device error word (debug), and a plain clear of the word.
+hipError_t launch_validate(const LaunchDesc& d, hipStream_t stream);
+hipError_t launch_clear_error(int32_t* err, hipStream_t stream);
 // act_set: bit (1 << act) for every activation present in the launch.
 // key_mode: 1 = d <= 64 and every key range fits the forward's LDS (16384 / d keys); 2 = d <= 64,
 // no window and some key range longer than that; 0 = any.
@@ -42,6 +45,11 @@ constexpr int bwd_waves() {
   return ((DSET & kDim128) || ((ASET & (1 << GDPA_ACT_SOFTMAX)) && !(ASET & kBwdWideSoftmax))) ? 4 : 8;
 }
 constexpr int kBwdKeyBlock = 32;
+// A sum of at most this many products (dK / dV of an item with that few query rows, O / dQ of one
+// with that few keys) takes its P / dS operands as two bf16 terms, high part and rounding
+// remainder: with few terms a product can be many times the output's RMS, and a single bf16
+// rounding of its operand (2^-9 relative) would then exceed 2e-2 of that RMS.
+constexpr int kSplitTerms = 16;
 constexpr int kBwdQueryTile = 64;
 inline constexpr int bwd_keys_per_wave(int d) { return d == 128 ? 32 : 64; }
 inline constexpr int bwd_capacity(int d) { return kBwdWaves * bwd_keys_per_wave(d); }
@@ -51,12 +59,17 @@ inline __host__ __device__ bool bwd_ring_ok(int d, int wl, int wr) {
   return wl >= 0 && wr >= 0 && kBwdQueryTile - 1 + wl + wr <= bwd_capacity(d) - kBwdKeyBlock;
 }
 // Otherwise a sequence with more keys than are resident is processed in key chunks, one after the
-// other, with dQ (and the softmax row term) accumulated in fp32 workspace rows.
-inline bool bwd_may_chunk(int d, int wl, int wr, int max_kv) {
-  return max_kv > bwd_capacity(d) && !bwd_ring_ok(d, wl, wr);
+// other, with dQ (and the softmax row term) accumulated in fp32 workspace rows. The ring path has
+// no split-operand form: with split operands everywhere, long windowed items run in key chunks.
+inline __host__ __device__ bool bwd_needs_chunks(int d, int wl, int wr, int n, bool split_all) {
+  return n > bwd_capacity(d) && (!bwd_ring_ok(d, wl, wr) || split_all);
+}
+inline bool bwd_may_chunk(int d, int wl, int wr, int max_kv, bool split_all) {
+  return bwd_needs_chunks(d, wl, wr, max_kv, split_all);
 }
 
-// Shared-query groups: sum the per-sequence fp32 dQ rows into dq (bf16).
-hipError_t launch_reduce_shared_dq(const GroupDesc& gd, hipStream_t stream);
+// Shared-query groups: sum the per-sequence fp32 dQ rows into dq (bf16); nothing when the
+// launch was refused (d.check_err and a non-zero error word).
+hipError_t launch_reduce_shared_dq(const LaunchDesc& d, const GroupDesc& gd, hipStream_t stream);
 
 }  // namespace gdpa

@@ -6,6 +6,7 @@
 // main kernels take items in list order, one workgroup per item, and the hardware dispatcher
 // hands the next item to whichever compute unit frees up first, so a longest-first order gives
 // the classic LPT balance without a persistent kernel or atomics in the main kernels.
+#include "gdpa_check.hpp"
 #include "gdpa_device.hpp"
 #include "gdpa_launch.hpp"
 
@@ -18,6 +19,7 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
   __shared__ int32_t cursor[kNumBuckets];
   __shared__ int32_t wave_total[kNumBuckets / 64];
   const int tid = threadIdx.x;
+  if (tid == 0) *d.err = 0;  // a new call: clear the device error word
   for (int i = tid; i < kNumBuckets; i += blockDim.x) hist[i] = 0;
   __syncthreads();
 
@@ -35,6 +37,7 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
     const int64_t work = (L + 32) * (N + 32) * gd.head_dim;  // +32: fixed per-tile costs
     int64_t key = work >> d.work_shift;
     if (key > kNumBuckets - 1) key = kNumBuckets - 1;
+    if (key < 0) key = 0;  // (offsets that decrease: the main kernels refuse such an item)
     if (s == tid) {
       key0 = (int)key;
       g0 = g;
@@ -88,6 +91,42 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
 
 hipError_t launch_schedule(const LaunchDesc& d, hipStream_t stream) {
   hipLaunchKernelGGL(build_schedule_kernel, dim3(1), dim3(kNumBuckets), 0, stream, d);
+  return hipGetLastError();
+}
+
+// Debug validation: one workgroup checks every sequence of every group by the offsets rules and
+// stores the OR of the error bits into the device error word (0 when all hold).
+__global__ void __launch_bounds__(1024) validate_offsets_kernel(LaunchDesc d) {
+  __shared__ int32_t bits;
+  if (threadIdx.x == 0) bits = 0;
+  __syncthreads();
+  int32_t e = 0;
+  for (int g = 0; g < d.n_groups; ++g) {
+    const GroupDesc& gd = d.grp[g];
+    OffsetsRules r;
+    r.num_seqs = gd.num_seqs;
+    r.self_attention = gd.self_attn;
+    r.total_q = gd.total_q;
+    r.total_kv = gd.total_kv;
+    r.max_q = gd.max_q;
+    r.max_kv = gd.max_kv;
+    for (int b = threadIdx.x; b < gd.num_seqs; b += blockDim.x) e |= seq_offsets_error(r, gd.q_off, gd.kv_off, b);
+  }
+  if (e) atomicOr(&bits, e);
+  __syncthreads();
+  if (threadIdx.x == 0) *d.err = bits;
+}
+
+hipError_t launch_validate(const LaunchDesc& d, hipStream_t stream) {
+  hipLaunchKernelGGL(validate_offsets_kernel, dim3(1), dim3(1024), 0, stream, d);
+  return hipGetLastError();
+}
+
+// Clears the device error word (calls whose kernels do not start with the work-list builder).
+__global__ void clear_error_kernel(int32_t* err) { *err = 0; }
+
+hipError_t launch_clear_error(int32_t* err, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(1), 0, stream, err);
   return hipGetLastError();
 }
 

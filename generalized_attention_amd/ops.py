@@ -38,6 +38,8 @@ class GroupArgs:
     shared_q: bool = False  # q is one query matrix shared by every sequence (rows of o: total_q)
     total_q: Optional[int] = None  # rows of o / lse / dout (default: rows of q)
     fp32_out: bool = False  # bf16 problem with float32 o, dq, dk, dv
+    validate: bool = False  # enqueue the offsets-validation kernel first (GDPA_FLAG_VALIDATE)
+    split_operands: bool = False  # P / dS as high + low bf16 pairs in every backward product
 
     @property
     def out_dtype(self) -> torch.dtype:
@@ -66,7 +68,9 @@ class GroupArgs:
         p.max_seqlen_kv = int(self.max_seqlen_kv)
         p.self_attention = 1 if self.self_attention else 0
         p.flags = ((_lib.GDPA_FLAG_PLANNED if self.planned else 0) | (_lib.GDPA_FLAG_SHARED_Q if self.shared_q else 0)
-                   | (_lib.GDPA_FLAG_FP32_OUT if self.fp32_out else 0))
+                   | (_lib.GDPA_FLAG_FP32_OUT if self.fp32_out else 0)
+                   | (_lib.GDPA_FLAG_VALIDATE if self.validate else 0)
+                   | (_lib.GDPA_FLAG_SPLIT_OPERANDS if self.split_operands else 0))
         p.q_offsets = self.q_offsets.data_ptr()
         p.kv_offsets = self.kv_offsets.data_ptr()
         p.head_acts = 0 if self.head_acts is None else self.head_acts.data_ptr()
@@ -124,6 +128,13 @@ def workspace(groups: Sequence[GroupArgs], pass_: int) -> torch.Tensor:
     if n == 0:
         raise _lib.GdpaError(_lib.GDPA_ERR_INVALID_ARGUMENT, "gdpa_workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=groups[0].q.device)
+
+
+def device_error(ws: torch.Tensor) -> int:
+    """The device error word of a workspace after the calls that used it (GDPA_DEVICE_ERR_* bits;
+    0 when every item's offsets passed). Synchronizes with the current stream."""
+    off = _lib.GDPA_WS_ERROR_OFFSET
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 def gdpa_plan(groups: Sequence[GroupArgs], ws: torch.Tensor) -> None:

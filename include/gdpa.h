@@ -20,19 +20,36 @@
  *   - Layouts are dense row-major with no strides: q, o, dout, dq are [total_q, H, d]; k, v, dk, dv
  *     are [total_kv, H, d]; g, dg are [total_kv, H] float32; lse is [total_q, H] float32.
  *   - q_offsets / kv_offsets are device int32 arrays of num_seqs+1 non-decreasing entries starting
- *     at 0; sequence b owns rows [offsets[b], offsets[b+1]). They are trusted (not re-validated on
- *     the device); the host-side hints max_seqlen_q / max_seqlen_kv must bound the real lengths.
+ *     at 0 and ending at total_q / total_kv; sequence b owns rows [offsets[b], offsets[b+1]). The
+ *     host-side hints max_seqlen_q / max_seqlen_kv must bound the real lengths (they size the
+ *     launch and the workspace).
  *   - The workspace `ws` (device memory of at least gdpa_workspace_size() bytes, 256-byte aligned)
  *     is scratch for the call's work list and, in the backward, for fp32 row accumulators (long
- *     key ranges that are processed in chunks, shared query matrices); its contents on entry are
- *     ignored.
+ *     key ranges that are processed in chunks, shared query matrices). Its first 4 bytes
+ *     (GDPA_WS_ERROR_OFFSET) are the device error word described below; the rest of its contents
+ *     on entry are ignored.
  *   - The library keeps no state between calls; distinct calls may run concurrently on different
  *     streams as long as they use distinct workspaces and outputs.
  *
  * Errors
  *   Every status check runs synchronously on the host before any HIP call: a non-zero return
  *   means nothing was enqueued. GDPA_ERR_HIP reports a failed kernel launch (hipGetLastError).
- *   Faults inside kernels surface on the caller's next synchronization, as usual in HIP.
+ *
+ *   The offsets live on the device, so the host cannot check them. Instead every kernel checks the
+ *   offsets of its own work item before touching memory: both row ranges inside their tensors,
+ *   lengths within what the launch provisioned from the max_seqlen hints, equal query and key
+ *   lengths under a window. An item that fails writes none of its outputs and sets bits of the
+ *   int32 device error word at GDPA_WS_ERROR_OFFSET in the workspace (GDPA_DEVICE_ERR_*), so a
+ *   violated precondition never leads to an out-of-bounds access. A call that launches kernels
+ *   clears the word first, except a bf16 call with GDPA_FLAG_PLANNED, which adds its bits to
+ *   what the word holds since the gdpa_plan that built its work list (gdpa_plan clears it). The
+ *   caller reads the word after synchronizing.
+ *
+ *   Debug validation: with GDPA_FLAG_VALIDATE in a problem's flags, or the environment variable
+ *   GDPA_DEBUG=1 at call time, the call first enqueues a kernel that checks every sequence by the
+ *   rules of gdpa_validate_offsets() (which runs the same checks on host copies) and writes the
+ *   result to the error word; when it is non-zero the main kernels then return without reading
+ *   or writing anything (outputs are left untouched).
  */
 #ifndef GDPA_H_
 #define GDPA_H_
@@ -67,6 +84,28 @@ extern "C" {
  * exact result. Groups of one call may differ in it. No effect on a float32 problem, whose
  * outputs are float32 already. */
 #define GDPA_FLAG_FP32_OUT 4
+
+/* gdpa_problem.flags: enqueue the offsets-validation kernel before the main kernels (see Errors
+ * above; the environment variable GDPA_DEBUG=1 has the same effect for every call). */
+#define GDPA_FLAG_VALIDATE 8
+
+/* gdpa_problem.flags (bf16, element-wise activations): P and dS enter every backward product as a
+ * high + low bf16 pair, as they do by default for sums of at most 16 terms (items with that few
+ * rows or keys) and for the softmax form. One rounding of P / dS to bf16 has a relative error of
+ * up to 2^-9 per term; for the dK / dV sums of a long sequence batched with many much shorter
+ * ones, that error can exceed 2e-2 of the whole tensor's RMS (which the short sequences lower).
+ * The pair brings it to about 2^-17. Costs two more matrix products per score block. */
+#define GDPA_FLAG_SPLIT_OPERANDS 16
+
+/* Byte offset of the int32 device error word in the workspace. */
+#define GDPA_WS_ERROR_OFFSET 0
+
+/* Bits of the device error word (and of gdpa_validate_offsets' result). */
+#define GDPA_DEVICE_ERR_OFFSETS 1 /* offsets decrease, leave their tensor, or do not start at 0 /
+                                     end at total_q, total_kv */
+#define GDPA_DEVICE_ERR_LENGTH 2  /* a sequence longer than max_seqlen_q / max_seqlen_kv allow */
+#define GDPA_DEVICE_ERR_SELF 4    /* self-attention (or a window) with query and key sequences that
+                                     differ */
 
 typedef enum gdpa_status {
   GDPA_OK = 0,
@@ -172,6 +211,17 @@ int gdpa_bwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, 
  * (Tile scheduling over jagged, large-batch inputs: Kunlun review, section 2.3.)
  */
 int gdpa_plan(const gdpa_problem* problems, int32_t n_groups, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The device offsets check on host copies: q_offsets_host / kv_offsets_host are host arrays of
+ * problem->num_seqs + 1 entries (the problem's own offset pointers are not read). Returns the OR
+ * of GDPA_DEVICE_ERR_* bits over all sequences (0: the offsets meet every rule the kernels rely
+ * on), or a negative gdpa_status if the problem itself is invalid or an array is NULL. The
+ * validation kernel enqueued by GDPA_FLAG_VALIDATE / GDPA_DEBUG=1 applies the same function to
+ * each sequence.
+ */
+int gdpa_validate_offsets(const gdpa_problem* problem, const int32_t* q_offsets_host,
+                          const int32_t* kv_offsets_host);
 
 /* Static description of a status code (never NULL). */
 const char* gdpa_strerror(int status);

@@ -241,6 +241,59 @@ def check_softmax_rows_sum_to_one(orc):
                 close(r["lse"][qo[b]:qo[b + 1], hh], torch.logsumexp(S, dim=1).numpy(), what="lse")
 
 
+def check_rows_without_keys(orc):
+    """A query row that sees no key: its softmax lse is log of an empty sum (torch.logsumexp of an
+    all -inf score row gives -inf) and its output is the empty sum, zero, in every form. Rows of a
+    sample with no keys (cross-attention, n_b = 0) and rows that a window moves past the last key
+    (cross-attention with window (0, 0): row i sees only key i) are both such rows."""
+    lq, lk = [3, 5, 2], [0, 2, 4]
+    pb = rand_problem(12, lq, lk, gate=True)
+    for window in ((-1, -1), (0, 0)):
+        for act in ("softmax", "gelu"):
+            r = orc.fwd(pb["q"], pb["k"], pb["v"], pb["qo"], pb["ko"], act=act, scale=0.6, g=pb["g"],
+                        window=window)
+            for b in range(len(lq)):
+                for i in range(lq[b]):
+                    row = int(pb["qo"][b]) + i
+                    allowed = _mask(lq[b], lk[b], window)[i] if lk[b] else torch.zeros(0, dtype=torch.bool)
+                    if bool(allowed.any()):
+                        continue
+                    assert np.all(r["o"][row] == 0.0), f"o of a row without keys ({act}, {window})"
+                    if act == "softmax":
+                        empty = torch.full((max(lk[b], 1),), float("-inf"), dtype=torch.float64)
+                        want = float(torch.logsumexp(empty, dim=0))
+                        got = r["lse"][row]
+                        assert np.all(got == want), f"lse of a row without keys: {got} vs {want}"
+    # and a row with keys keeps a finite lse
+    r = orc.fwd(pb["q"], pb["k"], pb["v"], pb["qo"], pb["ko"], act="softmax", scale=0.6, g=pb["g"])
+    assert np.all(np.isfinite(r["lse"][int(pb["qo"][1]):])), "rows with keys"
+
+
+def check_rejects_bad_arguments(orc):
+    """Arguments outside the definition are refused (ValueError) instead of read: offsets that
+    decrease or do not start at zero, and a sequence with more rows than a shared query matrix
+    holds. The shared matrix is a view into a larger buffer, so a wrongly accepted call reads
+    memory that exists."""
+    q = np.zeros((2, 1, 4))
+    for qo, ko in (([0, 2, 1], [0, 1, 2]), ([1, 2], [0, 2])):
+        try:
+            orc.fwd(q, q, q, qo, ko, act="gelu", scale=1.0)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"offsets {qo} / {ko} accepted")
+    big = np.zeros((8, 1, 4))
+    shared = big[:3]  # S = 3 rows
+    kv = np.zeros((6, 1, 4))
+    for lq in ([3, 2], [2, 4]):
+        try:
+            orc.fwd(shared, kv, kv, offsets(lq), offsets([3, 3]), act="softmax", scale=1.0, shared_q=True)
+        except ValueError:
+            assert max(lq) > 3, "a sequence within the shared rows was refused"
+        else:
+            assert max(lq) <= 3, f"a sequence of {max(lq)} rows over a 3-row shared query matrix accepted"
+
+
 def check_gate_infinity_is_sdpa(orc):
     pb = rand_problem(5, [7, 3], None, gate=False)
     g = np.full((pb["k"].shape[0], pb["k"].shape[1]), 40.0)
@@ -355,6 +408,8 @@ FAST_CHECKS = [
     ("PFFN identity gelu", lambda o: check_pffn_identity(o, "gelu")),
     ("PFFN identity silu", lambda o: check_pffn_identity(o, "silu")),
     ("rows sum to one", lambda o: check_softmax_rows_sum_to_one(o)),
+    ("rows without keys", lambda o: check_rows_without_keys(o)),
+    ("rejects bad arguments", lambda o: check_rejects_bad_arguments(o)),
     ("gate inf is sdpa", lambda o: check_gate_infinity_is_sdpa(o)),
     ("window covering sequence", lambda o: check_window_covering_sequence_is_full(o)),
     ("invariants", lambda o: check_invariants(o)),

@@ -140,7 +140,7 @@ INVALID_PROBLEMS = [
     ("nan scale", dict(scale=float("nan")), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window below -1", dict(window_left=-2), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("window on cross-attention", dict(window_left=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
-    ("unknown flag", dict(flags=8), _lib.GDPA_ERR_INVALID_ARGUMENT),
+    ("unknown flag", dict(flags=32), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("shared queries in self-attention", dict(flags=_lib.GDPA_FLAG_SHARED_Q, self_attention=1, total_kv=100,
                                               max_seqlen_kv=60), _lib.GDPA_ERR_INVALID_ARGUMENT),
     ("shared queries in fp32", dict(flags=_lib.GDPA_FLAG_SHARED_Q, dtype=_lib.GDPA_DTYPE_FP32), _lib.GDPA_ERR_UNSUPPORTED),
@@ -259,3 +259,50 @@ def test_binding_fp32_outputs_marshalling():
         want = torch.float32 if fp32_out else torch.bfloat16
         assert o.dtype == dq.dtype == dk.dtype == dv.dtype == want and lse is None and dg is None
         assert o.shape == q.shape and dk.shape == k.shape
+
+
+def _offsets(lengths):
+    import numpy as np
+    o = np.zeros(len(lengths) + 1, dtype=np.int32)
+    o[1:] = np.cumsum(lengths)
+    return o
+
+
+def test_validate_offsets_host(lib):
+    """The offsets rules that the kernels' own item checks and the debug validation kernel apply,
+    run on host arrays: each kind of violation sets its bit, and valid offsets give 0."""
+    import numpy as np
+    E_OFF, E_LEN, E_SELF = _lib.GDPA_DEVICE_ERR_OFFSETS, _lib.GDPA_DEVICE_ERR_LENGTH, _lib.GDPA_DEVICE_ERR_SELF
+    qo, ko = _offsets([40, 60]), _offsets([256, 256])
+    p = good_problem()  # B=2, total_q=100, total_kv=512, max 60 / 256
+    assert _lib.gdpa_validate_offsets(p, qo, ko) == 0
+    cases = [
+        ("decreasing", np.array([0, 50, 40], np.int32), ko, E_OFF),
+        ("not starting at 0", np.array([5, 45, 100], np.int32), ko, E_OFF),
+        ("not ending at total_q", np.array([0, 40, 90], np.int32), ko, E_OFF),
+        ("past total_kv", qo, np.array([0, 256, 600], np.int32), E_OFF | E_LEN),
+        ("longer than max_seqlen_q", np.array([0, 30, 100], np.int32), ko, E_LEN),
+        ("longer than max_seqlen_kv", qo, np.array([0, 200, 512], np.int32), E_LEN),
+        ("negative start", np.array([-4, 40, 100], np.int32), ko, E_OFF),
+    ]
+    for name, q_off, kv_off, bits in cases:
+        assert _lib.gdpa_validate_offsets(p, q_off, kv_off) == bits, name
+    # self-attention: the two offset arrays must coincide
+    sp = good_problem(self_attention=1, total_kv=100, max_seqlen_kv=60)
+    assert _lib.gdpa_validate_offsets(sp, qo, qo) == 0
+    assert _lib.gdpa_validate_offsets(sp, qo, np.array([0, 60, 100], np.int32)) == E_SELF
+    # a shared query matrix bounds every sequence's rows by its own row count max_seqlen_q
+    shared = good_problem(flags=_lib.GDPA_FLAG_SHARED_Q, max_seqlen_q=64, total_q=128)
+    assert _lib.gdpa_validate_offsets(shared, _offsets([64, 64]), ko) == 0
+    assert _lib.gdpa_validate_offsets(shared, _offsets([65, 63]), ko) == E_LEN
+    # an invalid problem is refused as such
+    assert _lib.gdpa_validate_offsets(good_problem(head_dim=48), qo, ko) == _lib.GDPA_ERR_UNSUPPORTED
+
+
+def test_validate_flag_accepted(lib):
+    """GDPA_FLAG_VALIDATE changes no workspace; the error word sits in the workspace header."""
+    for pass_ in (0, 1):
+        base = _lib.gdpa_workspace_size([good_problem()], pass_)
+        assert _lib.gdpa_workspace_size([good_problem(flags=_lib.GDPA_FLAG_VALIDATE)], pass_) == base
+        assert base >= 256 + 4  # header (error word) + a work list
+    assert _lib.GDPA_WS_ERROR_OFFSET == 0

@@ -39,6 +39,12 @@ MUTANTS = [
      "double sij = p.scale * dot(qi, p.k + ((k0 + j) * H + (H - 1 - h)) * d, d);"),
     ("dg missing sigmoid", "+= sigmoid(-p.g[(k0 + j) * H + h]) * dsij", "+= dsij"),
     ("per-head activation ignored", "return p.head_acts ? p.head_acts[h] : p.act;", "return p.act;"),
+    ("lse of an empty row is zero", "if (n <= 0) return -std::numeric_limits<double>::infinity();",
+     "if (n <= 0) return 0.0;"),
+    ("empty softmax row not zeroed", "for (int c = 0; c < d; ++c) oi[c] = 0.0;", "for (int c = 0; c < d; ++c) oi[c] = (hi < lo) ? 1.0 : 0.0;"),
+    ("shared query row bound dropped", "if (p.q_off[b + 1] - p.q_off[b] > p.shared_q) return false;",
+     "if (false) return false;"),
+    ("offsets start unchecked", "if (p.q_off[0] != 0 || p.kv_off[0] != 0) return false;", ""),
     ("v transposed", "oi[c] += pr[j - lo] * vj[c];", "oi[c] += pr[j - lo] * p.v[((k0 + c % (hi - lo + 1)) * H + h) * d + (j % d)];"),
 ]
 

@@ -38,15 +38,16 @@ def run_bwd(groups_dev, douts, fwd_outs, want_dg):
     return ga.gdpa_bwd_grouped(groups_dev, douts, fwd_outs=fwd_outs, want_dg=want_dg)
 
 
-def compare_workload(w, passes, sample=None, want_dg=True, scale=None, fp32_out=False):
+def compare_workload(w, passes, sample=None, want_dg=True, scale=None, fp32_out=False, split_operands=False):
     """Run the workload on the GPU; compare all (or the sampled) sequences with the oracle.
-    fp32_out: the bf16 groups write float32 outputs (checked by the literal rule)."""
+    fp32_out: the bf16 groups write float32 outputs (checked by the literal rule).
+    split_operands: GDPA_FLAG_SPLIT_OPERANDS on every group."""
+    import dataclasses
     groups = w.groups
     if scale is not None:
-        import dataclasses
         for g in groups:
             g.spec = dataclasses.replace(g.spec, scale=scale)
-    dev = [device_group(g, fp32_out=fp32_out) for g in groups]
+    dev = [dataclasses.replace(device_group(g, fp32_out=fp32_out), split_operands=split_operands) for g in groups]
     print(f"[gpu] {w.name} seed={w.seed} groups={len(groups)} T={[g.total_q for g in groups][:3]} "
           f"passes={passes}", flush=True)
     fwd_outs = run_fwd(dev)
@@ -85,7 +86,10 @@ def compare_workload(w, passes, sample=None, want_dg=True, scale=None, fp32_out=
             lr = ref["lse"][:, sm]
             fin = np.isfinite(lr)
             assert np.array_equal(fin, np.isfinite(lg))
-            assert np.max(np.abs(lg[fin] - lr[fin]), initial=0.0) < 2e-3 * max(1.0, np.abs(lr[fin]).max(initial=1.0))
+            if dt == "fp32":  # the stated fp32 rule: absolute 1e-5
+                report[f"g{gi}.lse"] = chk("fp32", lg[fin], lr[fin], f"{w.name} g{gi} lse")
+            else:  # a diagnostic of the bf16 kernels (not an output the rule grades)
+                assert np.max(np.abs(lg[fin] - lr[fin]), initial=0.0) < 2e-3 * max(1.0, np.abs(lr[fin]).max(initial=1.0))
         if bwd_outs is not None:
             rb = oracle.group_bwd(sub, want_dg=want_dg and g.g is not None)
             gb = bwd_outs[gi]
@@ -98,12 +102,10 @@ def compare_workload(w, passes, sample=None, want_dg=True, scale=None, fp32_out=
             report[f"g{gi}.dk"] = chk(dt, to64(gb["dk"])[kr], rb["dk"], f"{w.name} g{gi} dK")
             report[f"g{gi}.dv"] = chk(dt, to64(gb["dv"])[kr], rb["dv"], f"{w.name} g{gi} dV")
             if "dg" in gb:
-                # gate gradient in fp32: same relative-to-RMS rule (it is a sum over a column of dS)
-                ref_dg = rb["dg"]
-                err = np.abs(to64(gb["dg"])[kr] - ref_dg)
-                rms = math.sqrt(float(np.mean(ref_dg ** 2))) if ref_dg.size else 0.0
-                if not err.max(initial=0.0) <= 2e-2 * rms + 1e-7:
-                    failures.append(f"{w.name} g{gi} dG: max err {err.max():.3e} rms {rms:.3e}")
+                # the gate gradient is a float32 output: an fp32 problem takes the absolute 1e-5
+                # rule, a bf16 problem the 2e-2 x RMS rule with nothing rounded to bf16
+                report[f"g{gi}.dg"] = chk("fp32" if dt == "fp32" else "bf16/f32", to64(gb["dg"])[kr], rb["dg"],
+                                          f"{w.name} g{gi} dG")
     print(f"[gpu] {w.name} literal max|err|/RMS: " + ", ".join(f"{k}={v:.4f}" for k, v in report.items()), flush=True)
     assert not failures, "\n".join(failures)
     return report
@@ -238,6 +240,14 @@ def test_grouped10_full_size_sampled():
     compare_workload(make_workload("grouped10", 0), ("fwd", "bwd"), sample=_sampler(1))
 
 
+@pytest.mark.parametrize("name,k", [("pffn_train", 6), ("causal_gated", 3), ("grouped10", 1)])
+def test_full_size_sampled_fp32_outputs(name, k):
+    """The same full-size launches with float32 outputs, at each workload's own scale: nothing is
+    rounded to bf16 on the way out, so the stated rule max|gpu - ref| <= 2e-2 x RMS(ref) applies
+    literally (no storage term)."""
+    compare_workload(make_workload(name, 0), ("fwd", "bwd"), sample=_sampler(k), fp32_out=True)
+
+
 def _tiny_lengths(n):
     return np.random.default_rng(11).integers(0, 4, size=n).tolist()
 
@@ -256,15 +266,44 @@ def test_many_tiny_sequences():
     _compare_sampled_with_ends(make_workload("causal_gated", 12, lengths=_tiny_lengths(1 << 17)))
 
 
-@pytest.mark.xfail(strict=False, reason=(
-    "known accuracy gap: with 0-3 query rows per sample, dK and dV are sums of at most three "
-    "products; where two large ones nearly cancel, the bf16 rounding of the P / dS operands "
-    "(relative 2^-9 of each product) exceeds 2e-2 x RMS of the output (3 of ~400k sampled "
-    "elements, literal ratio up to 0.049 at seed 12). The softmax form's second bf16 term for "
-    "P and dS would remove it for the element-wise forms too."))
 def test_many_tiny_sequences_pffn():
-    """2^15 PFFN-form samples of 0 to 3 rows and 8 keys each (the short-key backward)."""
+    """2^15 PFFN-form samples of 0 to 3 rows and 8 keys each (the short-key backward): dK and dV
+    are sums of at most three products, O and dQ of eight, so P and dS enter those products as a
+    high + low bf16 pair."""
     _compare_sampled_with_ends(make_workload("pffn_train", 12, lengths=_tiny_lengths(1 << 17)[:1 << 15], keys=8))
+
+
+def test_many_tiny_sequences_pffn_256_keys():
+    """1024 PFFN-form samples of 0 to 3 rows and 256 keys (the workgroup backward, 8 waves at
+    d = 64): few-row items take the high + low operand pair in dV and dK."""
+    w = make_workload("pffn_train", 13, lengths=_tiny_lengths(1024), ctx_dim=64)
+    _compare_sampled_with_ends(w)
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_few_rows_long_keys_pffn(act):
+    """Samples of 0 to 16 rows over 600 keys (key chunks): every item takes the operand pair in
+    dV and dK of every chunk (a CPU emulation of single-rounded operands puts dK / dV at 0.028 to
+    0.035 of RMS for these inputs)."""
+    w = make_workload("pffn_train", 14, lengths=[0, 1, 2, 3, 16, 5, 2, 1, 3, 0, 16], keys=600, act=act, scale=0.125)
+    compare_workload(w, ("fwd", "bwd"))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("pffn_train", dict(lengths=[0, 1, 2, 3, 16, 17, 5, 300], keys=600, scale=0.125)),  # key chunks
+    ("pffn_train", dict(lengths=[0, 1, 2, 3, 16, 17, 5, 64], scale=0.125, act="gelu")),  # resident keys
+    ("pffn_train", dict(lengths=[1, 2, 3, 2, 30, 1, 3, 2], keys=24, scale=0.125)),  # short-key kernel
+    ("causal_gated", dict(lengths=[1, 2, 3, 40, 2, 700], act="silu", window=(300, 0))),  # window in key chunks
+    ("causal_gated", dict(lengths=[1, 2, 3, 40, 2, 700], act="gelu", window=(127, 0))),  # ring -> key chunks
+])
+def test_split_operands_flag(name, kw):
+    """Few-row samples beside a longer one: the short ones lower the tensor's RMS, and one bf16
+    rounding of P / dS in the longer sample's dK / dV sums then can exceed 2e-2 of it (a CPU emulation
+    gives 0.019 to 0.024 for the first three); GDPA_FLAG_SPLIT_OPERANDS puts every item on the
+    operand pair."""
+    import dataclasses
+    w = make_workload(name, 14, **kw)
+    compare_workload(w, ("fwd", "bwd"), split_operands=True)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -494,25 +533,13 @@ def test_short_keys_pffn(keys, act):
     compare_workload(w, ("fwd", "bwd"))
 
 
-def test_single_key_pffn():
-    """n = 1: every output row of O and dQ is one product of a bf16-rounded operand (P or dS) with
-    a key row, so its error is relative: rounding P / dS to bf16 (unit roundoff 2^-8) plus the
-    storage rounding. dK and dV still sum over all rows and keep the standard rule."""
-    w = make_workload("pffn_train", 12, num_seqs=7, len_range=(1, 300), keys=1, act="silu", scale=0.125)
-    g = w.groups[0]
-    dev = device_group(g)
-    o, lse = ga.gdpa_fwd(dev)
-    r = ga.gdpa_bwd(dev, g.dout.to("cuda:0"), o=o, lse=lse)
-    torch.cuda.synchronize()
-    ref_f = oracle.group_fwd(g)
-    ref_b = oracle.group_bwd(g)
-    for name, gpu, ref in (("O", to64(o), ref_f["o"]), ("dQ", to64(r["dq"]), ref_b["dq"])):
-        rms = float(np.sqrt(np.mean(ref * ref)))
-        bound = 2.0 ** -8 * np.abs(ref) + half_ulp_bf16(np.maximum(np.abs(ref), np.abs(gpu))) + 1e-6 * rms
-        err = np.abs(gpu - ref)
-        assert np.all(err <= bound), f"{name}: {int((err > bound).sum())} elements above the single-product bound"
-    check("bf16", to64(r["dk"]), ref_b["dk"], "dK")
-    check("bf16", to64(r["dv"]), ref_b["dv"], "dV")
+@pytest.mark.parametrize("keys", [1, 2, 16])
+def test_single_key_pffn(keys):
+    """n = 1, 2, 16: every output row of O and dQ is a sum of that few products, heavy-tailed
+    enough that one bf16 rounding of P / dS would exceed 2e-2 x RMS; with the operand pair they
+    meet the stated rule like every other case."""
+    w = make_workload("pffn_train", 12, num_seqs=7, len_range=(1, 300), keys=keys, act="silu", scale=0.125)
+    compare_workload(w, ("fwd", "bwd"))
 
 
 def test_short_keys_gated_self_attention():
