@@ -38,7 +38,8 @@ GDPA_DEVICE_ERR_LENGTH = 2
 GDPA_DEVICE_ERR_SELF = 4
 
 EXPORTED = ("gdpa_workspace_size", "gdpa_plan", "gdpa_fwd", "gdpa_bwd", "gdpa_fwd_grouped",
-            "gdpa_bwd_grouped", "gdpa_validate_offsets", "gdpa_strerror", "gdpa_version")
+            "gdpa_bwd_grouped", "gdpa_validate_offsets", "gdpa_bwd_noalloc", "gdpa_strerror", "gdpa_version")
+GDPA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class gdpa_problem(ctypes.Structure):
@@ -110,6 +111,8 @@ def load(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     lib.gdpa_plan.argtypes = [P(gdpa_problem), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.gdpa_plan.restype = ctypes.c_int
+    lib.gdpa_bwd_noalloc.argtypes = [P(gdpa_problem), P(gdpa_tensors), ctypes.c_void_p]
+    lib.gdpa_bwd_noalloc.restype = ctypes.c_int
     lib.gdpa_validate_offsets.argtypes = [P(gdpa_problem), ctypes.c_void_p, ctypes.c_void_p]
     lib.gdpa_validate_offsets.restype = ctypes.c_int
     lib.gdpa_strerror.argtypes = [ctypes.c_int]
@@ -157,6 +160,10 @@ def gdpa_fwd(problem, tensors, ws, ws_bytes, stream) -> int:
 def gdpa_bwd(problem, tensors, ws, ws_bytes, stream) -> int:
     return load().gdpa_bwd(ctypes.byref(problem), ctypes.byref(tensors), ctypes.c_void_p(ws),
                            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream))
+
+
+def gdpa_bwd_noalloc(problem, tensors, stream) -> int:
+    return load().gdpa_bwd_noalloc(ctypes.byref(problem), ctypes.byref(tensors), ctypes.c_void_p(stream))
 
 
 def gdpa_fwd_grouped(problems, tensors, ws, ws_bytes, stream) -> int:

@@ -7,12 +7,23 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gdpa.h"
 #include "gdpa_check.hpp"
 #include "gdpa_launch.hpp"
 
 namespace gdpa {
+
+// ---- Library-owned scratch for callers that cannot allocate (gdpa_bwd_noalloc) ----------------
+//
+// One array per GPU, in device memory for as long as the process runs. In host code `scratch` is
+// only a stand-in symbol: its device address is looked up once per device and kept in
+// scratch_ptr[device]; kernels and copies get that address, never the symbol itself.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static_assert(kScratchBytes == GDPA_NOALLOC_SCRATCH_BYTES, "documented scratch size");
+__device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -262,6 +273,28 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
   return e == hipSuccess ? GDPA_OK : GDPA_ERR_HIP;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device (looked up on the first call there).
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 }  // namespace gdpa
 
@@ -279,6 +312,20 @@ int gdpa_fwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws,
 
 int gdpa_bwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws, size_t ws_bytes, void* stream) {
   return gdpa::run(problem, tensors, 1, ws, ws_bytes, stream, 1);
+}
+
+int gdpa_bwd_noalloc(const gdpa_problem* problem, const gdpa_tensors* tensors, void* stream) {
+  gdpa::WsLayout L;
+  int rc = gdpa::layout(problem, 1, 1, &L);
+  if (rc != GDPA_OK) return rc;
+  if (problem->flags & GDPA_FLAG_PLANNED) return GDPA_ERR_INVALID_ARGUMENT;  // the scratch holds no plan of its own
+  if (L.total > gdpa::kScratchBytes) return GDPA_ERR_WORKSPACE;
+  // every argument check before the first HIP call (the address lookup)
+  if (!tensors) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((rc = gdpa::check_tensors(*problem, *tensors, 1)) != GDPA_OK) return rc;
+  void* ws = nullptr;
+  if (gdpa::scratch_on_current_device(&ws) != hipSuccess) return GDPA_ERR_HIP;
+  return gdpa::run(problem, tensors, 1, ws, gdpa::kScratchBytes, stream, 1);
 }
 
 int gdpa_fwd_grouped(const gdpa_problem* problems, const gdpa_tensors* tensors, int32_t n_groups, void* ws,
@@ -340,6 +387,6 @@ const char* gdpa_strerror(int status) {
   }
 }
 
-int gdpa_version(void) { return 300; }  // 0.3.0: device error word, offsets validation
+int gdpa_version(void) { return 300; }  // 0.3.0: device error word, offsets validation, gdpa_bwd_noalloc
 
 }  // extern "C"

@@ -192,6 +192,26 @@ int gdpa_fwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws,
 int gdpa_bwd(const gdpa_problem* problem, const gdpa_tensors* tensors, void* ws, size_t ws_bytes,
              void* stream);
 
+/* Largest workspace gdpa_bwd_noalloc can provide (bytes). */
+#define GDPA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * gdpa_bwd without a workspace argument and without any allocation, for callers that cannot
+ * allocate device memory at call time (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a 16 MiB array (GDPA_NOALLOC_SCRATCH_BYTES)
+ * of device memory that the library holds on each GPU it runs on until the process ends; the
+ * call uses the array of the current device (which must be the stream's device) and returns
+ * GDPA_ERR_WORKSPACE, with nothing enqueued, when gdpa_workspace_size(problem, 1, 1) exceeds it.
+ * It allocates, frees and synchronizes nothing (the first call on a device looks the array's
+ * address up). GDPA_FLAG_PLANNED is refused (GDPA_ERR_INVALID_ARGUMENT): every call builds its
+ * own work list. Every call on one GPU shares that GPU's array, so calls that overlap in time on
+ * one GPU (other streams, other threads) race and must not be issued; the array keeps the last
+ * call's contents, which no call reads before writing (the device error word is cleared by the
+ * call itself, and items that fail their offsets check still write nothing, but the word is not
+ * reported). Arguments, outputs and errors are otherwise those of gdpa_bwd.
+ */
+int gdpa_bwd_noalloc(const gdpa_problem* problem, const gdpa_tensors* tensors, void* stream);
+
 /*
  * Grouped forward / backward: `n_groups` (1..GDPA_MAX_GROUPS) independent problems, each with its
  * own shapes, activation and tensors, in ONE launch of the main kernel (event-level

@@ -306,3 +306,17 @@ def test_validate_flag_accepted(lib):
         assert _lib.gdpa_workspace_size([good_problem(flags=_lib.GDPA_FLAG_VALIDATE)], pass_) == base
         assert base >= 256 + 4  # header (error word) + a work list
     assert _lib.GDPA_WS_ERROR_OFFSET == 0
+
+
+def test_noalloc_rejections_on_host(lib):
+    """gdpa_bwd_noalloc checks everything before its first HIP call: a workspace beyond the 16 MiB
+    scratch (a shared query matrix's fp32 partials) and a planned call are refused, as is an
+    invalid problem."""
+    big = good_problem(flags=_lib.GDPA_FLAG_SHARED_Q, num_seqs=600, max_seqlen_q=256, total_q=600 * 256,
+                       total_kv=512, max_seqlen_kv=256)
+    assert _lib.gdpa_workspace_size([big], 1) > _lib.GDPA_NOALLOC_SCRATCH_BYTES
+    assert _lib.gdpa_bwd_noalloc(big, good_tensors(), 0) == _lib.GDPA_ERR_WORKSPACE
+    assert _lib.gdpa_bwd_noalloc(good_problem(flags=_lib.GDPA_FLAG_PLANNED), good_tensors(), 0) == \
+        _lib.GDPA_ERR_INVALID_ARGUMENT
+    assert _lib.gdpa_bwd_noalloc(good_problem(head_dim=48), good_tensors(), 0) == _lib.GDPA_ERR_UNSUPPORTED
+    assert _lib.gdpa_bwd_noalloc(good_problem(), good_tensors(dq=0), 0) == _lib.GDPA_ERR_INVALID_ARGUMENT
