@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.1,
+                    help="seconds of untimed steps before the warm-up steps (clock settling)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache steps (keeps a profiler's per-kernel averages to the warm steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -262,6 +264,17 @@ def main():
     except RuntimeError as exc:
         refs["hbm_error"] = str(exc)[:200]
     torch.cuda.empty_cache()
+
+    # Clock settling: the step itself, repeated for a fixed wall time before the W warm-up steps
+    # (an idle or GEMM-loaded GPU runs the first memory-bound steps at a lower clock; a training
+    # loop runs at the settled one). Untimed, reported as settle_steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         step()
@@ -346,6 +359,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

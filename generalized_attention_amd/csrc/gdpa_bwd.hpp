@@ -28,6 +28,8 @@
 // element-wise VALU work. Every output element is written exactly once (no atomics).
 #pragma once
 
+#include <type_traits>
+
 #include "gdpa_device.hpp"
 #include "gdpa_launch.hpp"
 
@@ -66,7 +68,8 @@ struct BwdGeo {
   static constexpr int QBUFS = NW == 8 ? 2 : 1;
   static constexpr int OFF_QN1 = OFF_GATE + CAP * 4;
   static constexpr int OFF_DON1 = OFF_QN1 + QT * NROW;
-  static constexpr int BYTES = QBUFS == 2 ? OFF_DON1 + QT * NROW : OFF_GATE + CAP * 4;
+  static constexpr int OFF_QNRM = QBUFS == 2 ? OFF_DON1 + QT * NROW : OFF_GATE + CAP * 4;  // [2][NW] max ||q||^2
+  static constexpr int BYTES = OFF_QNRM + 2 * NW * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
   static_assert(CAP == bwd_capacity(D), "resident keys per workgroup");
   static_assert(NW == 4 || D <= 64, "8 waves only for d <= 64");
@@ -96,6 +99,7 @@ struct BwdWave {
   float dgs[G::KB];
   float gate[G::KB];   // this lane's key: gate term (natural units; log2 units for softmax)
   float graw[G::KB];   // raw G of this lane's key (for dG)
+  float kn2[G::KB];    // largest ||k||^2 of each owned block's keys (uniform)
   int cur[G::KB];      // block held in each owned slot (-1: none); uniform
 };
 
@@ -157,6 +161,14 @@ __device__ __forceinline__ void take_commit(BwdWave<D, NW>& st, int kb, char* ld
   st.gate[kb] = t;
   st.graw[kb] = tr.graw;
   st.dgs[kb] = 0.0f;
+  if constexpr (ACT != GDPA_ACT_SOFTMAX) {
+    // the block's largest ||k||^2 (the series bound of ungated element-wise tiles); the lane holds
+    // half of its key's row, the other half sits 32 lanes away
+    float n2 = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) n2 += sumsq_bf16x8(tr.k[kk]);
+    st.kn2[kb] = wave_max(n2 + __shfl_xor(n2, 32, 64));
+  }
   if (g == 0) reinterpret_cast<float*>(lds + G::OFF_GATE)[pos] = t;
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
@@ -271,11 +283,26 @@ __device__ void prefetch_qtile(QTileRegs<D, NW>& pf, const bf16* qseq, const bf1
   }
 }
 
-// buf: which Q / dO tile buffer (the second exists with 8 waves)
-template <int D, int NW, bool SOFTMAX, bool DSUM = false>
+// buf: which Q / dO tile buffer (the second exists with 8 waves).
+// QNORM: each wave also writes the largest ||q||^2 of the tile rows it stored to
+// G::OFF_QNRM + 4 (buf * NW + w) (the series bound of ungated element-wise tiles).
+template <int D, int NW, bool SOFTMAX, bool DSUM = false, bool QNORM = false>
 __device__ void store_qtile(char* lds, const QTileRegs<D, NW>& pf, int buf = 0) {
   using G = BwdGeo<D, NW>;
   const int qoff = buf ? G::OFF_QN1 : G::OFF_QN, doff = buf ? G::OFF_DON1 : G::OFF_DON;
+  if constexpr (QNORM) {
+    // a row's CPR chunks sit in CPR consecutive lanes (rows past the end hold zeros)
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G::NPF; ++i) {
+      float n2 = sumsq_bf16x8(pf.q[i]);
+#pragma unroll
+      for (int off = 1; off < G::CPR; off <<= 1) n2 += __shfl_xor(n2, off, 64);
+      m = fmaxf(m, n2);
+    }
+    m = wave_max(m);
+    if (lane_id() == 0) reinterpret_cast<float*>(lds + G::OFF_QNRM)[buf * NW + (threadIdx.x >> 6)] = m;
+  }
 #pragma unroll
   for (int i = 0; i < G::NPF; ++i) {
     const int idx = threadIdx.x + i * G::THREADS;
@@ -415,6 +442,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     st.gate[kb] = 0.0f;
     st.graw[kb] = 0.0f;
     st.dgs[kb] = 0.0f;
+    st.kn2[kb] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) {
       st.kreg[kb][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
@@ -436,6 +464,11 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   // element-wise forms without a gate carry p' = phi(scale s) / scale; dV is scaled at the end
   float c1 = 0.0f, c3 = 0.0f;
   if constexpr (!softmax) PointAct<ACT>::coeffs(has_gate ? 1.0f : gd.scale, c1, c3);
+  // ungated element-wise tiles whose arguments are all proven within the series range (tile rows'
+  // largest ||q||^2 from the staging waves, the wave's keys' largest ||k||^2) take SeriesAct
+  constexpr bool kSeries = !softmax && !GATED;
+  float a1 = 0.0f, a3 = 0.0f, d1 = 0.0f, d3 = 0.0f;
+  if constexpr (kSeries) SeriesAct<ACT>::coeffs(gd.scale, a1, a3, d1, d3);
   const float dv_scale = (!softmax && !has_gate) ? gd.scale : 1.0f;
   const float* lse2 = reinterpret_cast<const float*>(lds + G::OFF_ROW);
   float* dpart = reinterpret_cast<float*>(lds + G::OFF_DPART);
@@ -447,7 +480,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   QTileRegs<D, NW> pf;
   prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, t0 * G::QT, L, it.dsumseq);
   __syncthreads();  // K^T staging zeroed
-  store_qtile<D, NW, softmax, DSUM>(lds, pf);  // first tile
+  store_qtile<D, NW, softmax, DSUM, kSeries>(lds, pf);  // first tile
   if (t0 + 1 < t1)
     prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, (t0 + 1) * G::QT, L, it.dsumseq);
   if constexpr (!WINDOWED) {
@@ -622,174 +655,205 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     // the S / dP products of iteration it+1 are issued before the element-wise work of it, so the
     // MFMA pipe runs while the VALU works.
     if constexpr (CHUNK != 2) {
-      constexpr int NIT = 2 * KACT;
-      const int sx_cur = (FQ && (j & 1)) ? G::OFF_SXL : G::OFF_SX;  // this tile's dS^T area
-      const int q_cur = (FQ && (j & 1)) ? G::OFF_QN1 : G::OFF_QN;    // this tile's Q / dO buffer
-      const int do_cur = (FQ && (j & 1)) ? G::OFF_DON1 : G::OFF_DON;
-      f32x16 sacc[2], dpacc[2];
-      bf16x8 qa[G::KK], da[G::KK];
-      bf16x8 dota[G::DT][2], qta[G::DT][2];
-      float lrow[16], drow[16];
-      auto load_a = [&](int qs) {
+      bool series = false;
+      if constexpr (kSeries) {
+        const float* qnrm = reinterpret_cast<const float*>(lds + G::OFF_QNRM) + ((FQ && (j & 1)) ? NW : 0);
+        float qn2 = 0.0f, kn2 = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < G::KK; ++kk) {
-          qa[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + q_cur + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
-          da[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + do_cur + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
-        }
-      };
-      auto issue_sdp = [&](int kb, int slot) {
-        sacc[slot] = f32x16{};
-        dpacc[slot] = f32x16{};
+        for (int ww = 0; ww < NW; ++ww) qn2 = fmaxf(qn2, qnrm[ww]);
 #pragma unroll
-        for (int kk = 0; kk < G::KK; ++kk) {
-          sacc[slot] = mfma32(qa[kk], st.kreg[kb][kk], sacc[slot]);
-          dpacc[slot] = mfma32(da[kk], st.vreg[kb][kk], dpacc[slot]);
-        }
-      };
-      // the products of iteration it+1 are issued before the element-wise work of it (the dO^T / Q^T
-      // operands of dV / dK are read only after it, which keeps their registers free meanwhile).
-      // Key-chunk passes, whose fp32 dQ rows already hold registers, run without it (measured
-      // faster there: shared seed queries 540 -> 523 us), and so does the softmax form with 8
-      // waves (no registers to spare).
-      constexpr bool PIPE = CHUNK == 0 && !(split && NW == 8);
-      if constexpr (PIPE) {
-        load_a(0);
-        issue_sdp(0, 0);
+        for (int kb = 0; kb < KACT; ++kb) kn2 = fmaxf(kn2, act[kb] ? st.kn2[kb] : 0.0f);
+        series = seq_series_ok(gd.scale, qn2, kn2);
       }
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int qs = it / KACT, kb = it % KACT, cs = PIPE ? (it & 1) : 0;
-        if constexpr (PIPE) {
-          if (it + 1 < NIT) {
-            if ((it + 1) / KACT != qs) load_a((it + 1) / KACT);
-            issue_sdp((it + 1) % KACT, cs ^ 1);
+      // the main pass of the tile, instantiated for the series and the exact activation
+      auto main_pass = [&](auto series_tag) {
+        constexpr bool SER = decltype(series_tag)::value;
+        constexpr int NIT = 2 * KACT;
+        const int sx_cur = (FQ && (j & 1)) ? G::OFF_SXL : G::OFF_SX;  // this tile's dS^T area
+        const int q_cur = (FQ && (j & 1)) ? G::OFF_QN1 : G::OFF_QN;    // this tile's Q / dO buffer
+        const int do_cur = (FQ && (j & 1)) ? G::OFF_DON1 : G::OFF_DON;
+        f32x16 sacc[2], dpacc[2];
+        bf16x8 qa[G::KK], da[G::KK];
+        bf16x8 dota[G::DT][2], qta[G::DT][2];
+        float lrow[16], drow[16];
+        auto load_a = [&](int qs) {
+  #pragma unroll
+          for (int kk = 0; kk < G::KK; ++kk) {
+            qa[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + q_cur + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
+            da[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + do_cur + (qs * 32 + lc) * G::NROW + g * D + kk * 16));
           }
-        } else {
-          if (kb == 0) load_a(qs);
-          issue_sdp(kb, 0);
-        }
-        const int rf = r0 + qs * 32;
-        if (kb == 0) {
-          if constexpr (softmax) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const int rr = qs * 32 + a * 8 + g * 4;
-              const f32x4 lv = *reinterpret_cast<const f32x4*>(lse2 + rr);
-              f32x4 dsum = *reinterpret_cast<const f32x4*>(dpart + rr);
-              if constexpr (!DSUM)
-#pragma unroll
-                for (int ww = 1; ww < G::NW; ++ww) dsum += *reinterpret_cast<const f32x4*>(dpart + ww * G::QT + rr);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                lrow[4 * a + e] = lv[e];
-                drow[4 * a + e] = dsum[e];
-              }
-            }
-          }
-        }
-        const int s = kb * G::NW + w;
-        const int kf = kofs + blk[kb] * kBwdKeyBlock;  // sequence position of the block
-        const int key = kf + lc;                       // this lane's key (sequence position)
-        const int spos = (s * kBwdKeyBlock + lc) * G::SXROW;
-        // P and dS as bf16 B operands (k-tile t = registers 8t..8t+7); zero for a block outside
-        // the tile. The softmax form (and a few-term element-wise item) also carries the rounding
-        // remainder as a second bf16 term (x ~ hi + lo): its products mix a few large terms, whose
-        // bf16 rounding alone would exceed the tolerance.
-        u32x4 pu[2], du[2], plu[2], dlu[2];
-        auto elementwise = [&]() {
-          // register r is query row rf + c_row(r, g), key `key`
-          float p[16], ds[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if constexpr (softmax) {
-              float x;
-              if constexpr (has_gate) x = __builtin_fmaf(sacc[cs][r], sc, st.gate[kb]);
-              else x = sacc[cs][r] * sc;
-              p[r] = fast_exp2(x - lrow[r]);
-              ds[r] = p[r] * (dpacc[cs][r] - drow[r]);
-            } else {
-              float dphi;
-              if constexpr (has_gate) {
-                PointAct<ACT>::value_grad(__builtin_fmaf(sacc[cs][r], sc, st.gate[kb]), 1.0f, c1, c3, p[r], dphi);
-              } else {
-                PointAct<ACT>::value_grad(sacc[cs][r], sc, c1, c3, p[r], dphi);
-              }
-              ds[r] = dpacc[cs][r] * dphi;
-            }
-          }
-          if constexpr (MASKED) {
-            if (!block_mask(kf, rf, kofs + n, L, wl, wr).full) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int row = rf + c_row(r, g);
-                const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
-                p[r] = ok ? p[r] : 0.0f;
-                ds[r] = ok ? ds[r] : 0.0f;
-              }
-            }
-          }
-          if constexpr (GATED) if (want_dg) {
-            float dsum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dsum += ds[r];
-            st.dgs[kb] += dsum;
-          }
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pu[t][e] = pack_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
-              du[t][e] = pack_bf16x2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1]);
-              if (split || chunk_rows_split) {
-                plu[t][e] = pack_bf16x2(p[8 * t + 2 * e] - bf16_lo(pu[t][e]), p[8 * t + 2 * e + 1] - bf16_hi(pu[t][e]));
-                dlu[t][e] = pack_bf16x2(ds[8 * t + 2 * e] - bf16_lo(du[t][e]), ds[8 * t + 2 * e + 1] - bf16_hi(du[t][e]));
-              }
-            }
         };
-        if constexpr (MASKED) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) pu[t] = du[t] = plu[t] = dlu[t] = u32x4{0u, 0u, 0u, 0u};
-          if (act[kb] && !block_mask(kf, rf, kofs + n, L, wl, wr).empty) elementwise();
-        } else {
-          // no mask: keys and rows past the ends meet zero operands, and phi(0) = 0
-          elementwise();
+        auto issue_sdp = [&](int kb, int slot) {
+          sacc[slot] = f32x16{};
+          dpacc[slot] = f32x16{};
+  #pragma unroll
+          for (int kk = 0; kk < G::KK; ++kk) {
+            sacc[slot] = mfma32(qa[kk], st.kreg[kb][kk], sacc[slot]);
+            dpacc[slot] = mfma32(da[kk], st.vreg[kb][kk], dpacc[slot]);
+          }
+        };
+        // the products of iteration it+1 are issued before the element-wise work of it (the dO^T / Q^T
+        // operands of dV / dK are read only after it, which keeps their registers free meanwhile).
+        // Key-chunk passes, whose fp32 dQ rows already hold registers, run without it (measured
+        // faster there: shared seed queries 540 -> 523 us), and so does the softmax form with 8
+        // waves (no registers to spare).
+        // (ungated element-wise forms: only the series tiles keep it; the exact tiles of such items
+      // would otherwise need more registers than the wave has)
+      constexpr bool PIPE = CHUNK == 0 && !(split && NW == 8) && (!kSeries || SER);
+        if constexpr (PIPE) {
+          load_a(0);
+          issue_sdp(0, 0);
         }
-        // dS^T to the exchange tile: registers 4a..4a+3 are 4 consecutive query rows
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int qo = (qs * 32 + a * 8 + g * 4) * 2;
-          const int t = a >> 1, hlf = (a & 1) * 2;
-          *reinterpret_cast<u32x2*>(lds + sx_cur + spos + qo) = u32x2{du[t][hlf], du[t][hlf + 1]};
-          if constexpr (split_dq)
-            *reinterpret_cast<u32x2*>(lds + G::OFF_SXL + spos + qo) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
-        }
-        if (kb == 0) {
-#pragma unroll
-          for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              dota[dt][t] = tr_operand<G::NROW>(lds, do_cur, qs, t, dt);
-              qta[dt][t] = tr_operand<G::NROW>(lds, q_cur, qs, t, dt);
+  #pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int qs = it / KACT, kb = it % KACT, cs = PIPE ? (it & 1) : 0;
+          if constexpr (PIPE) {
+            if (it + 1 < NIT) {
+              if ((it + 1) / KACT != qs) load_a((it + 1) / KACT);
+              issue_sdp((it + 1) % KACT, cs ^ 1);
             }
-        }
-#pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(pu[t]), st.dv[kb][dt]);
-            st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(du[t]), st.dk[kb][dt]);
-            if (split || chunk_rows_split) {
-              st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(plu[t]), st.dv[kb][dt]);
-              st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(dlu[t]), st.dk[kb][dt]);
+          } else {
+            if (kb == 0) load_a(qs);
+            issue_sdp(kb, 0);
+          }
+          const int rf = r0 + qs * 32;
+          if (kb == 0) {
+            if constexpr (softmax) {
+  #pragma unroll
+              for (int a = 0; a < 4; ++a) {
+                const int rr = qs * 32 + a * 8 + g * 4;
+                const f32x4 lv = *reinterpret_cast<const f32x4*>(lse2 + rr);
+                f32x4 dsum = *reinterpret_cast<const f32x4*>(dpart + rr);
+                if constexpr (!DSUM)
+  #pragma unroll
+                  for (int ww = 1; ww < G::NW; ++ww) dsum += *reinterpret_cast<const f32x4*>(dpart + ww * G::QT + rr);
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  lrow[4 * a + e] = lv[e];
+                  drow[4 * a + e] = dsum[e];
+                }
+              }
             }
           }
+          const int s = kb * G::NW + w;
+          const int kf = kofs + blk[kb] * kBwdKeyBlock;  // sequence position of the block
+          const int key = kf + lc;                       // this lane's key (sequence position)
+          const int spos = (s * kBwdKeyBlock + lc) * G::SXROW;
+          // P and dS as bf16 B operands (k-tile t = registers 8t..8t+7); zero for a block outside
+          // the tile. The softmax form (and a few-term element-wise item) also carries the rounding
+          // remainder as a second bf16 term (x ~ hi + lo): its products mix a few large terms, whose
+          // bf16 rounding alone would exceed the tolerance.
+          u32x4 pu[2], du[2], plu[2], dlu[2];
+          auto elementwise = [&]() {
+            // register r is query row rf + c_row(r, g), key `key`
+            float p[16], ds[16];
+            if (kSeries && series) {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                float dphi;
+                SeriesAct<ACT>::value_grad(sacc[cs][r], a1, a3, d1, d3, p[r], dphi);
+                ds[r] = dpacc[cs][r] * dphi;
+              }
+            } else {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                if constexpr (softmax) {
+                  float x;
+                  if constexpr (has_gate) x = __builtin_fmaf(sacc[cs][r], sc, st.gate[kb]);
+                  else x = sacc[cs][r] * sc;
+                  p[r] = fast_exp2(x - lrow[r]);
+                  ds[r] = p[r] * (dpacc[cs][r] - drow[r]);
+                } else {
+                  float dphi;
+                  if constexpr (has_gate) {
+                    PointAct<ACT>::value_grad(__builtin_fmaf(sacc[cs][r], sc, st.gate[kb]), 1.0f, c1, c3, p[r], dphi);
+                  } else {
+                    PointAct<ACT>::value_grad(sacc[cs][r], sc, c1, c3, p[r], dphi);
+                  }
+                  ds[r] = dpacc[cs][r] * dphi;
+                }
+              }
+            }
+            if constexpr (MASKED) {
+              if (!block_mask(kf, rf, kofs + n, L, wl, wr).full) {
+  #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int row = rf + c_row(r, g);
+                  const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+                  p[r] = ok ? p[r] : 0.0f;
+                  ds[r] = ok ? ds[r] : 0.0f;
+                }
+              }
+            }
+            if constexpr (GATED) if (want_dg) {
+              float dsum = 0.0f;
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) dsum += ds[r];
+              st.dgs[kb] += dsum;
+            }
+  #pragma unroll
+            for (int t = 0; t < 2; ++t)
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                pu[t][e] = pack_bf16x2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
+                du[t][e] = pack_bf16x2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1]);
+                if (split || chunk_rows_split) {
+                  plu[t][e] = pack_bf16x2(p[8 * t + 2 * e] - bf16_lo(pu[t][e]), p[8 * t + 2 * e + 1] - bf16_hi(pu[t][e]));
+                  dlu[t][e] = pack_bf16x2(ds[8 * t + 2 * e] - bf16_lo(du[t][e]), ds[8 * t + 2 * e + 1] - bf16_hi(du[t][e]));
+                }
+              }
+          };
+          if constexpr (MASKED) {
+  #pragma unroll
+            for (int t = 0; t < 2; ++t) pu[t] = du[t] = plu[t] = dlu[t] = u32x4{0u, 0u, 0u, 0u};
+            if (act[kb] && !block_mask(kf, rf, kofs + n, L, wl, wr).empty) elementwise();
+          } else {
+            // no mask: keys and rows past the ends meet zero operands, and phi(0) = 0
+            elementwise();
+          }
+          // dS^T to the exchange tile: registers 4a..4a+3 are 4 consecutive query rows
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int qo = (qs * 32 + a * 8 + g * 4) * 2;
+            const int t = a >> 1, hlf = (a & 1) * 2;
+            *reinterpret_cast<u32x2*>(lds + sx_cur + spos + qo) = u32x2{du[t][hlf], du[t][hlf + 1]};
+            if constexpr (split_dq)
+              *reinterpret_cast<u32x2*>(lds + G::OFF_SXL + spos + qo) = u32x2{dlu[t][hlf], dlu[t][hlf + 1]};
+          }
+          if (kb == 0) {
+  #pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt)
+  #pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                dota[dt][t] = tr_operand<G::NROW>(lds, do_cur, qs, t, dt);
+                qta[dt][t] = tr_operand<G::NROW>(lds, q_cur, qs, t, dt);
+              }
+          }
+  #pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt)
+  #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(pu[t]), st.dv[kb][dt]);
+              st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(du[t]), st.dk[kb][dt]);
+              if (split || chunk_rows_split) {
+                st.dv[kb][dt] = mfma32(dota[dt][t], as_bf16x8(plu[t]), st.dv[kb][dt]);
+                st.dk[kb][dt] = mfma32(qta[dt][t], as_bf16x8(dlu[t]), st.dk[kb][dt]);
+              }
+            }
+        }
+      };
+      if constexpr (kSeries) {
+        if (series) main_pass(std::true_type{});
+        else main_pass(std::false_type{});
+      } else {
+        main_pass(std::false_type{});
       }
     }
     if constexpr (FQ) {
       // one barrier per tile: the next tile goes into the other Q / dO buffer (last read by the
       // previous tile's main pass) before the barrier, then the previous tile's dQ
       if (j + 1 < t1) {
-        store_qtile<D, NW, softmax, DSUM>(lds, pf, (j + 1) & 1);
+        store_qtile<D, NW, softmax, DSUM, kSeries>(lds, pf, (j + 1) & 1);
         if (j + 2 < t1)
           prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
       }
@@ -802,7 +866,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     if (j + 1 < t1) {
       // next tile into LDS (while dQ runs), then the loads of the one after it: issued before this
       // tile's dQ stores, so waiting for them never waits for those stores
-      store_qtile<D, NW, softmax, DSUM>(lds, pf);
+      store_qtile<D, NW, softmax, DSUM, kSeries>(lds, pf);
       if (j + 2 < t1)
         prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, r0 + 2 * G::QT, L, it.dsumseq);
       if constexpr (WINDOWED) {
@@ -1154,6 +1218,13 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
     graw = gseq[(size_t)lc * H];
     gate = log_sigmoid_f(graw);
   }
+  // ungated: the keys' largest ||k||^2, for the series bound of each 32-row step
+  float kn2 = 0.0f;
+  if constexpr (!GATED) {
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) kn2 += sumsq_bf16x8(__builtin_bit_cast(u32x4, kreg[kk]));
+    kn2 = wave_max(kn2 + __shfl_xor(kn2, 32, 64));
+  }
   f32x16 dk[G::DT], dv[G::DT];
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) dk[dt] = dv[dt] = f32x16{};
@@ -1162,6 +1233,8 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
   float c1 = 0.0f, c3 = 0.0f;
   PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
   const float dv_scale = GATED ? 1.0f : gd.scale;
+  float a1 = 0.0f, a3 = 0.0f, d1 = 0.0f, d3 = 0.0f;
+  if constexpr (!GATED) SeriesAct<ACT>::coeffs(gd.scale, a1, a3, d1, d3);
   // few rows: dK, dV sums of at most kSplitTerms products; few keys: dQ sums likewise. Their P / dS
   // operands then carry the rounding remainder as a second bf16 term (uniform per item).
   const bool split_rows = L <= kSplitTerms || gd.split_all, split_keys = n <= kSplitTerms || gd.split_all;
@@ -1192,12 +1265,29 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
     // register r of lane (key lc, g) is row r0 + c_row(r, g); keys and rows past the ends meet
     // zero operands (phi(0) = 0, and their dO / Q rows are zero), so no mask is needed
     float p[16], ds[16];
+    bool series = false;
+    if constexpr (!GATED) {
+      // the step's rows: this lane holds half of row lc, the other half sits 32 lanes away
+      float qn2 = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float dphi;
-      if constexpr (GATED) PointAct<ACT>::value_grad(__builtin_fmaf(sacc[r], sc, gate), 1.0f, c1, c3, p[r], dphi);
-      else PointAct<ACT>::value_grad(sacc[r], sc, c1, c3, p[r], dphi);
-      ds[r] = dpacc[r] * dphi;
+      for (int kk = 0; kk < G::KK; ++kk) qn2 += sumsq_bf16x8(__builtin_bit_cast(u32x4, qa[kk]));
+      series = seq_series_ok(gd.scale, wave_max(qn2 + __shfl_xor(qn2, 32, 64)), kn2);
+    }
+    if (!GATED && series) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float dphi;
+        SeriesAct<ACT>::value_grad(sacc[r], a1, a3, d1, d3, p[r], dphi);
+        ds[r] = dpacc[r] * dphi;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float dphi;
+        if constexpr (GATED) PointAct<ACT>::value_grad(__builtin_fmaf(sacc[r], sc, gate), 1.0f, c1, c3, p[r], dphi);
+        else PointAct<ACT>::value_grad(sacc[r], sc, c1, c3, p[r], dphi);
+        ds[r] = dpacc[r] * dphi;
+      }
     }
     if constexpr (GATED) {
 #pragma unroll

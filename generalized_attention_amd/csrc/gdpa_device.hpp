@@ -266,6 +266,76 @@ struct PointAct {
   }
 };
 
+// Small-argument series of the same activations, exact forms (no logistic approximation): for
+// |x| <= kSeriesBound
+//   phi(x)  = x (1/2 + x (A + B x^2))      SiLU: Taylor series of x sigmoid(x) (A = 1/4, B = -1/48)
+//   phi'(x) = 1/2 + x (C + D x^2)          GELU: Taylor series of x Phi(x), Phi the normal CDF
+//                                                (A = phi0, B = -phi0/6, C = 2 phi0, D = -2 phi0/3,
+//                                                phi0 = 1/sqrt(2 pi))
+// The first omitted terms (x^6 / 480 and x^5 / 80 for SiLU, phi0 x^6 / 40 and 3 phi0 x^5 / 20 for
+// GELU) leave relative errors of at most 5e-6 (SiLU), 3e-5 (SiLU'), 2.5e-5 (GELU) and 1.9e-4
+// (GELU', at x = -1/4) over |x| <= 1/4: a tenth of the bf16 rounding of P and dS (2^-9) or less,
+// and of the order of the exact path's own GELU approximation (1.5e-4 in Phi). The kernels take this path for a tile only where a bound proves every argument of the
+// tile within the range (seq_series_ok); other tiles use PointAct. Four and two plain
+// multiply-adds replace the two transcendentals (a quarter-rate exp2 and reciprocal) and the
+// arithmetic around them.
+constexpr float kSeriesBound = 0.25f;
+template <int ACT>
+struct SeriesAct {
+  static constexpr float kPhi0 = 0.3989422804014327f;
+  static constexpr float A = ACT == GDPA_ACT_GELU ? kPhi0 : 0.25f;
+  static constexpr float B = ACT == GDPA_ACT_GELU ? -kPhi0 / 6.0f : -1.0f / 48.0f;
+  static constexpr float C = ACT == GDPA_ACT_GELU ? 2.0f * kPhi0 : 0.5f;
+  static constexpr float D = ACT == GDPA_ACT_GELU ? -2.0f * kPhi0 / 3.0f : -1.0f / 12.0f;
+  // coefficients for a raw score s with argument x = scale s, in the convention of PointAct for
+  // ungated scores: value p' = phi(x) / scale = s (1/2 + s (a1 + a3 s^2)); derivative
+  // phi'(x) = 1/2 + s (d1 + d3 s^2)
+  __host__ __device__ static inline void coeffs(float scale, float& a1, float& a3, float& d1, float& d3) {
+    const float s3 = scale * scale * scale;
+    a1 = A * scale;
+    a3 = B * s3;
+    d1 = C * scale;
+    d3 = D * s3;
+  }
+  __host__ __device__ static inline float value(float s, float a1, float a3) {
+    const float w = s * s;
+    const float c = __builtin_fmaf(s, __builtin_fmaf(w, a3, a1), 0.5f);
+    return s * c;
+  }
+  __host__ __device__ static inline void value_grad(float s, float a1, float a3, float d1, float d3, float& p,
+                                                    float& dphi) {
+    const float w = s * s;
+    p = s * __builtin_fmaf(s, __builtin_fmaf(w, a3, a1), 0.5f);
+    dphi = __builtin_fmaf(s, __builtin_fmaf(w, d3, d1), 0.5f);
+  }
+};
+
+// Every argument x = scale <q, k> of a tile lies in the series range when
+// scale^2 max ||q||^2 max ||k||^2 <= kSeriesBound^2 (Cauchy-Schwarz), with a margin for the fp32
+// accumulation of the scores and of the squared norms. False for NaN or infinite norms.
+__host__ __device__ inline bool seq_series_ok(float scale, float qn2, float kn2) {
+  return scale * scale * qn2 * kn2 <= kSeriesBound * kSeriesBound * 0.998f;
+}
+
+// Sum of squares of the 8 bf16 values of a 16-byte chunk (each product is exact in fp32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline float sumsq_bf16x8(const u32x4& u) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2_t v = __builtin_bit_cast(bf16x2_t, u[e]);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+  }
+  return acc;
+}
+
+// Maximum over the lanes of a wave (lanes whose value is not needed must hold something <= it).
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
 // log sigmoid(g) in fp32, overflow-free: min(g, 0) - log1p(exp(-|g|)).
 __device__ inline float log_sigmoid_f(float g) {
   return fminf(g, 0.0f) - log1pf(__expf(-fabsf(g)));

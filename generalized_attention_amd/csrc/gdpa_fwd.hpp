@@ -57,7 +57,8 @@ struct FwdGeo {
   static constexpr int DT = D / 32;            // 32-wide d tiles of the output
   static constexpr int OFF_V = NKV * KROW;
   static constexpr int OFF_G = OFF_V + D * VROW;
-  static constexpr int BYTES = OFF_G + NKV * 4;
+  static constexpr int OFF_KN = OFF_G + NKV * 4;  // per-wave maxima of the staged keys' ||k||^2
+  static constexpr int BYTES = OFF_KN + 16 * 4;
 };
 
 constexpr int fwd_max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
@@ -78,7 +79,8 @@ __device__ inline int vt_pos(int kl) { return (kl & ~15) + slot_row(kl & 15); }
 // write.
 // The keys land at LDS key positions dst + (0 .. span_pad-1) (dst a multiple of 32).
 // SERIAL: keep the rounds in order (the caller holds accumulators in registers across the staging).
-template <int D, int NKV, int NT, bool SERIAL = false>
+// KNORM: each wave also writes the largest ||k||^2 of the keys it staged to G::OFF_KN + 4 w.
+template <int D, int NKV, int NT, bool SERIAL = false, bool KNORM = false>
 __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float* gb, int hstride,
                          int span, int span_pad, bool softmax, int dst = 0) {
   using G = FwdGeo<D, NKV>;
@@ -97,6 +99,7 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
     gv[i] = 0.0f;
     if (gb != nullptr && r < span) gv[i] = gb[(size_t)r * hstride];
   }
+  float kn2 = 0.0f;  // KNORM: largest ||k||^2 among this lane's rows
   auto stage_round = [&](int round) {
     constexpr int KR = KI / ROUNDS, VR = (VI + ROUNDS - 1) / ROUNDS;
     u32x4 kbuf[KR], vbuf[VR][4];
@@ -106,6 +109,16 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
       const int r = idx / CPR, c = idx % CPR;
       kbuf[i] = u32x4{0u, 0u, 0u, 0u};
       if (idx < span_pad * CPR && r < span) kbuf[i] = *reinterpret_cast<const u32x4*>(kb + r * rs + c * 8);
+    }
+    if constexpr (KNORM) {
+      // a row's CPR chunks sit in CPR consecutive lanes: their partial sums meet by lane shuffles
+#pragma unroll
+      for (int i = 0; i < KR; ++i) {
+        float n2 = sumsq_bf16x8(kbuf[i]);
+#pragma unroll
+        for (int off = 1; off < CPR; off <<= 1) n2 += __shfl_xor(n2, off, 64);
+        kn2 = fmaxf(kn2, n2);
+      }
     }
 #pragma unroll
     for (int i = 0; i < VR; ++i) {
@@ -150,6 +163,10 @@ __device__ void stage_kv(char* lds, const bf16* kb, const bf16* vb, const float*
 #pragma unroll
     for (int round = 0; round < ROUNDS; ++round) stage_round(round);
   }
+  if constexpr (KNORM) {
+    kn2 = wave_max(kn2);
+    if (lane_id() == 0) reinterpret_cast<float*>(lds + G::OFF_KN)[threadIdx.x >> 6] = kn2;
+  }
   float* gl = reinterpret_cast<float*>(lds + G::OFF_G) + dst;
 #pragma unroll
   for (int i = 0; i < GI; ++i) {
@@ -186,6 +203,21 @@ __device__ inline void load_q(QFrags<D, QS>& q, const bf16* qseq, size_t rs, int
       q.f[qs][kk] = as_bf16x8(u);
     }
   }
+}
+
+// Largest ||q||^2 over the wave tile's rows (rows past the end are zero); uniform across the wave.
+template <int D, int QS>
+__device__ inline float q_norm_max(const QFrags<D, QS>& q) {
+  float m = 0.0f;
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    float n2 = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) n2 += sumsq_bf16x8(__builtin_bit_cast(u32x4, q.f[qs][kk]));
+    n2 += __shfl_xor(n2, 32, 64);  // the two halves of the row
+    m = fmaxf(m, n2);
+  }
+  return wave_max(m);
 }
 
 // S^T block kb (32 keys x QS*32 rows) = K_kb Q^T on MFMA, K rows from LDS.
@@ -229,8 +261,10 @@ __device__ __forceinline__ void acc_init(FwdAcc<D, QS>& a) {
 // a window); without it, keys past the end meet zero K and V rows in LDS and phi(0) = 0.
 // PSPLIT: at most kSplitTerms keys, so each output is a sum of that few products; P then enters
 // O^T = V^T P^T as a high + low bf16 pair (its single rounding would be too coarse there).
+// SERIES: ungated element-wise tile whose arguments are all proven within the series range
+// (SeriesAct instead of PointAct).
 template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool RING = false, bool PIPE = true,
-          bool PSPLIT = false>
+          bool PSPLIT = false, bool SERIES = false>
 __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf,
                                                FwdAcc<D, QS>& acc, int row0, int kbase, int kend, int kb0,
                                                int kb1) {
@@ -246,8 +280,10 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
   constexpr int smask = RING ? G::NKV / 32 - 1 : -1;  // block -> LDS slot
   // element-wise forms: without a gate p' = s g(scale s) = phi(scale s) / scale and O is scaled
   // once in the epilogue; with a gate the argument scale s + log sigmoid(G) is formed first.
-  float c1 = 0.0f, c3 = 0.0f;
-  if constexpr (!softmax) PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
+  float c1 = 0.0f, c3 = 0.0f, a1 = 0.0f, a3 = 0.0f, d1 = 0.0f, d3 = 0.0f;
+  static_assert(!SERIES || (!GATED && !softmax), "series only for ungated element-wise tiles");
+  if constexpr (SERIES) SeriesAct<ACT>::coeffs(gd.scale, a1, a3, d1, d3);
+  else if constexpr (!softmax) PointAct<ACT>::coeffs(GATED ? 1.0f : gd.scale, c1, c3);
 
   // Element-wise stage and P V for block kb whose scores are in s: register r of lane (qc, g) is
   // key kbase + kb*32 + c_row(r, g), row qs*32 + qc.
@@ -261,6 +297,7 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
         float x;
         if constexpr (GATED) x = __builtin_fmaf(s[qs][r], sc, gl[slot * 32 + c_row(r, g)]);
         if constexpr (softmax) p[qs][r] = GATED ? x : s[qs][r] * sc;
+        else if constexpr (SERIES) p[qs][r] = SeriesAct<ACT>::value(s[qs][r], a1, a3);
         else p[qs][r] = GATED ? PointAct<ACT>::value(x, c1, c3) : PointAct<ACT>::value(s[qs][r], c1, c3);
       }
     if constexpr (MASKED) {
@@ -401,13 +438,14 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
 }
 
 // One wave tile against staged key blocks [kb0, kb1), then its epilogue.
-template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool PIPE, bool PSPLIT = false>
+template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool PIPE, bool PSPLIT = false,
+          bool SERIES = false>
 __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, OutPtr oseq,
                                          float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   FwdAcc<D, QS> acc;
   acc_init(acc);
-  fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, false, PIPE, PSPLIT>(lds, gd, qf, acc, row0, klo, klo + span, kb0,
-                                                                      kb1);
+  fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, false, PIPE, PSPLIT, SERIES>(lds, gd, qf, acc, row0, klo, klo + span,
+                                                                              kb0, kb1);
   fwd_finish<D, NKV, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
 }
 
@@ -447,10 +485,16 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
     // d <= 64: the first Q tile is in flight during the staging and each next tile's Q during
     // the current tile (d = 128: the registers do not allow it; Q is loaded per tile)
     constexpr bool kPrefetchQ = D < 128 && NW == 4;  // (with 8 waves the other waves hide the load)
+    // ungated element-wise items: tiles proven within the series range take SeriesAct
+    constexpr bool kSeriesItem = !softmax && !GATED;
     QFrags<D, QS> qcur, qnext;
     if (kPrefetchQ && w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
-    stage_kv<D, NKV, NW * kWave>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
+    stage_kv<D, NKV, NW * kWave, false, kSeriesItem>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
     __syncthreads();
+    float kn2 = 0.0f;  // largest ||k||^2 of the item's keys
+    if constexpr (kSeriesItem)
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) kn2 = fmaxf(kn2, reinterpret_cast<const float*>(lds + G::OFF_KN)[ww]);
     for (int row0 = w * RW; row0 < L; row0 += NW * RW) {
       // next tile's Q is loaded while this tile computes
       if (!kPrefetchQ) load_q<D, QS>(qcur, qseq, rs, row0, L);
@@ -460,8 +504,13 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
       // (8 waves: four per SIMD, no software pipeline inside a wave; 4 waves: two per SIMD, with it)
+      bool series = false;
+      if constexpr (kSeriesItem) series = seq_series_ok(gd.scale, q_norm_max<D, QS>(qcur), kn2);
       if (N <= kSplitTerms)
         fwd_tile<D, NKV, ACT, QS, GATED, MASKED, false, true>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
+      else if (kSeriesItem && series)
+        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, NW == 4, false, kSeriesItem>(lds, gd, qcur, oseq, lseq, L, row0, 0,
+                                                                               N, kb0, kb1);
       else
         fwd_tile<D, NKV, ACT, QS, GATED, MASKED, NW == 4>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       if (kPrefetchQ) qcur = qnext;

@@ -307,6 +307,57 @@ def test_split_operands_flag(name, kw):
 
 
 # ------------------------------------------------------------------------------------------------
+# The small-argument series of the element-wise activations (tiles proven within |x| <= 1/4)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_series_and_exact_tiles_in_one_launch(act):
+    """At scale 1/1000 the PFFN rows and keys are proven within the series range tile by tile;
+    the keys of sequence 1 and the rows of sequence 5 are multiplied by 2.5, which lifts the bound
+    of their tiles to 0.23-0.27: some of them take the exact path, the rest the series (some just
+    under the bound), in the same launches. (Larger factors make those sequences' outputs dominate
+    the tensors' RMS, and the single bf16 rounding of P / dS alone then exceeds 2e-2 of it.)"""
+    w = make_workload("pffn_train", 31, num_seqs=8, len_range=(1, 400), act=act)
+    g = w.groups[0]
+    qo, ko = g.q_offsets, g.kv_offsets
+    q, k = g.q.clone(), g.k.clone()
+    q[qo[5]:qo[6]] *= 2.5
+    k[ko[1]:ko[2]] *= 2.5
+    g.q, g.k = q, k
+    compare_workload(w, ("fwd", "bwd"))
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_series_near_its_bound(act):
+    """Rows and keys along one common direction (plus small noise), with the scale chosen so that
+    scale * max||q|| * max||k|| = 0.245: the bound holds for every tile while the arguments spread
+    over most of [-1/4, 1/4], where the series' truncation is largest. Split operands and float32
+    outputs take the bf16 rounding of P / dS and of the results out of the gradients (on such
+    aligned inputs that rounding alone reaches 0.024-0.028 of RMS in dK), so what remains is the
+    series' own error: a CPU emulation of these formulas puts it at 1e-5 to 5e-4 of RMS, and the
+    gradients are held to 5e-3, ten times that (a wrong series coefficient exceeds it)."""
+    import dataclasses
+    w = make_workload("pffn_train", 37, lengths=[40, 300, 129, 1, 64, 257], act=act, ctx_dim=64)
+    g = w.groups[0]
+    rng = np.random.default_rng(37)
+    h, d = g.q.shape[1], g.q.shape[2]
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+
+    def along(rows):
+        a = rng.uniform(-1.0, 1.0, size=(rows, h, 1)) * 16.0
+        return torch.from_numpy(a * u + 0.05 * rng.standard_normal((rows, h, d))).to(torch.bfloat16)
+
+    g.q, g.k = along(g.total_q), along(g.total_kv)
+    qn = g.q.double().norm(dim=-1).max().item()
+    kn = g.k.double().norm(dim=-1).max().item()
+    g.spec = dataclasses.replace(g.spec, scale=0.245 / (qn * kn))
+    report = compare_workload(w, ("fwd", "bwd"), fp32_out=True, split_operands=True)
+    for name in ("g0.dq", "g0.dk", "g0.dv"):
+        assert report[name] <= 5e-3, (name, report[name])
+
+
+# ------------------------------------------------------------------------------------------------
 # Properties of the HIP path itself
 # ------------------------------------------------------------------------------------------------
 

@@ -1,0 +1,85 @@
+"""The small-argument series of the element-wise activations (SeriesAct in gdpa_device.hpp, the
+form the kernels take for tiles proven within |x| <= 1/4) against the exact functions, on the CPU:
+the header is compiled into a small host program that tabulates the series, and the test compares
+it with x sigmoid(x), x Phi(x) and their derivatives in float64 (Phi from math.erf)."""
+
+import math
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "generalized_attention_amd", "csrc")
+
+PROGRAM = r'''
+#include <cstdio>
+#include "gdpa_device.hpp"
+using namespace gdpa;
+template <int ACT> void table(float scale) {
+  float a1, a3, d1, d3;
+  SeriesAct<ACT>::coeffs(scale, a1, a3, d1, d3);
+  for (int i = -1000; i <= 1000; ++i) {
+    const float x = 0.25f * i / 1000.0f;   // the argument
+    const float s = x / scale;              // the raw score it comes from
+    float p, dphi;
+    SeriesAct<ACT>::value_grad(s, a1, a3, d1, d3, p, dphi);
+    const float pv = SeriesAct<ACT>::value(s, a1, a3);
+    printf("%d %.9g %.9g %.9g %.9g %.9g\n", ACT, scale, x, p * scale, pv * scale, dphi);
+  }
+}
+int main() {
+  for (float scale : {1.0f, 0.125f, 0.001f}) { table<GDPA_ACT_GELU>(scale); table<GDPA_ACT_SILU>(scale); }
+  // the bound: scale^2 qn2 kn2 <= (1/4)^2 with a margin
+  printf("B %d %d %d %d\n", (int)seq_series_ok(0.001f, 100.0f, 600.0f), (int)seq_series_ok(0.001f, 250.0f, 250.0f),
+         (int)seq_series_ok(0.001f, 251.0f, 250.0f), (int)seq_series_ok(0.001f, 1.0f / 0.0f, 1.0f));
+  return 0;
+}
+'''
+
+
+@pytest.fixture(scope="module")
+def table():
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "series.hip")
+        exe = os.path.join(tmp, "series")
+        open(src, "w").write(PROGRAM)
+        subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "--offload-arch=gfx950", "-I", CSRC, "-I",
+                        os.path.join(ROOT, "include"), src, "-o", exe], check=True, capture_output=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    rows = [l.split() for l in out if l and not l.startswith("B")]
+    bound = [l for l in out if l.startswith("B")][0].split()[1:]
+    return np.array(rows, dtype=np.float64), [int(b) for b in bound]
+
+
+def exact(act, x):
+    if act == 0:  # GELU, exact erf form
+        Phi = 0.5 * (1.0 + np.vectorize(math.erf)(x / math.sqrt(2.0)))
+        return x * Phi, Phi + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    sig = 1.0 / (1.0 + np.exp(-x))  # SiLU
+    return x * sig, sig * (1.0 + x * (1.0 - sig))
+
+
+def test_series_matches_activations(table):
+    tab, _ = table
+    for act in (0, 1):
+        for scale in (1.0, 0.125, 0.001):
+            rows = tab[(tab[:, 0] == act) & (np.isclose(tab[:, 1], scale))]
+            x = rows[:, 2]
+            p_ref, g_ref = exact(act, x)
+            # relative errors as the header states them (GELU', the largest, at x = -1/4), plus fp32
+            # rounding of the evaluation and of the scale round trip
+            tol_p, tol_g = (3e-5, 2e-4) if act == 0 else (6e-6, 4e-5)
+            assert np.all(np.abs(rows[:, 3] - p_ref) <= tol_p * np.abs(p_ref) + 1e-7), (act, scale)
+            assert np.array_equal(rows[:, 3], rows[:, 4])  # value() agrees with value_grad()
+            assert np.all(np.abs(rows[:, 5] - g_ref) <= tol_g * np.abs(g_ref)), (act, scale)
+            # a planted wrong coefficient would be seen: the cubic term of SiLU' alone is 1.3e-3 at 1/4
+            assert tol_g * 0.305 < 1.3e-3 / 2
+
+
+def test_series_bound(table):
+    _, b = table
+    # 1e-6 * 100 * 600 = 0.06 <= 1/16; 1e-6 * 250 * 250 = 1/16 itself is refused (margin); above: no; inf: no
+    assert b == [1, 0, 0, 0]
