@@ -17,10 +17,12 @@ HEADER = os.path.join(ROOT, "include", "gdpa.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_lib.LIB_PATH):
+    # GDPA_TEST_LIB: another build of the library to check (the sanitizer test's host-only build)
+    path = os.environ.get("GDPA_TEST_LIB", _lib.LIB_PATH)
+    if path == _lib.LIB_PATH and not os.path.exists(path):
         from generalized_attention_amd import build
         build.build()
-    return _lib.load()
+    return _lib.load(path)
 
 
 def declared_functions():
