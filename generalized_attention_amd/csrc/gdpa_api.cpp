@@ -142,6 +142,13 @@ int bit_length(uint64_t x) {
   return n;
 }
 
+// The backward runs a group's items one wave each (bwd_small_kernel) when every sequence has at
+// most 32 keys and the form is element-wise, without a window or a shared query matrix.
+bool short_key_group(const gdpa_problem& p) {
+  return p.dtype == GDPA_DTYPE_BF16 && p.max_seqlen_kv <= 32 && p.act != GDPA_ACT_SOFTMAX && !p.head_acts &&
+         p.window_left < 0 && p.window_right < 0 && !shared_q(p);
+}
+
 void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, const WsLayout& L,
                LaunchDesc* d) {
   std::memset(d, 0, sizeof(*d));
@@ -167,6 +174,7 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
     gd.shared_q = shared_q(p) ? p.max_seqlen_q : 0;
     gd.out_f32 = p.dtype == GDPA_DTYPE_BF16 && (p.flags & GDPA_FLAG_FP32_OUT) ? 1 : 0;
     gd.split_all = (p.flags & GDPA_FLAG_SPLIT_OPERANDS) ? 1 : 0;
+    gd.short_keys = short_key_group(p) ? 1 : 0;
     gd.q_off = p.q_offsets;
     gd.kv_off = p.kv_offsets;
     gd.num_seqs = p.num_seqs;
@@ -194,12 +202,6 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
   }
   const int bl = bit_length(max_work);
   d->work_shift = bl > 10 ? bl - 10 : 0;
-}
-
-int dim_set_of(const gdpa_problem* ps, int n_groups) {
-  int s = 0;
-  for (int g = 0; g < n_groups; ++g) s |= ps[g].head_dim == 32 ? kDim32 : ps[g].head_dim == 64 ? kDim64 : kDim128;
-  return s;
 }
 
 // GDPA_DEBUG=1 in the environment, or GDPA_FLAG_VALIDATE in any problem: validate the offsets first.
@@ -245,27 +247,45 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
     e = (ps[0].flags & GDPA_FLAG_PLANNED) ? hipSuccess : launch_schedule(d, s);  // clears the error word
     if (e == hipSuccess && validate) e = launch_validate(d, s);
     if (e == hipSuccess) {
-      const int dims = dim_set_of(ps, n_groups);
-      int acts = 0;
-      for (int g = 0; g < n_groups; ++g)
-        acts |= ps[g].head_acts ? (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX)
-                                : 1 << ps[g].act;
       // forward mode 1: d <= 64 and every key range resident in LDS; 2: d <= 64, a longer key
-      // range and no window (windows keep the 4-wave ring); 0 otherwise. Backward with one wave
-      // per item: at most 32 keys, element-wise, no window
+      // range and no window (windows keep the 4-wave ring); 0 otherwise. The backward runs the
+      // short-key groups' items (the tail of the work list) one wave each in a launch of their
+      // own, and every other group's items in the kernel family their head dims and activations
+      // select.
       bool any_long = false, any_window = false, any_d128 = false;
-      bool small = true;
+      int dims = 0, acts = 0, dims_short = 0, acts_short = 0;
+      int64_t n_short = 0;
       for (int g = 0; g < n_groups; ++g) {
-        const int kv = ps[g].max_seqlen_kv;
-        any_long |= kv > fwd_kv_capacity(ps[g].head_dim);
-        any_window |= ps[g].window_left >= 0 || ps[g].window_right >= 0;
-        any_d128 |= ps[g].head_dim == 128;
-        small = small && kv <= 32 && ps[g].act != GDPA_ACT_SOFTMAX && !ps[g].head_acts &&
-                ps[g].window_left < 0 && ps[g].window_right < 0 && !shared_q(ps[g]);
+        const gdpa_problem& p = ps[g];
+        any_long |= p.max_seqlen_kv > fwd_kv_capacity(p.head_dim);
+        any_window |= p.window_left >= 0 || p.window_right >= 0;
+        any_d128 |= p.head_dim == 128;
+        const int ds = p.head_dim == 32 ? kDim32 : p.head_dim == 64 ? kDim64 : kDim128;
+        const int as = p.head_acts ? (1 << GDPA_ACT_GELU) | (1 << GDPA_ACT_SILU) | (1 << GDPA_ACT_SOFTMAX)
+                                   : 1 << p.act;
+        if (pass == 1 && short_key_group(p)) {
+          n_short += (int64_t)p.num_seqs * p.num_heads;
+          dims_short |= ds;
+          acts_short |= as;
+        } else {
+          dims |= ds;
+          acts |= as;
+        }
       }
-      const int key_mode = any_d128 ? 0 : !any_long ? 1 : any_window ? 0 : 2;
-      e = pass == 0 ? launch_fwd_bf16(d, dims, acts, key_mode, s)
-                    : launch_bwd_bf16(d, dims, acts, small, !any_window, s);
+      if (pass == 0) {
+        const int key_mode = any_d128 ? 0 : !any_long ? 1 : any_window ? 0 : 2;
+        e = launch_fwd_bf16(d, dims, acts, key_mode, s);
+      } else {
+        LaunchDesc main = d;
+        main.n_items = d.n_items - (int32_t)n_short;
+        e = launch_bwd_bf16(main, dims, acts, false, !any_window, s);
+        if (e == hipSuccess && n_short > 0) {
+          LaunchDesc tail = d;
+          tail.items = d.items + main.n_items;
+          tail.n_items = (int32_t)n_short;
+          e = launch_bwd_bf16(tail, dims_short, acts_short, true, true, s);
+        }
+      }
     }
     for (int g = 0; g < n_groups && e == hipSuccess; ++g)
       if (pass == 1 && shared_q(ps[g])) e = launch_reduce_shared_dq(d, d.grp[g], s);

@@ -479,17 +479,26 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     reinterpret_cast<u32x4*>(lds + G::OFF_KT)[idx] = u32x4{0u, 0u, 0u, 0u};
   QTileRegs<D, NW> pf;
   prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, t0 * G::QT, L, it.dsumseq);
+  // without a window every block of the sequence is resident for the whole sweep: its K / V rows
+  // are loaded here, in flight together with the first tile (one memory latency, not two)
+  TakeRegs<D, NW> kv[KACT];
+  if constexpr (!WINDOWED) {
+#pragma unroll
+    for (int kb = 0; kb < KACT; ++kb) {
+      const int s = kb * G::NW + w;
+      if (s < nkb) take_load<D, NW>(kv[kb], gd, it.kseq, it.vseq, it.gseq, s, n);
+    }
+  }
   __syncthreads();  // K^T staging zeroed
   store_qtile<D, NW, softmax, DSUM, kSeries>(lds, pf);  // first tile
   if (t0 + 1 < t1)
     prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, (t0 + 1) * G::QT, L, it.dsumseq);
   if constexpr (!WINDOWED) {
-    // every block of the sequence is resident for the whole sweep: take them once
 #pragma unroll
     for (int kb = 0; kb < KACT; ++kb) {
       const int s = kb * G::NW + w;
       if (s < nkb) {
-        take_block<D, NW, ACT>(st, kb, lds, gd, it.kseq, it.vseq, it.gseq, s, n, s);
+        take_commit<D, NW, ACT>(st, kb, lds, kv[kb], it.gseq != nullptr, s);
         st.cur[kb] = s;
       }
     }

@@ -57,6 +57,8 @@ struct GroupDesc {
   int32_t max_kv;     // max_seqlen_kv hint
   int32_t self_attn;  // query and key sequences are the same rows
   int32_t split_all;  // element-wise backward: P and dS as high + low bf16 pairs in every item
+  int32_t short_keys; // backward: the group's items run the one-wave short-key kernel; the work
+                      // list puts them after every other group's items
 };
 
 struct LaunchDesc {
@@ -65,7 +67,8 @@ struct LaunchDesc {
   int32_t n_seqs_total;
   int32_t n_items;
   int32_t work_shift;  // bucket = min(kNumBuckets-1, work >> work_shift)
-  int32_t* items;      // [n_items] packed (group, head, seq) in longest-first order
+  int32_t* items;      // [n_items] packed (group, head, seq): longest first within each class (other
+                       // groups, then short-key groups)
   int32_t* scratch;    // builder scratch: [n_seqs_total] bucket keys + [2*kNumBuckets] counters
   int32_t* err;        // device error word (GDPA_DEVICE_ERR_* bits) in the workspace
   int32_t check_err;   // validation ran first: kernels return at once if the word is non-zero

@@ -485,10 +485,12 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
     // d <= 64: the first Q tile is in flight during the staging and each next tile's Q during
     // the current tile (d = 128: the registers do not allow it; Q is loaded per tile)
     constexpr bool kPrefetchQ = D < 128 && NW == 4;  // (with 8 waves the other waves hide the load)
+    // d <= 64: every wave's first tile is in flight during the staging (one memory latency)
+    constexpr bool kFirstQEarly = D < 128;
     // ungated element-wise items: tiles proven within the series range take SeriesAct
     constexpr bool kSeriesItem = !softmax && !GATED;
     QFrags<D, QS> qcur, qnext;
-    if (kPrefetchQ && w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
+    if (kFirstQEarly && w * RW < L) load_q<D, QS>(qcur, qseq, rs, w * RW, L);
     stage_kv<D, NKV, NW * kWave, false, kSeriesItem>(lds, kseq, vseq, gseq, H, N, span_pad, softmax);
     __syncthreads();
     float kn2 = 0.0f;  // largest ||k||^2 of the item's keys
@@ -497,7 +499,7 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       for (int ww = 0; ww < NW; ++ww) kn2 = fmaxf(kn2, reinterpret_cast<const float*>(lds + G::OFF_KN)[ww]);
     for (int row0 = w * RW; row0 < L; row0 += NW * RW) {
       // next tile's Q is loaded while this tile computes
-      if (!kPrefetchQ) load_q<D, QS>(qcur, qseq, rs, row0, L);
+      if (!kPrefetchQ && !(kFirstQEarly && row0 == w * RW)) load_q<D, QS>(qcur, qseq, rs, row0, L);
       if (kPrefetchQ && row0 + NW * RW < L) load_q<D, QS>(qnext, qseq, rs, row0 + NW * RW, L);
       int lo = 0, hi = N - 1;
       if (gd.wl >= 0) lo = row0 - gd.wl > 0 ? row0 - gd.wl : 0;

@@ -12,15 +12,21 @@
 
 namespace gdpa {
 
-// Launched with exactly kNumBuckets threads (one per bucket in the scan).
+// Two classes of items share one descending key space: the items of short-key groups (which the
+// backward runs in a kernel of its own, over the tail of the list) take keys [0, kNumBuckets), every
+// other group's items keys [kNumBuckets, 2 kNumBuckets), so the second class comes first and each
+// class is longest-first within itself.
+constexpr int kClassKeys = 2 * kNumBuckets;
+
+// Launched with exactly kNumBuckets threads (two adjacent keys per thread in the scan).
 __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc d) {
   static_assert(kNumBuckets % 64 == 0 && kNumBuckets / 64 <= 64, "bucket scan layout");
-  __shared__ int32_t hist[kNumBuckets];
-  __shared__ int32_t cursor[kNumBuckets];
+  __shared__ int32_t hist[kClassKeys];
+  __shared__ int32_t cursor[kClassKeys];
   __shared__ int32_t wave_total[kNumBuckets / 64];
   const int tid = threadIdx.x;
   if (tid == 0) *d.err = 0;  // a new call: clear the device error word
-  for (int i = tid; i < kNumBuckets; i += blockDim.x) hist[i] = 0;
+  for (int i = tid; i < kClassKeys; i += blockDim.x) hist[i] = 0;
   __syncthreads();
 
   // pass 1: bucket key of every sequence (the thread's first sequence stays in registers, later
@@ -38,6 +44,7 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
     int64_t key = work >> d.work_shift;
     if (key > kNumBuckets - 1) key = kNumBuckets - 1;
     if (key < 0) key = 0;  // (offsets that decrease: the main kernels refuse such an item)
+    if (!gd.short_keys) key += kNumBuckets;
     if (s == tid) {
       key0 = (int)key;
       g0 = g;
@@ -48,13 +55,13 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
     atomicAdd(&hist[key], gd.num_heads);
   }
   __syncthreads();
-  // exclusive prefix sum in descending bucket order (longest work first): thread t owns bucket
-  // kNumBuckets-1-t. Each wave scans its 64 buckets with lane shuffles; the wave totals are then
-  // added in wave order.
+  // exclusive prefix sum in descending key order (longest work first): thread t owns keys
+  // kClassKeys-1-2t and the one below it. Each wave scans its 64 key pairs with lane shuffles; the
+  // wave totals are then added in wave order.
   {
-    const int k = kNumBuckets - 1 - tid;
+    const int k = kClassKeys - 1 - 2 * tid;
     const int lane = tid & 63, wave = tid >> 6;
-    const int32_t v = hist[k];
+    const int32_t v = hist[k] + hist[k - 1];
     int32_t incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -66,6 +73,7 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
     int32_t base = 0;
     for (int w = 0; w < wave; ++w) base += wave_total[w];
     cursor[k] = base + incl - v;
+    cursor[k - 1] = base + incl - v + hist[k];
   }
   __syncthreads();
   // pass 2: each sequence takes num_heads consecutive slots of its bucket (the order inside a

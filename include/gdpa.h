@@ -66,7 +66,11 @@ extern "C" {
 /* gdpa_problem.flags: the workspace already holds the work list that gdpa_plan() built for
  * problems with the same n_groups, num_seqs and num_heads; the call skips rebuilding it. The list
  * is a permutation of (group, head, sequence) items, so a list built from older offsets of the
- * same shape is still complete (only its longest-first order may be stale). */
+ * same shape is still complete (only its longest-first order may be stale). The list puts the
+ * items of short-key groups (bf16, element-wise act, no head_acts, no window, no shared queries,
+ * max_seqlen_kv <= 32) after every other group's, and the backward runs that tail in a kernel of
+ * its own, so plan and call must also agree on which groups these are; where they do not, the
+ * short-key kernel refuses an item with more than 32 keys (GDPA_DEVICE_ERR_LENGTH). */
 #define GDPA_FLAG_PLANNED 1
 
 /* gdpa_problem.flags: one query matrix shared by every sequence (learnable seed or summary-token

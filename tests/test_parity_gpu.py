@@ -593,6 +593,41 @@ def test_single_key_pffn(keys):
     compare_workload(w, ("fwd", "bwd"))
 
 
+def _mixed_key_groups(seed):
+    """Three bf16 PFFN groups in one grouped launch: 24 keys (SiLU), 300 keys (SiLU) and 8 keys
+    (GELU). The backward runs the two short-key groups one wave per item over the tail of the work
+    list and the 300-key group in the 8-wave kernel."""
+    parts = [make_workload("pffn_train", seed, num_seqs=6, len_range=(1, 300), keys=24, act="silu", scale=0.125),
+             make_workload("pffn_train", seed + 1, num_seqs=5, len_range=(1, 300), keys=300, act="silu",
+                           scale=0.125),
+             make_workload("pffn_train", seed + 2, num_seqs=7, len_range=(0, 200), keys=8, act="gelu",
+                           scale=0.125)]
+    w = parts[0]
+    w.groups = [p.groups[0] for p in parts]
+    w.name = "pffn mixed keys 24 / 300 / 8"
+    return w
+
+
+def test_short_and_long_key_groups_in_one_launch():
+    compare_workload(_mixed_key_groups(51), ("fwd", "bwd"))
+
+
+def test_short_and_long_key_groups_planned():
+    """The same mix through gdpa_plan + GDPA_FLAG_PLANNED: bit-identical to the unplanned calls."""
+    w = _mixed_key_groups(52)
+    dev = [device_group(g) for g in w.groups]
+    douts = [g.dout.to("cuda:0") for g in w.groups]
+    ref_f = ga.gdpa_fwd_grouped(dev)
+    ref_b = ga.gdpa_bwd_grouped(dev, douts, fwd_outs=ref_f)
+    f, b = _run_planned(dev, dev, douts)
+    torch.cuda.synchronize()
+    for (o1, _), (o2, _) in zip(ref_f, f):
+        assert torch.equal(o1, o2)
+    for r1, r2 in zip(ref_b, b):
+        for k in r1:
+            assert torch.equal(r1[k], r2[k]), k
+
+
 def test_short_keys_gated_self_attention():
     w = make_workload("causal_gated", 13, lengths=[0, 1, 5, 31, 32, 17, 32], act="gelu", window=(-1, -1))
     compare_workload(w, ("fwd", "bwd"))
