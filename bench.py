@@ -141,7 +141,8 @@ def cpu_model_name():
 
 
 def host_threads() -> int:
-    """The CPU threads this process may run on (its affinity set; a GPU machine allots 16 per GPU)."""
+    """The CPU threads the oracle runs on: this process's affinity set, at most 16 (the CPU share a
+    GPU machine allots to one GPU, whatever count its host reports)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
@@ -172,9 +173,43 @@ def cpu_baseline(workload, passes, seqs: int):
         elapsed += time.perf_counter() - t0
         flops += wk["fwd_flops"] + (wk["bwd_flops"] if "bwd" in passes else 0.0)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model_name(),
+            "cpu_model": cpu_model_name(), "host_cpus_visible": os.cpu_count(),
             "sample": f"{picked} sequences drawn from the same workload (seeded), fwd{'+bwd' if 'bwd' in passes else ''}, "
                       f"{elapsed:.1f} s, {flops / 1e9:.2f} GFLOP of model work"}
+
+
+def oracle_table():
+    """Wall time of the fp64 oracle, as it stands, for each workload at full size: one forward and
+    one backward call per group (the backward call recomputes its own row statistics), the median
+    of 20 calls for the small fp32 workload. One JSON line per workload."""
+    import numpy as np
+    import oracle
+    from gdpa_workloads import group_work, make_workload
+    from gdpa_workloads.recipe import CONFIGS
+
+    threads = host_threads()
+    print(json.dumps({"oracle_threads": threads, "host_cpus_visible": os.cpu_count(),
+                      "cpu_model": cpu_model_name()}), flush=True)
+    for name in CONFIGS:
+        w = make_workload(name, 0)
+        reps = 20 if name == "tiny_fp32" else 1
+        row = {"workload": name, "calls": reps}
+        for pass_ in w.passes:
+            times = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                for g in w.groups:
+                    if pass_ == "fwd":
+                        oracle.group_fwd(g, nthreads=threads)
+                    else:
+                        oracle.group_bwd(g, nthreads=threads, want_dg=g.g is not None)
+                times.append(time.perf_counter() - t0)
+            wall = float(np.median(times))
+            gflop = sum(group_work(g)[f"{pass_}_flops"] for g in w.groups) / 1e9
+            row[f"{pass_}_s"] = wall
+            row[f"{pass_}_gflop"] = gflop
+            row[f"{pass_}_gflops_per_s"] = gflop / wall
+        print(json.dumps(row), flush=True)
 
 
 def main():
@@ -192,7 +227,12 @@ def main():
                     help="skip the cold-cache steps (keeps a profiler's per-kernel averages to the warm steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (scales HBM byte counters)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="only time the fp64 oracle (fwd and bwd wall time) on every workload at full size")
     args = ap.parse_args()
+    if args.oracle_table:
+        oracle_table()
+        return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); the GDPA path has no "
               f"cross-GPU step and is run per GPU on its share of the batch.", file=sys.stderr)
