@@ -36,6 +36,7 @@ GDPA_WS_ERROR_OFFSET = 0
 GDPA_DEVICE_ERR_OFFSETS = 1
 GDPA_DEVICE_ERR_LENGTH = 2
 GDPA_DEVICE_ERR_SELF = 4
+GDPA_DEVICE_ERR_PLAN = 8
 
 EXPORTED = ("gdpa_workspace_size", "gdpa_plan", "gdpa_fwd", "gdpa_bwd", "gdpa_fwd_grouped",
             "gdpa_bwd_grouped", "gdpa_validate_offsets", "gdpa_bwd_noalloc", "gdpa_strerror", "gdpa_version")

@@ -160,6 +160,12 @@ void fill_desc(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, voi
   d->scratch = reinterpret_cast<int32_t*>(base + L.keys);
   d->err = reinterpret_cast<int32_t*>(base + GDPA_WS_ERROR_OFFSET);
   d->check_err = 0;
+  // work-list signature: item count and the short-key split (both fixed by the problems alone)
+  int64_t n_short = 0;
+  for (int g = 0; g < n_groups; ++g)
+    if (short_key_group(ps[g])) n_short += (int64_t)ps[g].num_seqs * ps[g].num_heads;
+  d->plan_sig = (int32_t)(((uint32_t)L.n_items * 2654435761u) ^ ((uint32_t)n_short * 40503u) ^ 0x5bd1e995u);
+  d->check_plan = (ps[0].dtype == GDPA_DTYPE_BF16 && (ps[0].flags & GDPA_FLAG_PLANNED)) ? 1 : 0;
   uint64_t max_work = 1;
   int seq_base = 0;
   for (int g = 0; g < n_groups; ++g) {

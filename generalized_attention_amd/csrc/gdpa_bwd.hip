@@ -66,8 +66,15 @@ hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool s
 // second sums those slots in sequence order and writes dq in bf16.
 constexpr int kSeqsPerSlot = 8;
 
-__global__ void __launch_bounds__(256) reduce_shared_dq_stage1(GroupDesc gd, const int32_t* err, int32_t check_err) {
-  if (check_err && *err != 0) return;  // validation refused the launch
+// (both stages return at once where the main kernels refused the launch: failed validation, or a
+// planned call whose work list was built for other problems)
+__device__ inline bool reduce_refused(const int32_t* err, int32_t check_err, int32_t plan_sig, int32_t check_plan) {
+  return (check_err && err[0] != 0) || (check_plan && err[1] != plan_sig);
+}
+
+__global__ void __launch_bounds__(256) reduce_shared_dq_stage1(GroupDesc gd, const int32_t* err, int32_t check_err,
+                                                               int32_t plan_sig, int32_t check_plan) {
+  if (reduce_refused(err, check_err, plan_sig, check_plan)) return;
   const int S = gd.shared_q, rowf4 = gd.num_heads * gd.head_dim / 4;
   const int64_t cols = (int64_t)S * rowf4;
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -89,8 +96,9 @@ __global__ void __launch_bounds__(256) reduce_shared_dq_stage1(GroupDesc gd, con
   }
 }
 
-__global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd, const int32_t* err, int32_t check_err) {
-  if (check_err && *err != 0) return;
+__global__ void __launch_bounds__(256) reduce_shared_dq_stage2(GroupDesc gd, const int32_t* err, int32_t check_err,
+                                                               int32_t plan_sig, int32_t check_plan) {
+  if (reduce_refused(err, check_err, plan_sig, check_plan)) return;
   const int S = gd.shared_q, rowf4 = gd.num_heads * gd.head_dim / 4;
   const int64_t cols = (int64_t)S * rowf4;
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -117,9 +125,11 @@ hipError_t launch_reduce_shared_dq(const LaunchDesc& d, const GroupDesc& gd, hip
   if (gd.num_seqs > 0) {
     const int slots = (gd.num_seqs + kSeqsPerSlot - 1) / kSeqsPerSlot;
     const unsigned ny = (unsigned)(slots < 65535 ? slots : 65535);
-    hipLaunchKernelGGL(reduce_shared_dq_stage1, dim3(nx, ny), dim3(256), 0, stream, gd, d.err, d.check_err);
+    hipLaunchKernelGGL(reduce_shared_dq_stage1, dim3(nx, ny), dim3(256), 0, stream, gd, d.err, d.check_err,
+                       d.plan_sig, d.check_plan);
   }
-  hipLaunchKernelGGL(reduce_shared_dq_stage2, dim3(nx), dim3(256), 0, stream, gd, d.err, d.check_err);
+  hipLaunchKernelGGL(reduce_shared_dq_stage2, dim3(nx), dim3(256), 0, stream, gd, d.err, d.check_err, d.plan_sig,
+                     d.check_plan);
   return hipGetLastError();
 }
 

@@ -72,13 +72,21 @@ struct LaunchDesc {
   int32_t* scratch;    // builder scratch: [n_seqs_total] bucket keys + [2*kNumBuckets] counters
   int32_t* err;        // device error word (GDPA_DEVICE_ERR_* bits) in the workspace
   int32_t check_err;   // validation ran first: kernels return at once if the word is non-zero
+  int32_t plan_sig;    // signature of the work list these problems give (item count, short-key split)
+  int32_t check_plan;  // planned call: kernels compare the list's signature (err[1]) with plan_sig
 };
 // passed by value as the kernels' argument (the argument block holds at most 4 KB)
 static_assert(sizeof(LaunchDesc) <= 4096, "kernel argument size");
 
-// Debug validation found bad offsets: the main kernels leave every output untouched.
+// Debug validation found bad offsets, or a planned call's work list was built for other problems:
+// the main kernels leave every output untouched (the second case reports GDPA_DEVICE_ERR_PLAN).
 __device__ inline bool launch_refused(const LaunchDesc& d) {
-  return d.check_err && *d.err != 0;
+  if (d.check_err && *d.err != 0) return true;
+  if (d.check_plan && d.err[1] != d.plan_sig) {
+    if (threadIdx.x == 0) atomicOr(d.err, GDPA_DEVICE_ERR_PLAN);
+    return true;
+  }
+  return false;
 }
 
 // The item's own offsets, checked before any tensor access: row ranges inside their tensors,

@@ -25,7 +25,10 @@ __global__ void __launch_bounds__(kNumBuckets) build_schedule_kernel(LaunchDesc 
   __shared__ int32_t cursor[kClassKeys];
   __shared__ int32_t wave_total[kNumBuckets / 64];
   const int tid = threadIdx.x;
-  if (tid == 0) *d.err = 0;  // a new call: clear the device error word
+  if (tid == 0) {
+    d.err[0] = 0;           // a new call: clear the device error word
+    d.err[1] = d.plan_sig;  // the list's signature, for planned calls
+  }
   for (int i = tid; i < kClassKeys; i += blockDim.x) hist[i] = 0;
   __syncthreads();
 

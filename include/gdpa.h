@@ -26,8 +26,9 @@
  *   - The workspace `ws` (device memory of at least gdpa_workspace_size() bytes, 256-byte aligned)
  *     is scratch for the call's work list and, in the backward, for fp32 row accumulators (long
  *     key ranges that are processed in chunks, shared query matrices). Its first 4 bytes
- *     (GDPA_WS_ERROR_OFFSET) are the device error word described below; the rest of its contents
- *     on entry are ignored.
+ *     (GDPA_WS_ERROR_OFFSET) are the device error word described below, the next 4 the work
+ *     list's signature (written by the work-list builder, read by planned calls); the rest of its
+ *     contents on entry are ignored.
  *   - The library keeps no state between calls; distinct calls may run concurrently on different
  *     streams as long as they use distinct workspaces and outputs.
  *
@@ -69,8 +70,9 @@ extern "C" {
  * same shape is still complete (only its longest-first order may be stale). The list puts the
  * items of short-key groups (bf16, element-wise act, no head_acts, no window, no shared queries,
  * max_seqlen_kv <= 32) after every other group's, and the backward runs that tail in a kernel of
- * its own, so plan and call must also agree on which groups these are; where they do not, the
- * short-key kernel refuses an item with more than 32 keys (GDPA_DEVICE_ERR_LENGTH). */
+ * its own, so plan and call must also agree on which groups these are. gdpa_plan leaves a
+ * signature of the item count and of that split in the workspace header; a planned call whose
+ * problems give another signature writes nothing and sets GDPA_DEVICE_ERR_PLAN. */
 #define GDPA_FLAG_PLANNED 1
 
 /* gdpa_problem.flags: one query matrix shared by every sequence (learnable seed or summary-token
@@ -110,6 +112,9 @@ extern "C" {
 #define GDPA_DEVICE_ERR_LENGTH 2  /* a sequence longer than max_seqlen_q / max_seqlen_kv allow */
 #define GDPA_DEVICE_ERR_SELF 4    /* self-attention (or a window) with query and key sequences that
                                      differ */
+#define GDPA_DEVICE_ERR_PLAN 8    /* GDPA_FLAG_PLANNED with a work list that gdpa_plan built for
+                                     problems of another item count or short-key split: the call's
+                                     kernels returned without touching any output */
 
 typedef enum gdpa_status {
   GDPA_OK = 0,

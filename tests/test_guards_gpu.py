@@ -156,3 +156,32 @@ def test_debug_validation_leaves_outputs_untouched(how, monkeypatch):
     assert torch.isnan(fwd_out[0]).all()
     for t in grads[:3]:
         assert torch.isnan(t).all()
+
+
+def test_planned_call_with_another_split_is_refused():
+    """A work list that gdpa_plan built with a 24-key group in the short-key class, used by a
+    planned call whose problems put that group in the other class (its max_seqlen_kv hint raised
+    to 40): the list's signature differs from the call's, every kernel of the call returns at once
+    (GDPA_DEVICE_ERR_PLAN), and no output is touched. The same list used by the problems it was
+    built for computes as usual."""
+    short = make_workload("pffn_train", 85, num_seqs=4, len_range=(1, 200), keys=24, scale=0.125).groups[0]
+    long = make_workload("pffn_train", 86, num_seqs=3, len_range=(1, 200), keys=300, scale=0.125).groups[0]
+    built = [device_group(short), device_group(long)]
+    called = [dataclasses.replace(built[0], max_seqlen_kv=40), built[1]]
+    douts = [short.dout.to("cuda:0"), long.dout.to("cuda:0")]
+    for problems, expect in ((built, 0), (called, _lib.GDPA_DEVICE_ERR_PLAN)):
+        ws = ga.workspace(problems, 1)
+        ga.gdpa_plan(built, ws)
+        planned = [dataclasses.replace(p, planned=True) for p in problems]
+        outs = [_nan_outputs(p) for p in problems]
+        print(f"[gpu] guard: planned call, expected error word {expect}", flush=True)
+        ga.gdpa_fwd_grouped(planned, outs=[o[0] for o in outs], ws=ws)
+        ga.gdpa_bwd_grouped(planned, douts, fwd_outs=[o[0] for o in outs], outs=[o[1] for o in outs], ws=ws)
+        torch.cuda.synchronize()
+        assert ga.device_error(ws) == expect
+        for (o, _), grads in outs:
+            tensors = [o] + [t for t in grads[:3] if t is not None]
+            if expect:
+                assert all(torch.isnan(t).all() for t in tensors)
+            else:
+                assert all(torch.isfinite(t).all() for t in tensors)
