@@ -1248,23 +1248,35 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
   // operands then carry the rounding remainder as a second bf16 term (uniform per item).
   const bool split_rows = L <= kSplitTerms || gd.split_all, split_keys = n <= kSplitTerms || gd.split_all;
 
+  // Q and dO rows of a 32-row step: lane (row lc, half g) loads the 16-byte pieces it needs as the
+  // A operand of S = Q K^T and dP = dO V^T. The next step's rows are loaded during the current
+  // step (registers; the wave runs alone on its SIMD, so its own loads must cover the latency).
+  u32x4 qnext[G::KK], dnext[G::KK];
+  auto load_rows = [&](int rr0) {
+    const int row = rr0 + lc;
+#pragma unroll
+    for (int kk = 0; kk < G::KK; ++kk) {
+      qnext[kk] = u32x4{0u, 0u, 0u, 0u};
+      dnext[kk] = u32x4{0u, 0u, 0u, 0u};
+      if (row < L) {
+        qnext[kk] = *reinterpret_cast<const u32x4*>(qseq + row * rs + g * (D / 2) + kk * 8);
+        dnext[kk] = *reinterpret_cast<const u32x4*>(doseq + row * rs + g * (D / 2) + kk * 8);
+      }
+    }
+  };
+  load_rows(0);
   for (int r0 = 0; r0 < L; r0 += 32) {
-    // Q and dO rows r0 .. r0+31: lane (row lc, half g) loads the 16-byte pieces it needs as the A
-    // operand of S = Q K^T and dP = dO V^T, and stores them row-major for the transposing reads
-    const int row = r0 + lc;
+    // this step's rows as A operands, and row-major in LDS for the transposing reads
     bf16x8 qa[G::KK], da[G::KK];
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) {
-      u32x4 qu = {0u, 0u, 0u, 0u}, du = {0u, 0u, 0u, 0u};
-      if (row < L) {
-        qu = *reinterpret_cast<const u32x4*>(qseq + row * rs + g * (D / 2) + kk * 8);
-        du = *reinterpret_cast<const u32x4*>(doseq + row * rs + g * (D / 2) + kk * 8);
-      }
-      qa[kk] = as_bf16x8(qu);
-      da[kk] = as_bf16x8(du);
-      *reinterpret_cast<u32x4*>(wl + G::OFF_Q + lc * G::NROW + g * D + kk * 16) = qu;
-      *reinterpret_cast<u32x4*>(wl + G::OFF_DO + lc * G::NROW + g * D + kk * 16) = du;
+      qa[kk] = as_bf16x8(qnext[kk]);
+      da[kk] = as_bf16x8(dnext[kk]);
+      *reinterpret_cast<u32x4*>(wl + G::OFF_Q + lc * G::NROW + g * D + kk * 16) = qnext[kk];
+      *reinterpret_cast<u32x4*>(wl + G::OFF_DO + lc * G::NROW + g * D + kk * 16) = dnext[kk];
     }
+    if (r0 + 32 < L) load_rows(r0 + 32);
+    const int row = r0 + lc;
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) {
