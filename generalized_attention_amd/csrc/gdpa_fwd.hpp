@@ -482,11 +482,12 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
   if (N <= G::NKV) {
     // whole key range resident: stage once, sweep all query tiles
     const int span_pad = (N + 31) & ~31;
-    // d <= 64: the first Q tile is in flight during the staging and each next tile's Q during
-    // the current tile (d = 128: the registers do not allow it; Q is loaded per tile)
-    constexpr bool kPrefetchQ = D < 128 && NW == 4;  // (with 8 waves the other waves hide the load)
-    // d <= 64: every wave's first tile is in flight during the staging (one memory latency)
-    constexpr bool kFirstQEarly = D < 128;
+    // 4 waves: each next tile's Q is in flight during the current tile (at d = 128 this takes the
+    // registers of the second score buffer, which that build gives up); 8 waves: the other waves
+    // hide the load
+    constexpr bool kPrefetchQ = NW == 4;
+    // every wave's first tile is in flight during the staging (one memory latency)
+    constexpr bool kFirstQEarly = true;
     // ungated element-wise items: tiles proven within the series range take SeriesAct
     constexpr bool kSeriesItem = !softmax && !GATED;
     QFrags<D, QS> qcur, qnext;
@@ -511,10 +512,10 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       if (N <= kSplitTerms)
         fwd_tile<D, NKV, ACT, QS, GATED, MASKED, false, true>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       else if (kSeriesItem && series)
-        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, NW == 4, false, kSeriesItem>(lds, gd, qcur, oseq, lseq, L, row0, 0,
+        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, (NW == 4 && D < 128), false, kSeriesItem>(lds, gd, qcur, oseq, lseq, L, row0, 0,
                                                                                N, kb0, kb1);
       else
-        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, NW == 4>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
+        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, (NW == 4 && D < 128)>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       if (kPrefetchQ) qcur = qnext;
     }
   } else if (LONG && D < 128 && fwd_ring_fits<D, NKV>(gd.wl, gd.wr, NW * RW)) {
@@ -555,7 +556,7 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
         FwdAcc<D, QS> acc;
         acc_init(acc);
         if (hi >= lo)
-          fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, true, NW == 4>(lds, gd, qf, acc, row0, 0, N, lo / 32,
+          fwd_accumulate<D, NKV, ACT, QS, GATED, MASKED, true, (NW == 4 && D < 128)>(lds, gd, qf, acc, row0, 0, N, lo / 32,
                                                                       hi / 32 + 1);
         fwd_finish<D, NKV, ACT, QS, GATED>(gd, acc, oseq, lseq, L, row0);
       }
@@ -592,7 +593,7 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
         const int chi = hi < kc + span - 1 ? hi : kc + span - 1;
         if (active && chi >= clo) {
           if (!kHoldQ) load_q<D, QL>(qf, qseq, rs, row0, L);
-          fwd_accumulate<D, NKV, ACT, QL, GATED, MASKED, false, NW == 4>(lds, gd, qf, acc, row0, kc, kc + span,
+          fwd_accumulate<D, NKV, ACT, QL, GATED, MASKED, false, (NW == 4 && D < 128)>(lds, gd, qf, acc, row0, kc, kc + span,
                                                                      (clo - kc) / 32, (chi - kc) / 32 + 1);
         }
       }
