@@ -258,7 +258,7 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
       // short-key groups' items (the tail of the work list) one wave each in a launch of their
       // own, and every other group's items in the kernel family their head dims and activations
       // select.
-      bool any_long = false, any_window = false, any_d128 = false;
+      bool any_long = false, any_window = false, any_d128 = false, all_ring = true;
       int dims = 0, acts = 0, dims_short = 0, acts_short = 0;
       int64_t n_short = 0;
       for (int g = 0; g < n_groups; ++g) {
@@ -276,6 +276,7 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
         } else {
           dims |= ds;
           acts |= as;
+          all_ring &= bwd_ring_ok(p.head_dim, p.window_left, p.window_right);
         }
       }
       if (pass == 0) {
@@ -284,12 +285,14 @@ int run(const gdpa_problem* ps, const gdpa_tensors* ts, int n_groups, void* ws, 
       } else {
         LaunchDesc main = d;
         main.n_items = d.n_items - (int32_t)n_short;
-        e = launch_bwd_bf16(main, dims, acts, false, !any_window, s);
+        // softmax at d <= 64: 8 waves without windows, or with every window in the ring
+        const BwdSoftmaxForm form = !any_window ? kSoftmaxNoWindow : all_ring ? kSoftmaxRingWindow : kSoftmaxAnySweep;
+        e = launch_bwd_bf16(main, dims, acts, false, form, s);
         if (e == hipSuccess && n_short > 0) {
           LaunchDesc tail = d;
           tail.items = d.items + main.n_items;
           tail.n_items = (int32_t)n_short;
-          e = launch_bwd_bf16(tail, dims_short, acts_short, true, true, s);
+          e = launch_bwd_bf16(tail, dims_short, acts_short, true, kSoftmaxNoWindow, s);
         }
       }
     }

@@ -11,7 +11,7 @@ namespace gdpa {
 // with MFMA results in the VGPR form; the softmax form at d = 128 or over several head dims
 // (gdpa_bwd_agpr.hip) and launches holding every activation (gdpa_bwd_mix_*.hip) without it.
 hipError_t launch_bwd_pointwise(const LaunchDesc& d, int dim_set, int act_set, hipStream_t stream);
-hipError_t launch_bwd_softmax(const LaunchDesc& d, int dim_set, bool wide_softmax, hipStream_t stream);
+hipError_t launch_bwd_softmax(const LaunchDesc& d, int dim_set, BwdSoftmaxForm form, hipStream_t stream);
 hipError_t launch_bwd_softmax_agpr(const LaunchDesc& d, int dim_set, hipStream_t stream);
 hipError_t launch_bwd_mixed_d32(const LaunchDesc& d, hipStream_t stream);
 hipError_t launch_bwd_mixed_d64(const LaunchDesc& d, hipStream_t stream);
@@ -21,8 +21,9 @@ hipError_t launch_bwd_mixed_all(const LaunchDesc& d, hipStream_t stream);
 // One instantiation per head-dim set and activation present: a launch with one element-wise
 // activation runs a kernel without the softmax paths (and their registers); several head dims
 // share the kernel that holds all three.
-// wide_softmax: no window in the launch; the softmax-only launches at d <= 64 then run 8 waves.
-hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, bool wide_softmax,
+// softmax_form: the softmax-only launches at d <= 64 run 8 waves when the launch has no window or
+// every window streams through the ring.
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, BwdSoftmaxForm softmax_form,
                            hipStream_t stream) {
   if (d.n_items == 0) return hipSuccess;
   constexpr int kGelu_ = 1 << GDPA_ACT_GELU, kSilu_ = 1 << GDPA_ACT_SILU;
@@ -48,7 +49,7 @@ hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool s
   constexpr int kSoftmax = 1 << GDPA_ACT_SOFTMAX;
   if (act_set == kGelu_ || act_set == kSilu_) return launch_bwd_pointwise(d, dim_set, act_set, stream);
   if (act_set == kSoftmax && (dim_set == kDim32 || dim_set == kDim64))
-    return launch_bwd_softmax(d, dim_set, wide_softmax, stream);
+    return launch_bwd_softmax(d, dim_set, softmax_form, stream);
   if (act_set == kSoftmax) return launch_bwd_softmax_agpr(d, dim_set, stream);
   switch (dim_set) {
     case kDim32: return launch_bwd_mixed_d32(d, stream);

@@ -615,22 +615,24 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         const BlockMask bm = block_mask(kofs + kf, rf, kofs + n, L, wl, wr);
         if (act[kb] && !bm.empty) {
           const int s = kb * G::NW + w;
+          // register r holds key c_row(r, g): its gate term is read for every entry, masked or
+          // not (a read under the mask would turn each entry into a branch of its own)
+          float e[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = st2[cs][r] * sc;
+            if constexpr (has_gate) x += gl[s * kBwdKeyBlock + c_row(r, g)];
+            e[r] = fast_exp2(x - l2) * dp2[cs][r];
+          }
           if (bm.full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float x = st2[cs][r] * sc;
-              if constexpr (has_gate) x += gl[s * kBwdKeyBlock + c_row(r, g)];
-              part += fast_exp2(x - l2) * dp2[cs][r];
-            }
+            for (int r = 0; r < 16; ++r) part += e[r];
           } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int kloc = c_row(r, g);
-              const int key = kofs + kf + kloc;
-              float x = st2[cs][r] * sc;
-              if constexpr (has_gate) x += gl[s * kBwdKeyBlock + kloc];
+              const int key = kofs + kf + c_row(r, g);
               const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
-              part += ok ? fast_exp2(x - l2) * dp2[cs][r] : 0.0f;
+              part += ok ? e[r] : 0.0f;
             }
           }
         }
@@ -964,7 +966,10 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       if (st.cur[kb] >= 0) flush_block<D, NW>(st, kb, gd, it.dkseq, it.dvseq, it.dgseq, n, dv_scale);
 }
 
-template <int D, int NW, int ACT, bool GATED>
+// Sweeps a backward kernel holds (its launch guarantees its items need no other).
+enum BwdPaths { kPathsAll = 0, kPathsNoWindow = 1, kPathsRing = 2 };
+
+template <int D, int NW, int ACT, bool GATED, int PATHS = kPathsAll>
 __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, int h) {
   using G = BwdGeo<D, NW>;
   BwdItem it;
@@ -1026,6 +1031,11 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   }
   const bool windowed = it.wl >= 0 || it.wr >= 0;
   const bool split_all = ACT != GDPA_ACT_SOFTMAX && gd.split_all;
+  if constexpr (PATHS == kPathsRing) {
+    // every item's window streams its keys through the ring (no key chunks, no shared queries)
+    bwd_sweep<D, NW, ACT, GATED, G::KB, true>(lds, gd, it);
+    return;
+  }
   if (it.shared_q || bwd_needs_chunks(D, it.wl, it.wr, n, split_all)) {
     // key chunks of CAP keys, one after the other; each sweeps the query tiles whose rows see it.
     // Softmax first accumulates D_i over every chunk (a pass of its own), then the main passes.
@@ -1074,7 +1084,7 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   // entries past the ends vanish for the element-wise forms (phi(0) = 0; dO and V rows past the
   // ends are zero), so only the softmax form and windows need explicit masks.
   const bool few_keys = (n + kBwdKeyBlock - 1) / kBwdKeyBlock <= G::NW;
-  if (windowed) {
+  if (PATHS == kPathsAll && windowed) {
     if (G::KB > 1 && few_keys) bwd_sweep<D, NW, ACT, GATED, 1, true>(lds, gd, it);
     else bwd_sweep<D, NW, ACT, GATED, G::KB, true>(lds, gd, it);
   } else {
@@ -1083,20 +1093,21 @@ __device__ __forceinline__ void bwd_item(char* lds, const GroupDesc& gd, int b, 
   }
 }
 
-template <int D, int NW, int ACT>
+template <int D, int NW, int ACT, int PATHS>
 __device__ __forceinline__ void bwd_dispatch_gate(char* lds, const GroupDesc& gd, int b, int h) {
-  if (gd.g != nullptr) bwd_item<D, NW, ACT, true>(lds, gd, b, h);
-  else bwd_item<D, NW, ACT, false>(lds, gd, b, h);
+  if (gd.g != nullptr) bwd_item<D, NW, ACT, true, PATHS>(lds, gd, b, h);
+  else bwd_item<D, NW, ACT, false, PATHS>(lds, gd, b, h);
 }
 
 template <int D, int NW, int ASET>
 __device__ __forceinline__ void bwd_dispatch_act(char* lds, const GroupDesc& gd, int b, int h) {
+  constexpr int P = (ASET & kBwdWideSoftmax) ? kPathsNoWindow : (ASET & kBwdRingSoftmax) ? kPathsRing : kPathsAll;
   if constexpr ((ASET & (1 << GDPA_ACT_GELU)) != 0)
-    if (gd.act == GDPA_ACT_GELU) { bwd_dispatch_gate<D, NW, GDPA_ACT_GELU>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_GELU) { bwd_dispatch_gate<D, NW, GDPA_ACT_GELU, P>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SILU)) != 0)
-    if (gd.act == GDPA_ACT_SILU) { bwd_dispatch_gate<D, NW, GDPA_ACT_SILU>(lds, gd, b, h); return; }
+    if (gd.act == GDPA_ACT_SILU) { bwd_dispatch_gate<D, NW, GDPA_ACT_SILU, P>(lds, gd, b, h); return; }
   if constexpr ((ASET & (1 << GDPA_ACT_SOFTMAX)) != 0)
-    if (gd.act == GDPA_ACT_SOFTMAX) bwd_dispatch_gate<D, NW, GDPA_ACT_SOFTMAX>(lds, gd, b, h);
+    if (gd.act == GDPA_ACT_SOFTMAX) bwd_dispatch_gate<D, NW, GDPA_ACT_SOFTMAX, P>(lds, gd, b, h);
 }
 
 template <int DSET, int ASET>

@@ -19,8 +19,10 @@ hipError_t launch_clear_error(int32_t* err, hipStream_t stream);
 // no window and some key range longer than that; 0 = any.
 hipError_t launch_fwd_bf16(const LaunchDesc& d, int dim_set, int act_set, int key_mode, hipStream_t stream);
 // small: every problem has at most 32 keys per sequence, an element-wise activation and no window
-// (one wave per work item).
-hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, bool wide_softmax,
+// (one wave per work item). softmax_form: which kernel a softmax launch at d <= 64 takes (4 waves
+// and every sweep, or the 8-wave kernels of kBwdWideSoftmax / kBwdRingSoftmax).
+enum BwdSoftmaxForm { kSoftmaxAnySweep = 0, kSoftmaxNoWindow = 1, kSoftmaxRingWindow = 2 };
+hipError_t launch_bwd_bf16(const LaunchDesc& d, int dim_set, int act_set, bool small, BwdSoftmaxForm softmax_form,
                            hipStream_t stream);
 // fp32 kernels are flat over (row, head) / (key, head); prefix tables over groups.
 struct Fp32Aux {
@@ -36,13 +38,19 @@ hipError_t launch_bwd_fp32(const LaunchDesc& d, const Fp32Aux& aux, hipStream_t 
 inline constexpr int fwd_kv_capacity(int d) { return 16384 / d; }
 // Backward: a workgroup holds 256 keys (128 at d = 128) for the whole sweep over query tiles of
 // 64 rows: 4 waves owning 64 keys each (32 at d = 128), or, in launches without d = 128 and
-// without the softmax form (or with it but no window: kBwdWideSoftmax in the activation set),
+// without the softmax form (or with it and one of the two flags below in the activation set),
 // 8 waves (two per SIMD) owning 32 keys each.
 constexpr int kBwdWaves = 4;
-constexpr int kBwdWideSoftmax = 1 << 3;  // activation-set flag: softmax launch with 8 waves
+// Activation-set flags of the 8-wave softmax launches at d <= 64. Each compiles only the sweeps
+// its items can take (a sweep compiled into the kernel but never run still costs registers in
+// all of it): no window in the launch (resident keys or key chunks), or every group's window
+// streaming its keys through the ring (bwd_ring_ok).
+constexpr int kBwdWideSoftmax = 1 << 3;
+constexpr int kBwdRingSoftmax = 1 << 4;
 template <int DSET, int ASET>
 constexpr int bwd_waves() {
-  return ((DSET & kDim128) || ((ASET & (1 << GDPA_ACT_SOFTMAX)) && !(ASET & kBwdWideSoftmax))) ? 4 : 8;
+  return ((DSET & kDim128) ||
+          ((ASET & (1 << GDPA_ACT_SOFTMAX)) && !(ASET & (kBwdWideSoftmax | kBwdRingSoftmax)))) ? 4 : 8;
 }
 constexpr int kBwdKeyBlock = 32;
 // A sum of at most this many products (dK / dV of an item with that few query rows, O / dQ of one
