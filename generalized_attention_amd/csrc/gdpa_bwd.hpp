@@ -364,6 +364,25 @@ __device__ inline BlockMask block_mask(int kf, int rf, int n, int L, int wl, int
   return m;
 }
 
+// Allowed entries of one lane in a 32x32 pair as a range of the index its registers run over
+// (rows for a lane holding a key, keys for a lane holding a row): register r, at index
+// first + c_row(r, g), is allowed iff (unsigned)(base + c_row(r, g)) <= span. lo..hi: the lane's
+// allowed range of that index (empty when hi < lo).
+struct LaneRange {
+  int base;
+  unsigned span;
+};
+__device__ inline LaneRange lane_range(int first, int lo, int hi) {
+  LaneRange m;
+  const bool empty = hi < lo;
+  m.base = empty ? -(1 << 30) : first - lo;
+  m.span = empty ? 0u : (unsigned)(hi - lo);
+  return m;
+}
+__device__ inline bool lane_ok(const LaneRange& m, int r, int g) {
+  return (unsigned)(m.base + c_row(r, g)) <= m.span;
+}
+
 // Pointers and scalars of one (sequence, head) item.
 struct BwdItem {
   const bf16* qseq;
@@ -628,12 +647,13 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r) part += e[r];
           } else {
+            // this lane's row sees keys [klo, khi] (sequence positions)
+            int klo = kofs, khi = row < L ? kofs + n - 1 : kofs - 1;
+            if (wl >= 0) klo = max(klo, row - wl);
+            if (wr >= 0) khi = min(khi, row + wr);
+            const LaneRange m = lane_range(kofs + kf, klo, khi);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kofs + kf + c_row(r, g);
-              const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
-              part += ok ? e[r] : 0.0f;
-            }
+            for (int r = 0; r < 16; ++r) part += lane_ok(m, r, g) ? e[r] : 0.0f;
           }
         }
         if (kb == KACT - 1) {
@@ -659,6 +679,17 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
             *dst = c == cf ? v : *dst + v;
           }
         }
+      } else {
+        // D_i of each tile row, once: NW consecutive lanes take a row's NW wave partials and add
+        // them in a fixed tree order; the sum replaces the first wave's partial
+        constexpr int RPW = kWave / G::NW;  // rows per wave (G::QT = NW * RPW)
+        static_assert(G::QT == G::NW * RPW, "one row per group of NW lanes");
+        const int drw = w * RPW + lane / G::NW;
+        float v = dpart[(lane % G::NW) * G::QT + drw];
+#pragma unroll
+        for (int off = 1; off < G::NW; off <<= 1) v += __shfl_xor(v, off, 64);
+        if (lane % G::NW == 0) dpart[drw] = v;
+        __syncthreads();
       }
     }
 
@@ -734,10 +765,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
               for (int a = 0; a < 4; ++a) {
                 const int rr = qs * 32 + a * 8 + g * 4;
                 const f32x4 lv = *reinterpret_cast<const f32x4*>(lse2 + rr);
-                f32x4 dsum = *reinterpret_cast<const f32x4*>(dpart + rr);
-                if constexpr (!DSUM)
-  #pragma unroll
-                  for (int ww = 1; ww < G::NW; ++ww) dsum += *reinterpret_cast<const f32x4*>(dpart + ww * G::QT + rr);
+                const f32x4 dsum = *reinterpret_cast<const f32x4*>(dpart + rr);  // D_i of the rows
   #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   lrow[4 * a + e] = lv[e];
@@ -787,10 +815,14 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
             }
             if constexpr (MASKED) {
               if (!block_mask(kf, rf, kofs + n, L, wl, wr).full) {
+                // this lane's key is seen by rows [rlo, rhi]
+                int rlo = 0, rhi = key < kofs + n ? L - 1 : -1;
+                if (wr >= 0) rlo = max(rlo, key - wr);
+                if (wl >= 0) rhi = min(rhi, key + wl);
+                const LaneRange m = lane_range(rf, rlo, rhi);
   #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                  const int row = rf + c_row(r, g);
-                  const bool ok = (key < kofs + n) & (row < L) & ((wl < 0) | (key >= row - wl)) & ((wr < 0) | (key <= row + wr));
+                  const bool ok = lane_ok(m, r, g);
                   p[r] = ok ? p[r] : 0.0f;
                   ds[r] = ok ? ds[r] : 0.0f;
                 }
