@@ -364,25 +364,6 @@ __device__ inline BlockMask block_mask(int kf, int rf, int n, int L, int wl, int
   return m;
 }
 
-// Allowed entries of one lane in a 32x32 pair as a range of the index its registers run over
-// (rows for a lane holding a key, keys for a lane holding a row): register r, at index
-// first + c_row(r, g), is allowed iff (unsigned)(base + c_row(r, g)) <= span. lo..hi: the lane's
-// allowed range of that index (empty when hi < lo).
-struct LaneRange {
-  int base;
-  unsigned span;
-};
-__device__ inline LaneRange lane_range(int first, int lo, int hi) {
-  LaneRange m;
-  const bool empty = hi < lo;
-  m.base = empty ? -(1 << 30) : first - lo;
-  m.span = empty ? 0u : (unsigned)(hi - lo);
-  return m;
-}
-__device__ inline bool lane_ok(const LaneRange& m, int r, int g) {
-  return (unsigned)(m.base + c_row(r, g)) <= m.span;
-}
-
 // Pointers and scalars of one (sequence, head) item.
 struct BwdItem {
   const bf16* qseq;

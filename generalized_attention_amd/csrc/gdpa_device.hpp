@@ -158,6 +158,25 @@ __device__ inline u32x2 lds_read_tr16(const char* lds, int byte_offset) {
 // C-register -> row mapping of a 32x32 MFMA result, for lane half g = lane/32.
 __device__ __host__ inline constexpr int c_row(int r, int g) { return (r / 4) * 8 + g * 4 + (r % 4); }
 
+// Allowed entries of one lane in a 32x32 pair as a range of the index its registers run over
+// (rows for a lane holding a key, keys for a lane holding a row): register r, at index
+// first + c_row(r, g), is allowed iff (unsigned)(base + c_row(r, g)) <= span. lo..hi: the lane's
+// allowed range of that index (empty when hi < lo).
+struct LaneRange {
+  int base;
+  unsigned span;
+};
+__device__ inline LaneRange lane_range(int first, int lo, int hi) {
+  LaneRange m;
+  const bool empty = hi < lo;
+  m.base = empty ? -(1 << 30) : first - lo;
+  m.span = empty ? 0u : (unsigned)(hi - lo);
+  return m;
+}
+__device__ inline bool lane_ok(const LaneRange& m, int r, int g) {
+  return (unsigned)(m.base + c_row(r, g)) <= m.span;
+}
+
 // When a C tile (rows = a contraction index of the next product) is fed back as a B operand,
 // B k-tile t (16 slots) takes C registers 8t..8t+7. Slot s = g*8+e of k-tile t then carries
 // row c_row(8t+e, g) = 16t + slot_row(s). slot_row is an involution on 0..15 that swaps the two

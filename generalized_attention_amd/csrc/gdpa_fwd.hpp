@@ -309,13 +309,15 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
       if (!full_block) {
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
+          // this lane's row sees keys [klo, khi] of the block's (register r: key kfirst + c_row(r, g))
           const int row = row0 + qs * 32 + qc;
+          int klo = kfirst, khi = kend - 1;
+          if (wl >= 0) klo = max(klo, row - wl);
+          if (wr >= 0) khi = min(khi, row + wr);
+          const LaneRange mr = lane_range(kfirst, klo, khi);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kpos = kfirst + c_row(r, g);
-            const bool ok = (kpos < kend) & ((wl < 0) | (kpos >= row - wl)) & ((wr < 0) | (kpos <= row + wr));
-            p[qs][r] = ok ? p[qs][r] : (softmax ? -__builtin_inff() : 0.0f);
-          }
+          for (int r = 0; r < 16; ++r)
+            p[qs][r] = lane_ok(mr, r, g) ? p[qs][r] : (softmax ? -__builtin_inff() : 0.0f);
         }
       }
     }
