@@ -914,28 +914,44 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
       }
     }
 
-    // ---- 4. dQ^T = K^T dS^T over the ring slots in use (a slot outside the tile holds zero dS);
+    // ---- 4. dQ^T = K^T dS^T over the ring slots (a slot outside the tile holds zero dS);
     // register r of lane (query, g) is d = dtile*32 + g*16 + r (out_perm order of the K^T rows)
     if (CHUNK != 2 && !FQ && dq_role) {
 #pragma unroll
       for (int qi = 0; qi < G::QH; ++qi) {
         const int qh = qh_first + qi;
-        // 16-key steps over the slots in use; the operands of step k+1 are read while step k
-        // multiplies, and two accumulators keep consecutive MFMAs independent
-        bf16x8 ka[2], sb[2], sl[2];
-        auto load_step = [&](int k, int buf) {
-          const int kbase = k * 16;
-          ka[buf] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_KT + drow * G::KTROW + (kbase + g * 8) * 2));
-          sb[buf] = sx_operand<G::SXROW>(lds, G::OFF_SX, kbase, qh);
-          if constexpr (split_dq) sl[buf] = sx_operand<G::SXROW>(lds, G::OFF_SXL, kbase, qh);
-        };
         f32x16 acc2[2] = {f32x16{}, f32x16{}};
-        load_step(0, 0);
+        if constexpr (WINDOWED) {
+          // 16-key steps over every ring slot (a slot outside the tile holds zero dS); the operands
+          // of step k+1 are read while step k multiplies, and two accumulators keep consecutive
+          // MFMAs independent
+          bf16x8 ka[2], sb[2], sl[2];
+          auto load_step = [&](int k, int buf) {
+            const int kbase = k * 16;
+            ka[buf] = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_KT + drow * G::KTROW + (kbase + g * 8) * 2));
+            sb[buf] = sx_operand<G::SXROW>(lds, G::OFF_SX, kbase, qh);
+            if constexpr (split_dq) sl[buf] = sx_operand<G::SXROW>(lds, G::OFF_SXL, kbase, qh);
+          };
+          load_step(0, 0);
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-          if (k + 1 < NK) load_step(k + 1, (k + 1) & 1);
-          acc2[k & 1] = mfma32(ka[k & 1], sb[k & 1], acc2[k & 1]);
-          if constexpr (split_dq) acc2[k & 1] = mfma32(ka[k & 1], sl[k & 1], acc2[k & 1]);
+          for (int k = 0; k < NK; ++k) {
+            if (k + 1 < NK) load_step(k + 1, (k + 1) & 1);
+            acc2[k & 1] = mfma32(ka[k & 1], sb[k & 1], acc2[k & 1]);
+            if constexpr (split_dq) acc2[k & 1] = mfma32(ka[k & 1], sl[k & 1], acc2[k & 1]);
+          }
+        } else {
+          // only the slots of the item's (or chunk's) nkb blocks: a ragged last chunk leaves the
+          // others empty. Two 16-key steps per slot, one accumulator each.
+          const int n_act = nkb < NS ? nkb : NS;
+          for (int a = 0; a < n_act; ++a) {
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) {
+              const int kbase = a * kBwdKeyBlock + hk * 16;
+              const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + G::OFF_KT + drow * G::KTROW + (kbase + g * 8) * 2));
+              acc2[hk] = mfma32(ka, sx_operand<G::SXROW>(lds, G::OFF_SX, kbase, qh), acc2[hk]);
+              if constexpr (split_dq) acc2[hk] = mfma32(ka, sx_operand<G::SXROW>(lds, G::OFF_SXL, kbase, qh), acc2[hk]);
+            }
+          }
         }
         const f32x16 acc = acc2[0] + acc2[1];
         const int row = r0 + qh * 32 + lc;
