@@ -678,7 +678,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     // the S / dP products of iteration it+1 are issued before the element-wise work of it, so the
     // MFMA pipe runs while the VALU works.
     if constexpr (CHUNK != 2) {
-      bool series = false;
+      int series = 0;  // 2: within the shorter series' range, 1: within kSeriesBound, 0: exact
       if constexpr (kSeries) {
         const float* qnrm = reinterpret_cast<const float*>(lds + G::OFF_QNRM) + ((FQ && (j & 1)) ? NW : 0);
         float qn2 = 0.0f, kn2 = 0.0f;
@@ -686,11 +686,13 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         for (int ww = 0; ww < NW; ++ww) qn2 = fmaxf(qn2, qnrm[ww]);
 #pragma unroll
         for (int kb = 0; kb < KACT; ++kb) kn2 = fmaxf(kn2, act[kb] ? st.kn2[kb] : 0.0f);
-        series = seq_series_ok(gd.scale, qn2, kn2);
+        series = seq_series_within(gd.scale, qn2, kn2, series_short_bound_bwd<ACT>()) ? 2
+                 : seq_series_ok(gd.scale, qn2, kn2)                              ? 1
+                                                                                  : 0;
       }
-      // the main pass of the tile, instantiated for the series and the exact activation
+      // the main pass of the tile, instantiated for the two series and the exact activation
       auto main_pass = [&](auto series_tag) {
-        constexpr bool SER = decltype(series_tag)::value;
+        constexpr int SER = decltype(series_tag)::value;
         constexpr int NIT = 2 * KACT;
         const int sx_cur = (FQ && (j & 1)) ? G::OFF_SXL : G::OFF_SX;  // this tile's dS^T area
         const int q_cur = (FQ && (j & 1)) ? G::OFF_QN1 : G::OFF_QN;    // this tile's Q / dO buffer
@@ -722,7 +724,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         // waves (no registers to spare).
         // (ungated element-wise forms: only the series tiles keep it; the exact tiles of such items
       // would otherwise need more registers than the wave has)
-      constexpr bool PIPE = CHUNK == 0 && !(split && NW == 8) && (!kSeries || SER);
+      constexpr bool PIPE = CHUNK == 0 && !(split && NW == 8) && (!kSeries || SER != 0);
         if constexpr (PIPE) {
           load_a(0);
           issue_sdp(0, 0);
@@ -767,7 +769,14 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           auto elementwise = [&]() {
             // register r is query row rf + c_row(r, g), key `key`
             float p[16], ds[16];
-            if (kSeries && series) {
+            if constexpr (kSeries && SER == 2) {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                float dphi;
+                SeriesAct<ACT>::value_grad_short(sacc[cs][r], a1, d1, p[r], dphi);
+                ds[r] = dpacc[cs][r] * dphi;
+              }
+            } else if constexpr (kSeries && SER == 1) {
   #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 float dphi;
@@ -867,10 +876,11 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         }
       };
       if constexpr (kSeries) {
-        if (series) main_pass(std::true_type{});
-        else main_pass(std::false_type{});
+        if (series == 2) main_pass(std::integral_constant<int, 2>{});
+        else if (series == 1) main_pass(std::integral_constant<int, 1>{});
+        else main_pass(std::integral_constant<int, 0>{});
       } else {
-        main_pass(std::false_type{});
+        main_pass(std::integral_constant<int, 0>{});
       }
     }
     if constexpr (FQ) {
@@ -1326,15 +1336,25 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
     // register r of lane (key lc, g) is row r0 + c_row(r, g); keys and rows past the ends meet
     // zero operands (phi(0) = 0, and their dO / Q rows are zero), so no mask is needed
     float p[16], ds[16];
-    bool series = false;
+    int series = 0;  // 2: within the shorter series' range, 1: within kSeriesBound, 0: exact
     if constexpr (!GATED) {
       // the step's rows: this lane holds half of row lc, the other half sits 32 lanes away
       float qn2 = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < G::KK; ++kk) qn2 += sumsq_bf16x8(__builtin_bit_cast(u32x4, qa[kk]));
-      series = seq_series_ok(gd.scale, wave_max(qn2 + __shfl_xor(qn2, 32, 64)), kn2);
+      qn2 = wave_max(qn2 + __shfl_xor(qn2, 32, 64));
+      series = seq_series_within(gd.scale, qn2, kn2, series_short_bound_bwd<ACT>()) ? 2
+               : seq_series_ok(gd.scale, qn2, kn2)                              ? 1
+                                                                                : 0;
     }
-    if (!GATED && series) {
+    if (!GATED && series == 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float dphi;
+        SeriesAct<ACT>::value_grad_short(sacc[r], a1, d1, p[r], dphi);
+        ds[r] = dpacc[r] * dphi;
+      }
+    } else if (!GATED && series == 1) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float dphi;

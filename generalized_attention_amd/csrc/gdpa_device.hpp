@@ -338,13 +338,34 @@ struct SeriesAct {
     p = s * __builtin_fmaf(s, __builtin_fmaf(w, a3, a1), 0.5f);
     dphi = __builtin_fmaf(s, __builtin_fmaf(w, d3, d1), 0.5f);
   }
+  // One term fewer, for tiles proven within the smaller ranges below: phi(x) = x (1/2 + A x),
+  // phi'(x) = 1/2 + C x (two and one multiply-adds).
+  __host__ __device__ static inline float value_short(float s, float a1) { return s * __builtin_fmaf(s, a1, 0.5f); }
+  __host__ __device__ static inline void value_grad_short(float s, float a1, float d1, float& p, float& dphi) {
+    p = s * __builtin_fmaf(s, a1, 0.5f);
+    dphi = __builtin_fmaf(s, d1, 0.5f);
+  }
 };
+
+// Ranges of the shorter series. The omitted terms B x^4 and D x^3 leave relative errors of about
+// 2 |B| x^3 (phi) and 2 |D| x^3 (phi'): x^3 / 24 and x^3 / 6 for SiLU, phi0 x^3 / 3 and
+// 4 phi0 x^3 / 3 for GELU. The forward needs phi only: over |x| <= 0.16 (SiLU) and 0.11 (GELU)
+// its error is at most 1.9e-4; the backward needs both: over |x| <= 0.1 (SiLU) and 0.07 (GELU)
+// phi' is off by at most 1.9e-4 (SiLU) and 2.1e-4 (GELU), and phi by 5e-5. That is about a tenth
+// of the bf16 rounding of P and dS (2^-9), the level of the longer series' own error.
+template <int ACT>
+__host__ __device__ constexpr float series_short_bound_fwd() { return ACT == GDPA_ACT_GELU ? 0.11f : 0.16f; }
+template <int ACT>
+__host__ __device__ constexpr float series_short_bound_bwd() { return ACT == GDPA_ACT_GELU ? 0.07f : 0.1f; }
 
 // Every argument x = scale <q, k> of a tile lies in the series range when
 // scale^2 max ||q||^2 max ||k||^2 <= kSeriesBound^2 (Cauchy-Schwarz), with a margin for the fp32
 // accumulation of the scores and of the squared norms. False for NaN or infinite norms.
+__host__ __device__ inline bool seq_series_within(float scale, float qn2, float kn2, float bound) {
+  return scale * scale * qn2 * kn2 <= bound * bound * 0.998f;
+}
 __host__ __device__ inline bool seq_series_ok(float scale, float qn2, float kn2) {
-  return scale * scale * qn2 * kn2 <= kSeriesBound * kSeriesBound * 0.998f;
+  return seq_series_within(scale, qn2, kn2, kSeriesBound);
 }
 
 // Sum of squares of the 8 bf16 values of a 16-byte chunk (each product is exact in fp32).

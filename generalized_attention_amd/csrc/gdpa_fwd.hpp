@@ -262,9 +262,9 @@ __device__ __forceinline__ void acc_init(FwdAcc<D, QS>& a) {
 // PSPLIT: at most kSplitTerms keys, so each output is a sum of that few products; P then enters
 // O^T = V^T P^T as a high + low bf16 pair (its single rounding would be too coarse there).
 // SERIES: ungated element-wise tile whose arguments are all proven within the series range
-// (SeriesAct instead of PointAct).
+// (SeriesAct instead of PointAct): 1 = |x| <= kSeriesBound, 2 = within the shorter series' range.
 template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool RING = false, bool PIPE = true,
-          bool PSPLIT = false, bool SERIES = false>
+          bool PSPLIT = false, int SERIES = 0>
 __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf,
                                                FwdAcc<D, QS>& acc, int row0, int kbase, int kend, int kb0,
                                                int kb1) {
@@ -297,7 +297,8 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
         float x;
         if constexpr (GATED) x = __builtin_fmaf(s[qs][r], sc, gl[slot * 32 + c_row(r, g)]);
         if constexpr (softmax) p[qs][r] = GATED ? x : s[qs][r] * sc;
-        else if constexpr (SERIES) p[qs][r] = SeriesAct<ACT>::value(s[qs][r], a1, a3);
+        else if constexpr (SERIES == 2) p[qs][r] = SeriesAct<ACT>::value_short(s[qs][r], a1);
+        else if constexpr (SERIES == 1) p[qs][r] = SeriesAct<ACT>::value(s[qs][r], a1, a3);
         else p[qs][r] = GATED ? PointAct<ACT>::value(x, c1, c3) : PointAct<ACT>::value(s[qs][r], c1, c3);
       }
     if constexpr (MASKED) {
@@ -441,7 +442,7 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
 
 // One wave tile against staged key blocks [kb0, kb1), then its epilogue.
 template <int D, int NKV, int ACT, int QS, bool GATED, bool MASKED, bool PIPE, bool PSPLIT = false,
-          bool SERIES = false>
+          int SERIES = 0>
 __device__ __forceinline__ void fwd_tile(const char* lds, const GroupDesc& gd, const QFrags<D, QS>& qf, OutPtr oseq,
                                          float* lseq, int L, int row0, int klo, int span, int kb0, int kb1) {
   FwdAcc<D, QS> acc;
@@ -509,13 +510,21 @@ __device__ __forceinline__ void fwd_item(char* lds, const GroupDesc& gd, int b, 
       if (gd.wr >= 0) hi = row0 + RW - 1 + gd.wr < N - 1 ? row0 + RW - 1 + gd.wr : N - 1;
       const int kb0 = lo / 32, kb1 = hi >= lo ? hi / 32 + 1 : kb0;
       // (8 waves: four per SIMD, no software pipeline inside a wave; 4 waves: two per SIMD, with it)
-      bool series = false;
-      if constexpr (kSeriesItem) series = seq_series_ok(gd.scale, q_norm_max<D, QS>(qcur), kn2);
+      int series = 0;  // 2: within the shorter series' range, 1: within kSeriesBound
+      if constexpr (kSeriesItem) {
+        const float qn2 = q_norm_max<D, QS>(qcur);
+        series = seq_series_within(gd.scale, qn2, kn2, series_short_bound_fwd<ACT>()) ? 2
+                 : seq_series_ok(gd.scale, qn2, kn2)                              ? 1
+                                                                                  : 0;
+      }
       if (N <= kSplitTerms)
         fwd_tile<D, NKV, ACT, QS, GATED, MASKED, false, true>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
-      else if (kSeriesItem && series)
-        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, (NW == 4 && D < 128), false, kSeriesItem>(lds, gd, qcur, oseq, lseq, L, row0, 0,
-                                                                               N, kb0, kb1);
+      else if (kSeriesItem && series == 2)
+        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, (NW == 4 && D < 128), false, kSeriesItem ? 2 : 0>(
+            lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
+      else if (kSeriesItem && series == 1)
+        fwd_tile<D, NKV, ACT, QS, GATED, MASKED, (NW == 4 && D < 128), false, kSeriesItem ? 1 : 0>(
+            lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       else
         fwd_tile<D, NKV, ACT, QS, GATED, MASKED, (NW == 4 && D < 128)>(lds, gd, qcur, oseq, lseq, L, row0, 0, N, kb0, kb1);
       if (kPrefetchQ) qcur = qnext;

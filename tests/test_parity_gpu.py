@@ -327,15 +327,18 @@ def test_series_and_exact_tiles_in_one_launch(act):
     compare_workload(w, ("fwd", "bwd"))
 
 
+@pytest.mark.parametrize("tier", ["series", "short"])
 @pytest.mark.parametrize("act", ["silu", "gelu"])
-def test_series_near_its_bound(act):
+def test_series_near_its_bound(act, tier):
     """Rows and keys along one common direction (plus small noise), with the scale chosen so that
     scale * max||q|| * max||k|| = 0.245: the bound holds for every tile while the arguments spread
     over most of [-1/4, 1/4], where the series' truncation is largest. Split operands and float32
     outputs take the bf16 rounding of P / dS and of the results out of the gradients (on such
     aligned inputs that rounding alone reaches 0.024-0.028 of RMS in dK), so what remains is the
     series' own error: a CPU emulation of these formulas puts it at 1e-5 to 5e-4 of RMS, and the
-    gradients are held to 5e-3, ten times that (a wrong series coefficient exceeds it)."""
+    gradients are held to 5e-3, ten times that (a wrong series coefficient exceeds it).
+    tier "short": the same just inside the shorter series' backward range (0.98 of 0.1 for SiLU,
+    of 0.07 for GELU; the forward's range is wider), where every tile of both passes takes it."""
     import dataclasses
     w = make_workload("pffn_train", 37, lengths=[40, 300, 129, 1, 64, 257], act=act, ctx_dim=64)
     g = w.groups[0]
@@ -351,7 +354,8 @@ def test_series_near_its_bound(act):
     g.q, g.k = along(g.total_q), along(g.total_kv)
     qn = g.q.double().norm(dim=-1).max().item()
     kn = g.k.double().norm(dim=-1).max().item()
-    g.spec = dataclasses.replace(g.spec, scale=0.245 / (qn * kn))
+    reach = 0.245 if tier == "series" else 0.98 * (0.1 if act == "silu" else 0.07)
+    g.spec = dataclasses.replace(g.spec, scale=reach / (qn * kn))
     report = compare_workload(w, ("fwd", "bwd"), fp32_out=True, split_operands=True)
     for name in ("g0.dq", "g0.dk", "g0.dv"):
         assert report[name] <= 5e-3, (name, report[name])

@@ -30,8 +30,26 @@ template <int ACT> void table(float scale) {
     printf("%d %.9g %.9g %.9g %.9g %.9g\n", ACT, scale, x, p * scale, pv * scale, dphi);
   }
 }
+// the shorter series over its forward range (value) and its backward range (value and derivative)
+template <int ACT> void table_short(float scale) {
+  float a1, a3, d1, d3;
+  SeriesAct<ACT>::coeffs(scale, a1, a3, d1, d3);
+  for (int i = -1000; i <= 1000; ++i) {
+    const float x = series_short_bound_fwd<ACT>() * i / 1000.0f, s = x / scale;
+    printf("F %d %.9g %.9g %.9g\n", ACT, scale, x, SeriesAct<ACT>::value_short(s, a1) * scale);
+    const float xb = series_short_bound_bwd<ACT>() * i / 1000.0f, sb = xb / scale;
+    float p, dphi;
+    SeriesAct<ACT>::value_grad_short(sb, a1, d1, p, dphi);
+    printf("G %d %.9g %.9g %.9g %.9g\n", ACT, scale, xb, p * scale, dphi);
+  }
+}
 int main() {
   for (float scale : {1.0f, 0.125f, 0.001f}) { table<GDPA_ACT_GELU>(scale); table<GDPA_ACT_SILU>(scale); }
+  for (float scale : {1.0f, 0.001f}) { table_short<GDPA_ACT_GELU>(scale); table_short<GDPA_ACT_SILU>(scale); }
+  printf("R %.9g %.9g %.9g %.9g\n", series_short_bound_fwd<GDPA_ACT_GELU>(), series_short_bound_fwd<GDPA_ACT_SILU>(),
+         series_short_bound_bwd<GDPA_ACT_GELU>(), series_short_bound_bwd<GDPA_ACT_SILU>());
+  printf("W %d %d %d\n", (int)seq_series_within(0.001f, 99.0f, 100.0f, 0.1f),
+         (int)seq_series_within(0.001f, 100.0f, 100.0f, 0.1f), (int)seq_series_within(0.001f, 1.0f / 0.0f, 1.0f, 0.1f));
   // the bound: scale^2 qn2 kn2 <= (1/4)^2 with a margin
   printf("B %d %d %d %d\n", (int)seq_series_ok(0.001f, 100.0f, 600.0f), (int)seq_series_ok(0.001f, 250.0f, 250.0f),
          (int)seq_series_ok(0.001f, 251.0f, 250.0f), (int)seq_series_ok(0.001f, 1.0f / 0.0f, 1.0f));
@@ -49,9 +67,15 @@ def table():
         subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "--offload-arch=gfx950", "-I", CSRC, "-I",
                         os.path.join(ROOT, "include"), src, "-o", exe], check=True, capture_output=True)
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
-    rows = [l.split() for l in out if l and not l.startswith("B")]
+    rows = [l.split() for l in out if l and l[0] not in "BFGRW"]
     bound = [l for l in out if l.startswith("B")][0].split()[1:]
+    tagged = {t: [l.split()[1:] for l in out if l.startswith(t + " ")] for t in "FGRW"}
+    global SHORT
+    SHORT = {t: np.array(v, dtype=np.float64) for t, v in tagged.items()}
     return np.array(rows, dtype=np.float64), [int(b) for b in bound]
+
+
+SHORT = {}
 
 
 def exact(act, x):
@@ -83,3 +107,35 @@ def test_series_bound(table):
     _, b = table
     # 1e-6 * 100 * 600 = 0.06 <= 1/16; 1e-6 * 250 * 250 = 1/16 itself is refused (margin); above: no; inf: no
     assert b == [1, 0, 0, 0]
+
+
+def test_short_series_matches_activations(table):
+    """The one-term-shorter series (value_short / value_grad_short) within the ranges its tiles are
+    proven to lie in: relative errors as the header states them (phi within 1.9e-4 over the forward
+    range; phi' within 1.9e-4 for SiLU and 2.1e-4 for GELU, phi within 5e-5, over the backward
+    range), plus fp32 rounding."""
+    F, Gt, R = SHORT["F"], SHORT["G"], SHORT["R"][0]
+    np.testing.assert_allclose(R, [0.11, 0.16, 0.07, 0.1], rtol=1e-6)
+    for act in (0, 1):
+        for scale in (1.0, 0.001):
+            rows = F[(F[:, 0] == act) & np.isclose(F[:, 1], scale)]
+            x = rows[:, 2]
+            p_ref, _ = exact(act, x)
+            assert len(rows) == 2001 and abs(np.max(np.abs(x)) - R[act]) < 1e-6  # the forward range
+            assert np.all(np.abs(rows[:, 3] - p_ref) <= 1.95e-4 * np.abs(p_ref) + 1e-7), (act, scale)
+            rows = Gt[(Gt[:, 0] == act) & np.isclose(Gt[:, 1], scale)]
+            x = rows[:, 2]
+            p_ref, g_ref = exact(act, x)
+            assert abs(np.max(np.abs(x)) - R[2 + act]) < 1e-6  # the backward range
+            assert np.all(np.abs(rows[:, 3] - p_ref) <= 6e-5 * np.abs(p_ref) + 1e-7), (act, scale)
+            tol_g = 2.15e-4 if act == 0 else 1.95e-4
+            assert np.all(np.abs(rows[:, 4] - g_ref) <= tol_g * np.abs(g_ref)), (act, scale)
+            # the omitted cubic term of phi' (2 |D| x^3 relative) is what these bounds are about:
+            # dropping the linear one instead would be off by C x / (1/2), 0.05 or more at the ends
+            assert np.max(np.abs(rows[:, 4] - g_ref) / np.abs(g_ref)) > 0.5 * tol_g
+
+
+def test_short_series_range_check(table):
+    """seq_series_within: scale^2 qn2 kn2 against bound^2 with the 0.998 margin (0.0099 passes
+    0.1^2 * 0.998, 0.01 does not); an infinite norm never passes."""
+    assert list(SHORT["W"][0]) == [1, 0, 0]
