@@ -68,8 +68,9 @@ struct BwdGeo {
   static constexpr int QBUFS = NW == 8 ? 2 : 1;
   static constexpr int OFF_QN1 = OFF_GATE + CAP * 4;
   static constexpr int OFF_DON1 = OFF_QN1 + QT * NROW;
-  static constexpr int OFF_QNRM = QBUFS == 2 ? OFF_DON1 + QT * NROW : OFF_GATE + CAP * 4;  // [2][NW] max ||q||^2
-  static constexpr int BYTES = OFF_QNRM + 2 * NW * 4;
+  // [2][NW][4] max ||q||^2 of the tile rows each row of 16 lanes of a staging wave stored
+  static constexpr int OFF_QNRM = QBUFS == 2 ? OFF_DON1 + QT * NROW : OFF_GATE + CAP * 4;
+  static constexpr int BYTES = OFF_QNRM + 2 * NW * 4 * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
   static_assert(CAP == bwd_capacity(D), "resident keys per workgroup");
   static_assert(NW == 4 || D <= 64, "8 waves only for d <= 64");
@@ -284,8 +285,11 @@ __device__ void prefetch_qtile(QTileRegs<D, NW>& pf, const bf16* qseq, const bf1
 }
 
 // buf: which Q / dO tile buffer (the second exists with 8 waves).
-// QNORM: each wave also writes the largest ||q||^2 of the tile rows it stored to
-// G::OFF_QNRM + 4 (buf * NW + w) (the series bound of ungated element-wise tiles).
+// QNORM: each row of 16 lanes also writes the largest ||q||^2 of the tile rows it stored to
+// G::OFF_QNRM + 4 (4 (buf * NW + w) + lane / 16) (the series bound of ungated element-wise tiles).
+// With 8 waves the row sums and maxima stay inside rows of 16 lanes (DPP, no LDS round trip on
+// the tile's critical path); the 4-wave kernels take the wave's maximum by shuffles and write it
+// from four lanes.
 template <int D, int NW, bool SOFTMAX, bool DSUM = false, bool QNORM = false>
 __device__ void store_qtile(char* lds, const QTileRegs<D, NW>& pf, int buf = 0) {
   using G = BwdGeo<D, NW>;
@@ -296,12 +300,17 @@ __device__ void store_qtile(char* lds, const QTileRegs<D, NW>& pf, int buf = 0) 
 #pragma unroll
     for (int i = 0; i < G::NPF; ++i) {
       float n2 = sumsq_bf16x8(pf.q[i]);
+      if constexpr (NW == 8) {
+        n2 = group_sum<G::CPR>(n2);
+      } else {
 #pragma unroll
-      for (int off = 1; off < G::CPR; off <<= 1) n2 += __shfl_xor(n2, off, 64);
+        for (int off = 1; off < G::CPR; off <<= 1) n2 += __shfl_xor(n2, off, 64);
+      }
       m = fmaxf(m, n2);
     }
-    m = wave_max(m);
-    if (lane_id() == 0) reinterpret_cast<float*>(lds + G::OFF_QNRM)[buf * NW + (threadIdx.x >> 6)] = m;
+    m = NW == 8 ? row16_max(m) : wave_max(m);
+    if ((lane_id() & 15) == 0)
+      reinterpret_cast<float*>(lds + G::OFF_QNRM)[(buf * NW + (threadIdx.x >> 6)) * 4 + (lane_id() >> 4)] = m;
   }
 #pragma unroll
   for (int i = 0; i < G::NPF; ++i) {
@@ -474,9 +483,11 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
   float* dpart = reinterpret_cast<float*>(lds + G::OFF_DPART);
   const float* gl = reinterpret_cast<const float*>(lds + G::OFF_GATE);
 
-  // K^T staging of slots never taken must hold finite values (they meet zero dS in dQ)
-  for (int idx = threadIdx.x; idx < D * (G::KTROW / 16); idx += G::THREADS)
-    reinterpret_cast<u32x4*>(lds + G::OFF_KT)[idx] = u32x4{0u, 0u, 0u, 0u};
+  // K^T staging of slots never taken must hold finite values (they meet zero dS in dQ); without a
+  // window, an item (or chunk) with a block for every slot takes them all
+  if (WINDOWED || nkb < NS)
+    for (int idx = threadIdx.x; idx < D * (G::KTROW / 16); idx += G::THREADS)
+      reinterpret_cast<u32x4*>(lds + G::OFF_KT)[idx] = u32x4{0u, 0u, 0u, 0u};
   QTileRegs<D, NW> pf;
   prefetch_qtile<D, NW, softmax, DSUM>(pf, it.qseq, it.doseq, it.lseseq, rs, H, t0 * G::QT, L, it.dsumseq);
   // without a window every block of the sequence is resident for the whole sweep: its K / V rows
@@ -680,10 +691,10 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
     if constexpr (CHUNK != 2) {
       int series = 0;  // 2: within the shorter series' range, 1: within kSeriesBound, 0: exact
       if constexpr (kSeries) {
-        const float* qnrm = reinterpret_cast<const float*>(lds + G::OFF_QNRM) + ((FQ && (j & 1)) ? NW : 0);
+        const float* qnrm = reinterpret_cast<const float*>(lds + G::OFF_QNRM) + ((FQ && (j & 1)) ? 4 * NW : 0);
         float qn2 = 0.0f, kn2 = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) qn2 = fmaxf(qn2, qnrm[ww]);
+        for (int ww = 0; ww < 4 * NW; ++ww) qn2 = fmaxf(qn2, qnrm[ww]);
 #pragma unroll
         for (int kb = 0; kb < KACT; ++kb) kn2 = fmaxf(kn2, act[kb] ? st.kn2[kb] : 0.0f);
         series = seq_series_within(gd.scale, qn2, kn2, series_short_bound_bwd<ACT>()) ? 2

@@ -387,6 +387,41 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// Lane exchanges inside rows of 16 lanes through DPP operand modifiers: a VALU instruction reads
+// the other lane's register directly, with no LDS round trip (each ds_bpermute shuffle of a chain
+// waits for the LDS). Call with every lane active.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]: lane i ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]: lane i ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane 7 - i inside each group of 8
+constexpr int kDppMirror = 0x140;     // lane 15 - i inside each row of 16
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of N consecutive lanes (N = 1, 2, 4, 8 or 16), on every lane of the
+// group. Each step adds the partner's partial sum: after the first two steps every lane of a quad
+// holds the same quad sum, so the mirrored lane of the other quad (or half-row) carries the value
+// that lane i ^ 4 (i ^ 8) would: the result is that of the xor butterfly.
+template <int N>
+__device__ inline float group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+  if constexpr (N >= 2) v += dpp_mov<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_mov<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_mov<kDppMirror>(v);
+  return v;
+}
+
+// Maximum over each row of 16 lanes, on every lane of the row (the wave's maximum is then the
+// largest of lanes 0, 16, 32 and 48).
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_mov<kDppMirror>(v));
+}
+
 // log sigmoid(g) in fp32, overflow-free: min(g, 0) - log1p(exp(-|g|)).
 __device__ inline float log_sigmoid_f(float g) {
   return fminf(g, 0.0f) - log1pf(__expf(-fabsf(g)));
