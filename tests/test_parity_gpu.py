@@ -361,6 +361,47 @@ def test_series_near_its_bound(act, tier):
         assert report[name] <= 5e-3, (name, report[name])
 
 
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_series_check_sees_every_row(act):
+    """The backward's series check of a query tile takes the largest ||q||^2 over its rows: each
+    row's norm is summed over the lanes holding its 16-byte pieces and the maximum taken over the
+    tile's rows. Here every 64-row tile has one outlier row, at a different row offset and with its
+    weight in a different 8-wide piece of d from tile to tile, whose arguments reach |x| ~ 6, far
+    outside the series range, while every other row stays inside it. A reduction that missed the
+    outlier's lane or row would put its tile on the series, whose derivative there is off by more
+    than ten (a CPU emulation puts that row's dQ error at 14 to 50 x RMS(dQ)). dQ is graded by the
+    stated rule (bf16 rounding of dS alone: 0.01 x RMS). O, dK and dV are not: the outlier rows
+    dominate them, and one bf16 rounding of such rows' P or dS alone reaches 0.03 of their RMS."""
+    w = make_workload("pffn_train", 41, lengths=[1000, 777, 640, 130, 64, 65], act=act)
+    g = w.groups[0]
+    q = g.q.clone()
+    qo = g.q_offsets
+    outliers = []
+    for b in range(len(qo) - 1):
+        L = int(qo[b + 1] - qo[b])
+        for t in range((L + 63) // 64):
+            off = (7 * t + 13 * b) % min(64, L - 64 * t)
+            c = (t + 3 * b) % 8
+            row = int(qo[b]) + 64 * t + off
+            q[row, :, 8 * c:8 * c + 8] = 700.0
+            outliers.append(row)
+    g.q = q
+    scale = g.spec.scale
+    kmax = g.k.double().norm(dim=-1).max().item()
+    qn = q.double().norm(dim=-1).amax(dim=-1)
+    mask = torch.zeros(q.shape[0], dtype=torch.bool)
+    mask[outliers] = True
+    assert scale * qn[~mask].max().item() * kmax < 0.25  # inside the series range
+    assert scale * qn[mask].min().item() * kmax > 1.0    # far outside it
+    dev = [device_group(g)]
+    fwd_outs = run_fwd(dev)
+    bwd_outs = run_bwd(dev, [g.dout.to("cuda:0")], fwd_outs, want_dg=False)
+    torch.cuda.synchronize()
+    ref = oracle.group_bwd(g.subset(list(range(g.spec.num_seqs))), want_dg=False)
+    err = check("bf16", to64(bwd_outs[0]["dq"]), ref["dq"], f"outlier rows {act} dQ")
+    print(f"[gpu] outlier rows {act}: literal max|err|/RMS dQ={err:.4f}", flush=True)
+
+
 # ------------------------------------------------------------------------------------------------
 # Properties of the HIP path itself
 # ------------------------------------------------------------------------------------------------
