@@ -649,7 +649,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
           }
         }
         if (kb == KACT - 1) {
-          part += __shfl_xor(part, 32);
+          part = half32_sum(part);
           if (g == 0) dpart[w * G::QT + qs * 32 + lc] = part;
           part = 0.0f;
           if (qs == 0) l2 = lse2[32 + lc];
@@ -678,8 +678,7 @@ __device__ __forceinline__ void bwd_sweep(char* lds, const GroupDesc& gd, const 
         static_assert(G::QT == G::NW * RPW, "one row per group of NW lanes");
         const int drw = w * RPW + lane / G::NW;
         float v = dpart[(lane % G::NW) * G::QT + drw];
-#pragma unroll
-        for (int off = 1; off < G::NW; off <<= 1) v += __shfl_xor(v, off, 64);
+        v = group_sum<G::NW>(v);
         if (lane % G::NW == 0) dpart[drw] = v;
         __syncthreads();
       }
@@ -1353,7 +1352,7 @@ __device__ __forceinline__ void bwd_small_item(char* wl, const GroupDesc& gd, in
       float qn2 = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < G::KK; ++kk) qn2 += sumsq_bf16x8(__builtin_bit_cast(u32x4, qa[kk]));
-      qn2 = wave_max(qn2 + __shfl_xor(qn2, 32, 64));
+      qn2 = wave_max_lanes(half32_sum(qn2));
       series = seq_series_within(gd.scale, qn2, kn2, series_short_bound_bwd<ACT>()) ? 2
                : seq_series_ok(gd.scale, qn2, kn2)                              ? 1
                                                                                 : 0;

@@ -413,6 +413,27 @@ __device__ inline float group_sum(float v) {
   return v;
 }
 
+// This lane's value combined with lane l ^ 32's (or l ^ 16's) by a commutative operation, with one
+// VALU lane swap instead of an LDS round trip: v_permlane32_swap (v_permlane16_swap) of a register
+// with itself returns two registers that hold, on every lane, its own value and its partner's (in
+// an order that depends on the half), so the sum or the maximum of the two needs no lane select and
+// equals that of the shuffle exactly. Call with every lane active.
+__device__ inline float half32_sum(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+__device__ inline float half32_max(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ inline float half16_max(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
 // Maximum over each row of 16 lanes, on every lane of the row (the wave's maximum is then the
 // largest of lanes 0, 16, 32 and 48).
 __device__ inline float row16_max(float v) {
@@ -421,6 +442,10 @@ __device__ inline float row16_max(float v) {
   v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
   return fmaxf(v, dpp_mov<kDppMirror>(v));
 }
+
+// Maximum over the lanes of a wave, the same on every lane, without LDS or scalar registers: rows of
+// 16 lanes by DPP, then across rows by the two lane swaps (the same value as wave_max).
+__device__ inline float wave_max_lanes(float v) { return half32_max(half16_max(row16_max(v))); }
 
 // log sigmoid(g) in fp32, overflow-free: min(g, 0) - log1p(exp(-|g|)).
 __device__ inline float log_sigmoid_f(float g) {

@@ -328,7 +328,7 @@ __device__ __forceinline__ void fwd_accumulate(const char* lds, const GroupDesc&
         float bm = p[qs][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) bm = fmaxf(bm, p[qs][r]);
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = half32_max(bm);
         const float mnew = fmaxf(m[qs], bm);
         const float msafe = mnew == -__builtin_inff() ? 0.0f : mnew;
         const float alpha = fast_exp2(m[qs] - msafe);
@@ -423,7 +423,7 @@ __device__ __forceinline__ void fwd_finish(const GroupDesc& gd, const FwdAcc<D, 
     const int row = row0 + qs * 32 + qc;
     float inv = out_scale, lse = 0.0f;
     if (softmax) {
-      const float ltot = acc.lsum[qs] + __shfl_xor(acc.lsum[qs], 32);
+      const float ltot = half32_sum(acc.lsum[qs]);
       inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
       lse = ltot > 0.0f ? (acc.m[qs] + __log2f(ltot)) * 0.69314718055994531f : -__builtin_inff();
     }
