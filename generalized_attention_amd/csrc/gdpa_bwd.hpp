@@ -168,7 +168,9 @@ __device__ __forceinline__ void take_commit(BwdWave<D, NW>& st, int kb, char* ld
     float n2 = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < G::KK; ++kk) n2 += sumsq_bf16x8(tr.k[kk]);
-    st.kn2[kb] = wave_max(n2 + __shfl_xor(n2, 32, 64));
+    // (8 waves: without LDS round trips; the 4-wave kernels keep the shuffles, since this compiler
+    // crashes on them with DPP)
+    st.kn2[kb] = NW == 8 ? wave_max_lanes(half32_sum(n2)) : wave_max(n2 + __shfl_xor(n2, 32, 64));
   }
   if (g == 0) reinterpret_cast<float*>(lds + G::OFF_GATE)[pos] = t;
 #pragma unroll
