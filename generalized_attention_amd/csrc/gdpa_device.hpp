@@ -113,6 +113,24 @@ __device__ inline GroupDesc select_group(const LaunchDesc& d, int g) {
   return gd;
 }
 
+// List position of the item that workgroup x of a launch over n items takes. The dispatcher hands
+// consecutive workgroups to the 8 XCDs in turn, and each XCD has an L2 of its own; the heads of one
+// sequence are consecutive in the list and share the cache lines of the row-interleaved [T, H]
+// float arrays (gate, lse, dG: H heads' 4-byte entries of a row side by side). So each run of 8
+// consecutive list items goes to one XCD: in round r = k / 8, the k-th workgroup of XCD c takes
+// item 64 r + 8 c' + k % 8 with c' = c in even rounds and 7 - c in odd ones. The list order is kept
+// at the granularity of 64 items, and the alternation cancels the skew that a fixed order would give
+// (in a longest-first list XCD 0 would take the longest run of every round); a ragged tail keeps its
+// positions.
+constexpr int kXcds = 8;
+__device__ inline int xcd_item(int x, int n) {
+  const int full = n & ~(kXcds * kXcds - 1);
+  if (x >= full) return x;
+  const int c = x % kXcds, k = x / kXcds, r = k / kXcds;
+  const int cs = (r & 1) ? kXcds - 1 - c : c;
+  return r * (kXcds * kXcds) + cs * kXcds + k % kXcds;
+}
+
 // Packed work item: group (5 bits) | head (8 bits) | sequence (19 bits).
 __host__ __device__ inline int32_t pack_item(int g, int h, int b) {
   return (int32_t)(((uint32_t)g << 27) | ((uint32_t)h << 19) | (uint32_t)b);

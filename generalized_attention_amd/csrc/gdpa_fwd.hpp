@@ -643,7 +643,7 @@ __global__ void __launch_bounds__(fwd_waves<MODE>() * kWave, fwd_waves_per_simd<
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if ((int)blockIdx.x >= d.n_items || launch_refused(d)) return;
   int g, h, b;
-  unpack_item(d.items[blockIdx.x], g, h, b);
+  unpack_item(d.items[xcd_item((int)blockIdx.x, d.n_items)], g, h, b);
   if (g >= d.n_groups) return;
   GroupDesc gd = select_group(d, g);
   if (b >= gd.num_seqs || h >= gd.num_heads) return;  // list built for another shape
